@@ -1,0 +1,292 @@
+"""CPU oracle of the fused MoE layer forward on one expert-parallel share.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links this
+module: only the test suite, the smoke check of ``__graft_entry__`` and the CPU
+baseline leg of ``bench.py`` use it. It shares no code with the HIP library and
+reads nothing the HIP library wrote.
+
+What it computes is the plain definition of the MoE layer as the pages give it:
+
+* "[Feature] Expert parallelism support" (sglang issue #1435), ``MixtralMoE.forward``:
+  router logits from a replicated gate, softmax in fp32, top-k, renormalise, then for
+  each local expert the expert MLP weighted by the routing weight, summed; the rank's
+  partial sum is all-reduced over ranks, so one share's output is that sum restricted
+  to its local experts.
+* "ep_fused_moe_patch.py: EP-aware FusedMoE override for vllm 0.6.3", ``_ep_init`` /
+  ``_ep_forward``: routing over ALL experts on every rank (``select_experts`` sees the
+  global count), local experts at FULL intermediate size, the renormalize /
+  grouped-top-k switches, and the per-token sum of the weighted expert rows
+  (Step 4, scatter-add by token).
+* "vllm.model_executor.models.transformers.moe", ``MoEMixin.recursive_replace``:
+  ``routed_scaling_factor``, grouped top-k enabled by ``n_group`` / ``topk_group``,
+  the ``silu`` activation, packed ``gate_up_proj`` of shape (E, 2I, H), and shared
+  experts that the fused layer adds itself.
+* "Expert Parallel" (vllm-omni design doc), Step 5 forward: the shared expert output is
+  added to the routed output on every rank.
+
+Precision. Router logits are the fp32 rounding of the exact (fp64-accumulated) dot
+products; softmax, top-k selection and routing weights are fp32, because the pages run
+the softmax with ``dtype=torch.float`` and select on those values. The expert MLPs and
+the combine run in fp64 on the exact (upcast) input values.
+
+Readings of points the pages leave open (each is listed with its reason in the design
+notes): the expert MLP is ``W2 (silu(W1 x) * (W3 x))`` with ``w13`` = [W1 rows; W3 rows];
+grouped top-k scores a group by its largest softmax probability, keeps ``topk_group``
+groups and picks top-k among their experts; ties go to the lower expert (or group) id;
+renormalisation is over all k global picks, before the expert_map mask; the routed
+scaling factor multiplies the routing weights after renormalisation and does not touch
+the shared expert; the routing weight multiplies the expert output (after W2).
+
+Pins: every function here is checked by the ``not gpu`` tests against closed forms,
+library routines on special cases, brute force on tiny inputs and invariants of the
+method (see the tests of the oracle). The absolute outputs of the large workloads are
+pinned only through those checks.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "softmax_fp32", "select_experts", "routing_weights", "route",
+    "gated_mlp", "moe_forward_given_routing", "moe_forward", "moe_forward_per_token",
+    "align_permute", "weight_bytes",
+]
+
+
+def router_logits(x, w_gate, logit_bias=None):
+    """fp32 router logits [T, E] = x [T, H] . w_gate [E, H]^T (+ bias [E]).
+
+    The replicated gate of ``MixtralMoE`` (``ReplicatedLinear(hidden, num_experts,
+    bias=False)``; sglang issue #1435) and of ``HunYuanSparseMoeBlock`` ("Expert
+    Parallel", Step 2). The skewed-load workload adds a per-expert bias to the logits.
+    Dot products are accumulated in fp64 and rounded once to fp32.
+    """
+    l = np.asarray(x, np.float64) @ np.asarray(w_gate, np.float64).T
+    if logit_bias is not None:
+        l = l + np.asarray(logit_bias, np.float64)[None, :]
+    return l.astype(np.float32)
+
+
+def softmax_fp32(logits):
+    """Row softmax in fp32: exp(l - max) / sum exp(l - max).
+
+    ``F.softmax(router_logits, dim=1, dtype=torch.float)`` in ``MixtralMoE.forward``.
+    """
+    l = np.asarray(logits, np.float32)
+    m = l.max(axis=1, keepdims=True)
+    with np.errstate(under="ignore"):
+        e = np.exp(l - m)
+    s = e.sum(axis=1, keepdims=True, dtype=np.float32)
+    return (e / s).astype(np.float32)
+
+
+def select_experts(p, top_k, use_grouped_topk=False, num_expert_group=1, topk_group=1):
+    """Top-k expert ids per token, plain or group-limited.
+
+    Plain: the k largest probabilities (``torch.topk`` in ``MixtralMoE.forward``).
+    Grouped (``use_grouped_topk`` / ``num_expert_group`` / ``topk_group`` of ``_ep_init``;
+    ``n_group`` / ``topk_group`` of ``recursive_replace``): experts form
+    ``num_expert_group`` contiguous groups of E/G; a group's score is its largest
+    probability; the ``topk_group`` best groups are kept and the top-k is taken among
+    their experts only (others are excluded, not zeroed).
+
+    Order and ties: slots are sorted by probability descending; equal values go to the
+    lower expert id (groups: the lower group id).
+
+    Returns ``ids`` int32 [T, k], ``gap`` fp32 [T] = k-th minus (k+1)-th candidate score
+    (+inf without a (k+1)-th candidate) and ``ggap`` fp32 [T] = the same gap between the
+    last kept and the first dropped group score (+inf when every group is kept).
+    """
+    p = np.asarray(p, np.float32)
+    T, E = p.shape
+    ggap = np.full(T, np.inf, np.float32)
+    if use_grouped_topk:
+        G = int(num_expert_group)
+        per = E // G
+        gs = p.reshape(T, G, per).max(axis=2)
+        gorder = np.argsort(-gs, axis=1, kind="stable")
+        if topk_group < G:
+            gsorted = np.take_along_axis(gs, gorder, axis=1)
+            ggap = (gsorted[:, topk_group - 1] - gsorted[:, topk_group]).astype(np.float32)
+        keep = np.zeros((T, G), bool)
+        np.put_along_axis(keep, gorder[:, :topk_group], True, axis=1)
+        score = np.where(np.repeat(keep, per, axis=1), p, np.float32(-np.inf))
+        ncand = topk_group * per
+    else:
+        score = p
+        ncand = E
+    order = np.argsort(-score, axis=1, kind="stable")
+    ids = order[:, :top_k].astype(np.int32)
+    if top_k < ncand:
+        ss = np.take_along_axis(score, order[:, top_k - 1:top_k + 1], axis=1)
+        gap = (ss[:, 0] - ss[:, 1]).astype(np.float32)
+    else:
+        gap = np.full(T, np.inf, np.float32)
+    return ids, gap, ggap
+
+
+def routing_weights(p, ids, renormalize, routed_scaling_factor=1.0):
+    """fp32 routing weights [T, k] of the chosen experts.
+
+    ``w = p[ids]``; with ``renormalize`` (``routing_weights /= routing_weights.sum(...)``
+    in ``MixtralMoE.forward``) divided by their sum, taken in slot order over all k global
+    picks; then multiplied by ``routed_scaling_factor`` (``recursive_replace``).
+    """
+    w = np.take_along_axis(np.asarray(p, np.float32), ids.astype(np.int64), axis=1)
+    if renormalize:
+        s = w[:, 0].copy()
+        for j in range(1, w.shape[1]):
+            s = (s + w[:, j]).astype(np.float32)
+        w = (w / s[:, None]).astype(np.float32)
+    return (w * np.float32(routed_scaling_factor)).astype(np.float32)
+
+
+def route(x, w_gate, top_k, renormalize, use_grouped_topk=False, num_expert_group=1,
+          topk_group=1, routed_scaling_factor=1.0, logit_bias=None):
+    """Router: logits -> fp32 softmax -> (grouped) top-k -> weights. Returns a dict."""
+    logits = router_logits(x, w_gate, logit_bias)
+    p = softmax_fp32(logits)
+    ids, gap, ggap = select_experts(p, top_k, use_grouped_topk, num_expert_group, topk_group)
+    w = routing_weights(p, ids, renormalize, routed_scaling_factor)
+    return {"logits": logits, "probs": p, "ids": ids, "weights": w, "gap": gap, "ggap": ggap}
+
+
+def gated_mlp(x, w13, w2):
+    """fp64 gated-SiLU expert MLP on rows of x: W2 (silu(W1 x) * (W3 x)).
+
+    ``w13`` is [2I, H] with the W1 (gate) rows first and the W3 (up) rows after them, the
+    packed ``gate_up_proj`` (E, 2I, H) of ``recursive_replace``; ``w2`` is [H, I].
+    silu(g) = g / (1 + exp(-g)).
+    """
+    x64 = np.asarray(x, np.float64)
+    w13 = np.asarray(w13, np.float64)
+    I = w13.shape[0] // 2
+    g = x64 @ w13[:I].T
+    u = x64 @ w13[I:].T
+    with np.errstate(over="ignore"):
+        a = g / (1.0 + np.exp(-g)) * u
+    return a @ np.asarray(w2, np.float64).T
+
+
+def moe_forward_given_routing(x, ids, weights, expert_map, w13_local, w2_local,
+                              shared_w13=None, shared_w2=None):
+    """One share's output [T, H] (fp64) for given routing, as ``MixtralMoE.forward`` does it.
+
+    For each local expert (slot s of ``expert_map``): the per-token weight is the sum over
+    the k slots of ``weights * (ids == expert)``; tokens with that expert get
+    ``weight * MLP_s(x)`` added. Tokens that did not pick the expert would add 0 * MLP
+    (page 1 runs every token through every local expert); they are skipped, which is
+    the same value for finite inputs. Experts outside the share (map value -1)
+    contribute nothing. The shared expert, if given, is added with weight 1 ("Expert
+    Parallel" Step 5). ``w13_local[s]`` / ``w2_local[s]`` may be any per-slot sequence
+    of arrays (converted one slot at a time).
+    """
+    x64 = np.asarray(x, np.float64)
+    T, H = x64.shape
+    ids = np.asarray(ids)
+    wts = np.asarray(weights, np.float64)
+    emap = np.asarray(expert_map)
+    slots = emap[ids]
+    out = np.zeros((T, H), np.float64)
+    for s in range(int(emap.max(initial=-1)) + 1):
+        hit = slots == s
+        rows = np.nonzero(hit.any(axis=1))[0]
+        if rows.size == 0:
+            continue
+        w_tok = (wts * hit).sum(axis=1)
+        out[rows] += w_tok[rows, None] * gated_mlp(x64[rows], w13_local[s], w2_local[s])
+    if shared_w13 is not None:
+        out += gated_mlp(x64, shared_w13, shared_w2)
+    return out
+
+
+def moe_forward(x, w_gate, expert_map, w13_local, w2_local, top_k, renormalize,
+                use_grouped_topk=False, num_expert_group=1, topk_group=1,
+                routed_scaling_factor=1.0, logit_bias=None, shared_w13=None, shared_w2=None):
+    """Route then combine: returns (out fp64 [T, H], routing dict)."""
+    r = route(x, w_gate, top_k, renormalize, use_grouped_topk, num_expert_group, topk_group,
+              routed_scaling_factor, logit_bias)
+    out = moe_forward_given_routing(x, r["ids"], r["weights"], expert_map, w13_local, w2_local,
+                                    shared_w13, shared_w2)
+    return out, r
+
+
+def moe_forward_per_token(x, ids, weights, expert_map, w13_local, w2_local,
+                          shared_w13=None, shared_w2=None):
+    """The per-token definition, with Python loops (small inputs only).
+
+    out[t] = sum over slots j whose expert is local of weights[t, j] * MLP(x[t]) (+ shared
+    MLP), the per-token sum of weighted expert rows of ``_ep_forward`` Step 4. Each MLP is
+    evaluated with explicit per-row dot products.
+    """
+    x64 = np.asarray(x, np.float64)
+    T, H = x64.shape
+    out = np.zeros((T, H), np.float64)
+    emap = np.asarray(expert_map)
+
+    def mlp_row(xt, w13, w2):
+        w13 = np.asarray(w13, np.float64)
+        w2 = np.asarray(w2, np.float64)
+        I = w13.shape[0] // 2
+        act = np.empty(I)
+        for i in range(I):
+            g = float(np.dot(w13[i], xt))
+            u = float(np.dot(w13[I + i], xt))
+            act[i] = g / (1.0 + np.exp(-g)) * u if g > -700 else 0.0
+        return np.array([float(np.dot(w2[h], act)) for h in range(w2.shape[0])])
+
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(ids.shape[1]):
+            s = int(emap[int(ids[t, j])])
+            if s < 0:
+                continue
+            acc += float(weights[t, j]) * mlp_row(x64[t], w13_local[s], w2_local[s])
+        if shared_w13 is not None:
+            acc += mlp_row(x64[t], shared_w13, shared_w2)
+        out[t] = acc
+    return out
+
+
+def align_permute(topk_local, num_local_experts, block_m):
+    """Token-pair permutation by local expert, padded per expert to a multiple of block_m.
+
+    The method's grouping of work by expert (the per-expert loop of ``MixtralMoE.forward``;
+    the sort-and-gather before ``fused_experts`` in ``_ep_forward`` Step 2/3), laid out
+    for a grouped GEMM. Pair id p = t * k + j. For each local slot e the pairs with
+    ``topk_local == e`` are listed in increasing pair id; segment e starts at
+    offsets[e] = sum over e' < e of ceil(count[e'] / block_m) * block_m; unused slots of a
+    segment hold -1. ``pair_row[p]`` is the position of pair p (-1 if its expert is not
+    local); ``block_expert[b]`` is the slot that owns rows [b*block_m, (b+1)*block_m).
+    """
+    tl = np.asarray(topk_local, np.int64).reshape(-1)
+    E_l = int(num_local_experts)
+    pairs = np.nonzero(tl >= 0)[0]
+    order = np.argsort(tl[pairs], kind="stable")
+    by_expert = pairs[order]
+    counts = np.bincount(tl[pairs], minlength=E_l).astype(np.int64)
+    padded = -(-counts // block_m) * block_m
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    num_padded = int(offsets[-1])
+    sorted_pairs = np.full(num_padded, -1, np.int32)
+    pair_row = np.full(tl.shape[0], -1, np.int32)
+    for e in range(E_l):
+        seg = by_expert[starts[e]:starts[e + 1]]
+        sorted_pairs[offsets[e]:offsets[e] + counts[e]] = seg
+        pair_row[seg] = offsets[e] + np.arange(counts[e])
+    block_expert = np.repeat(np.arange(E_l, dtype=np.int32), padded // block_m)
+    return {"sorted_pairs": sorted_pairs, "block_expert": block_expert, "pair_row": pair_row,
+            "num_padded": num_padded, "counts": counts.astype(np.int32),
+            "offsets": offsets.astype(np.int32)}
+
+
+def weight_bytes(n_experts, hidden, inter, dtype_bytes, layers=1):
+    """Expert-weight bytes on one card: n * (2*I*H + H*I) * bytes * layers.
+
+    The per-card memory arithmetic of the ep_fused_moe_patch.py docstring ("Memory layout
+    comparison"): each expert holds a gate/up matrix (2I x H) and a down matrix (H x I)
+    at the card's intermediate size.
+    """
+    return int(n_experts) * (2 * int(inter) * int(hidden) + int(hidden) * int(inter)) \
+        * int(dtype_bytes) * int(layers)
