@@ -1,0 +1,146 @@
+// Alignment of the (token, slot) pairs by local expert (gfx950).
+//
+// The expert loop of "[Feature] Expert parallelism support" (MixtralMoE.forward) works
+// expert by expert; "ep_fused_moe_patch.py" (_ep_forward Steps 2-3) sorts the work items
+// before handing them to the fused expert kernel. Here the pairs p = t*k + j whose slot is
+// local are grouped by slot, kept in increasing p inside a slot, and each slot's segment is
+// padded to a multiple of block_m rows so that a GEMM tile never straddles two experts.
+//
+// Three passes, no host synchronisation:
+//   count   : one workgroup per chunk of 256 tokens, LDS histogram of its pairs per slot
+//   scan    : one workgroup; per-slot exclusive scan over chunks (chunk bases), padded
+//             segment sizes, exclusive scan over slots (offsets), block -> slot table, -1 fill
+//   scatter : one workgroup per chunk; each wave marks its 64 tokens per slot in an LDS
+//             64-bit mask; a pair's rank inside its slot is the chunk base plus the number of
+//             marked tokens before it (earlier waves, then earlier lanes), which keeps the
+//             order stable without sorting
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int local_slot(const int32_t* tl, int64_t i, int E_l) {
+  const int s = tl[i];
+  return (s >= 0 && s < E_l) ? s : -1;
+}
+
+__global__ void __launch_bounds__(256) align_count(const int32_t* __restrict__ tl, int T, int k,
+                                                   int E_l, int32_t* __restrict__ chunk) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E_l; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kAlignChunk + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int s = local_slot(tl, static_cast<int64_t>(t) * k + j, E_l);
+      if (s >= 0) atomicAdd(&hist[s], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E_l; e += 256) chunk[static_cast<int64_t>(blockIdx.x) * E_l + e] = hist[e];
+}
+
+__global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, int nchunks, int E_l,
+                                                  int bm, int32_t* __restrict__ meta,
+                                                  int32_t* __restrict__ num_padded,
+                                                  int32_t* __restrict__ block_expert,
+                                                  int32_t* __restrict__ sorted_pairs) {
+  __shared__ int seg[257];
+  int32_t* offsets = meta + 1;
+  int32_t* counts = meta + 1 + (E_l + 1);
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E_l) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int64_t i = static_cast<int64_t>(c) * E_l + e;
+      const int v = chunk[i];
+      chunk[i] = run;
+      run += v;
+    }
+    counts[e] = run;
+    seg[e] = (run + bm - 1) / bm * bm;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0;
+    for (int i = 0; i < E_l; ++i) {
+      const int v = seg[i];
+      seg[i] = acc;
+      acc += v;
+    }
+    seg[E_l] = acc;
+    offsets[E_l] = acc;
+    meta[0] = acc;
+    *num_padded = acc;
+  }
+  __syncthreads();
+  if (e < E_l) {
+    const int off = seg[e];
+    const int end = seg[e + 1];
+    offsets[e] = off;
+    for (int b = off / bm; b < end / bm; ++b) block_expert[b] = e;
+    for (int i = off; i < end; ++i) sorted_pairs[i] = -1;
+  }
+}
+
+__global__ void __launch_bounds__(256) align_scatter(const int32_t* __restrict__ tl, int T, int k,
+                                                     int E_l, const int32_t* __restrict__ chunk,
+                                                     const int32_t* __restrict__ meta,
+                                                     int32_t* __restrict__ sorted_pairs,
+                                                     int32_t* __restrict__ pair_row) {
+  __shared__ unsigned long long mask[4][256];
+  __shared__ int base[256];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int32_t* offsets = meta + 1;
+  for (int e = tid; e < E_l; e += 256) {
+    base[e] = offsets[e] + chunk[static_cast<int64_t>(blockIdx.x) * E_l + e];
+    mask[0][e] = mask[1][e] = mask[2][e] = mask[3][e] = 0ull;
+  }
+  __syncthreads();
+  const int t = blockIdx.x * kAlignChunk + tid;
+  const bool valid = t < T;
+  if (valid)
+    for (int j = 0; j < k; ++j) {
+      const int s = local_slot(tl, static_cast<int64_t>(t) * k + j, E_l);
+      if (s >= 0) atomicOr(&mask[wave][s], 1ull << lane);
+    }
+  __syncthreads();
+  if (!valid) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int64_t pid = static_cast<int64_t>(t) * k + j;
+    const int s = local_slot(tl, pid, E_l);
+    if (s < 0) {
+      pair_row[pid] = -1;
+      continue;
+    }
+    int before = __popcll(mask[wave][s] & below);
+    for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
+    const int pos = base[s] + before;
+    sorted_pairs[pos] = static_cast<int32_t>(pid);
+    pair_row[pid] = pos;
+  }
+}
+
+}  // namespace
+
+int launch_align(const moe_params& p, int T, const int32_t* topk_local, int block_m,
+                 int32_t* sorted_pairs, int32_t* block_expert, int32_t* pair_row,
+                 int32_t* num_padded, int32_t* meta, int32_t* chunk, hipStream_t s) {
+  const int E_l = p.num_local_experts;
+  const int k = p.top_k;
+  const int nchunks = align_chunks(T);
+  align_count<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk);
+  MOE_LAUNCH_CHECK();
+  align_scan<<<1, 256, 0, s>>>(chunk, nchunks, E_l, block_m, meta, num_padded, block_expert,
+                               sorted_pairs);
+  MOE_LAUNCH_CHECK();
+  align_scatter<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, meta, sorted_pairs, pair_row);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,307 @@
+// C ABI of the fused MoE forward: argument checks, workspace layout, launch order.
+// Declarations and the contract of every entry point are in include/moe.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+using moe::align_chunks;
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline size_t elt_bytes(const moe_params& p) { return p.dtype == MOE_F32 ? 4 : 2; }
+
+inline bool mult64(int32_t v) { return v > 0 && v % 64 == 0; }
+
+int check_params(const moe_params* p) {
+  if (!p) return MOE_EINVAL;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  const int E = p->num_experts;
+  if (E < 1 || p->top_k < 1 || p->top_k > E) return MOE_EINVAL;
+  if (!mult64(p->hidden_size) || !mult64(p->intermediate_size)) return MOE_EINVAL;
+  if (p->renormalize != 0 && p->renormalize != 1) return MOE_EINVAL;
+  if (p->use_grouped_topk != 0 && p->use_grouped_topk != 1) return MOE_EINVAL;
+  if (p->use_grouped_topk) {
+    const int G = p->num_expert_group;
+    if (G < 1 || E % G != 0 || p->topk_group < 1 || p->topk_group > G) return MOE_EINVAL;
+    if (p->top_k > p->topk_group * (E / G)) return MOE_EINVAL;
+    if (G > 64) return MOE_EUNSUPPORTED;
+  }
+  if (!isfinite(p->routed_scaling_factor)) return MOE_EINVAL;
+  if (p->num_local_experts < 1 || p->num_local_experts > E) return MOE_EINVAL;
+  if (p->shared_intermediate_size < 0) return MOE_EINVAL;
+  if (p->shared_intermediate_size > 0 && !mult64(p->shared_intermediate_size)) return MOE_EINVAL;
+  if (E > 256 || p->top_k > 64) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(const moe_params& p, int64_t T) {
+  if (T < 0) return MOE_EINVAL;
+  // pair ids t*k+j and sorted rows are int32
+  if (T * p.top_k + static_cast<int64_t>(p.num_local_experts) * 128 >= (int64_t{1} << 31))
+    return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int pick_block_m(const moe_params& p, int64_t T) {
+  // Expected rows per local expert under uniform routing: T*k/E.
+  const double rows = static_cast<double>(T) * p.top_k / p.num_experts;
+  if (p.dtype == MOE_F32) return 16;
+  if (rows <= 12.0) return 16;
+  if (rows <= 48.0) return 64;
+  return 128;
+}
+
+int64_t capacity(const moe_params& p, int64_t T, int bm) {
+  return T * p.top_k + static_cast<int64_t>(p.num_local_experts) * (bm - 1);
+}
+
+// Workspace layout of moe_forward. Each split entry point uses only `scratch`-style
+// regions it owns, placed from offset 0 of the caller's workspace.
+struct Layout {
+  size_t topk_ids, topk_w, topk_local, sorted_pairs, block_expert, pair_row, num_padded;
+  size_t meta, chunk, y, shared_y, scratch, total;
+  // sizes of the split entry points' scratch needs
+  size_t route_need, align_need, mlp_need, shared_need;
+};
+
+Layout layout(const moe_params& p, int64_t T, int bm) {
+  Layout L{};
+  const size_t tk = static_cast<size_t>(T) * p.top_k;
+  const size_t cap = static_cast<size_t>(capacity(p, T, bm));
+  const size_t eb = elt_bytes(p);
+  const size_t E_l = p.num_local_experts;
+  const size_t nch = static_cast<size_t>(align_chunks(T));
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.topk_ids = take(tk * 4);
+  L.topk_w = take(tk * 4);
+  L.topk_local = take(tk * 4);
+  L.sorted_pairs = take(cap * 4);
+  L.block_expert = take((cap / bm + 1) * 4);
+  L.pair_row = take(tk * 4);
+  L.num_padded = take(4);
+  L.meta = take((2 * E_l + 2) * 4);
+  L.chunk = take(nch * E_l * 4);
+  L.y = take(cap * p.hidden_size * eb);
+  L.shared_y = take(p.shared_intermediate_size ? static_cast<size_t>(T) * p.hidden_size * eb : 0);
+  L.route_need = round_up(static_cast<size_t>(T) * p.num_experts * 4);
+  L.align_need = round_up((2 * E_l + 2) * 4) + round_up(nch * E_l * 4);
+  L.mlp_need = round_up(cap * p.intermediate_size * eb);
+  L.shared_need = round_up(static_cast<size_t>(T) * p.shared_intermediate_size * eb);
+  size_t need = L.route_need;
+  if (L.mlp_need > need) need = L.mlp_need;
+  if (L.shared_need > need) need = L.shared_need;
+  L.scratch = take(need);
+  L.total = o;
+  // The split entry points place their own regions at offset 0; forward's total covers
+  // each of them because it is at least the scratch region plus the align tables.
+  if (L.align_need > L.total) L.total = L.align_need;
+  return L;
+}
+
+template <typename T_>
+T_* at(void* ws, size_t off) {
+  return reinterpret_cast<T_*>(static_cast<char*>(ws) + off);
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported configuration";
+    case MOE_ENOSPC: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+int moe_check_params(const moe_params* p) { return check_params(p); }
+
+int moe_pick_block_m(const moe_params* p, int64_t num_tokens, int32_t* block_m) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!block_m || num_tokens < 0) return MOE_EINVAL;
+  *block_m = pick_block_m(*p, num_tokens);
+  return MOE_OK;
+}
+
+int64_t moe_sorted_capacity(const moe_params* p, int64_t num_tokens, int32_t block_m) {
+  if (check_params(p) || num_tokens < 0 || !valid_block_m(block_m)) return -1;
+  return capacity(*p, num_tokens, block_m);
+}
+
+int moe_workspace_size(const moe_params* p, int64_t num_tokens, int32_t block_m, size_t* bytes) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!bytes) return MOE_EINVAL;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  const int bm = block_m == 0 ? pick_block_m(*p, num_tokens) : block_m;
+  if (!valid_block_m(bm)) return MOE_EINVAL;
+  *bytes = layout(*p, num_tokens, bm).total;
+  return MOE_OK;
+}
+
+int moe_make_expert_map(int32_t num_experts, int32_t ep_size, int32_t ep_rank, int32_t* map_host) {
+  if (!map_host || num_experts < 1 || ep_size < 1 || ep_size > num_experts) return MOE_EINVAL;
+  if (num_experts % ep_size != 0 || ep_rank < 0 || ep_rank >= ep_size) return MOE_EINVAL;
+  const int per = num_experts / ep_size;
+  const int start = ep_rank * per;
+  for (int e = 0; e < num_experts; ++e) map_host[e] = (e >= start && e < start + per) ? e - start : -1;
+  return MOE_OK;
+}
+
+int64_t moe_weight_bytes(int64_t n_experts, int64_t hidden, int64_t inter, int32_t dtype_bytes,
+                         int64_t layers) {
+  if (n_experts < 0 || hidden < 0 || inter < 0 || dtype_bytes < 0 || layers < 0) return -1;
+  return n_experts * (2 * inter * hidden + hidden * inter) * dtype_bytes * layers;
+}
+
+int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+              const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
+              float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x || !w_gate || !expert_map || !topk_ids || !topk_w || !topk_local || !ws) return MOE_EINVAL;
+  const Layout L = layout(*p, num_tokens, 16);
+  if (ws_bytes < L.route_need) return MOE_ENOSPC;
+  const int T = static_cast<int>(num_tokens);
+  float* logits = static_cast<float*>(ws);
+  if ((rc = moe::launch_router_logits(*p, T, x, w_gate, logits, as_stream(stream)))) return rc;
+  return moe::launch_topk(*p, T, logits, logit_bias, expert_map, topk_ids, topk_w, topk_local,
+                          as_stream(stream));
+}
+
+int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* topk_local,
+                      int32_t block_m, int32_t* sorted_pairs, int32_t* block_expert,
+                      int32_t* pair_row, int32_t* num_padded, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (num_tokens == 0) return MOE_OK;
+  if (!topk_local || !sorted_pairs || !block_expert || !pair_row || !num_padded || !ws)
+    return MOE_EINVAL;
+  const Layout L = layout(*p, num_tokens, block_m);
+  if (ws_bytes < L.align_need) return MOE_ENOSPC;
+  int32_t* meta = static_cast<int32_t*>(ws);
+  int32_t* chunk = at<int32_t>(ws, round_up((2 * static_cast<size_t>(p->num_local_experts) + 2) * 4));
+  return moe::launch_align(*p, static_cast<int>(num_tokens), topk_local, block_m, sorted_pairs,
+                           block_expert, pair_row, num_padded, meta, chunk, as_stream(stream));
+}
+
+int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
+                    const void* w2, const int32_t* sorted_pairs, const int32_t* block_expert,
+                    const int32_t* num_padded, int32_t block_m, void* y, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x || !w13 || !w2 || !sorted_pairs || !block_expert || !num_padded || !y || !ws)
+    return MOE_EINVAL;
+  const Layout L = layout(*p, num_tokens, block_m);
+  if (ws_bytes < L.mlp_need) return MOE_ENOSPC;
+  const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
+  return moe::launch_mlp(*p, static_cast<int>(num_tokens), x, w13, w2, p->intermediate_size,
+                         sorted_pairs, num_padded, block_expert, block_m, rows, ws, y,
+                         as_stream(stream));
+}
+
+int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,
+                   const void* shared_w13, const void* shared_w2, void* shared_y, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (p->shared_intermediate_size == 0) return MOE_EINVAL;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x || !shared_w13 || !shared_w2 || !shared_y || !ws) return MOE_EINVAL;
+  const Layout L = layout(*p, num_tokens, 16);
+  if (ws_bytes < L.shared_need) return MOE_ENOSPC;
+  const int T = static_cast<int>(num_tokens);
+  return moe::launch_mlp(*p, T, x, shared_w13, shared_w2, p->shared_intermediate_size, nullptr,
+                         nullptr, nullptr, 0, T, ws, shared_y, as_stream(stream));
+}
+
+int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const int32_t* pair_row,
+                const float* topk_w, const void* shared_y, void* out, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (num_tokens == 0) return MOE_OK;
+  if (!y || !pair_row || !topk_w || !out) return MOE_EINVAL;
+  return moe::launch_combine(*p, static_cast<int>(num_tokens), y, pair_row, topk_w, shared_y, out,
+                             as_stream(stream));
+}
+
+int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+                const float* logit_bias, const int32_t* expert_map, const void* w13,
+                const void* w2, const void* shared_w13, const void* shared_w2, void* out,
+                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if ((shared_w13 == nullptr) != (shared_w2 == nullptr)) return MOE_EINVAL;
+  const bool shared = shared_w13 != nullptr;
+  if (shared && p->shared_intermediate_size == 0) return MOE_EINVAL;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x || !w_gate || !expert_map || !w13 || !w2 || !out || !ws) return MOE_EINVAL;
+  const int bm = pick_block_m(*p, num_tokens);
+  const Layout L = layout(*p, num_tokens, bm);
+  if (ws_bytes < L.total) return MOE_ENOSPC;
+  const int T = static_cast<int>(num_tokens);
+  const hipStream_t s = as_stream(stream);
+
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.topk_ids);
+  float* tw = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
+  int32_t* local = at<int32_t>(ws, L.topk_local);
+  int32_t* sorted_pairs = at<int32_t>(ws, L.sorted_pairs);
+  int32_t* block_expert = at<int32_t>(ws, L.block_expert);
+  int32_t* pair_row = at<int32_t>(ws, L.pair_row);
+  int32_t* num_padded = at<int32_t>(ws, L.num_padded);
+  void* y = at<char>(ws, L.y);
+  void* shared_y = shared ? at<char>(ws, L.shared_y) : nullptr;
+  void* scratch = at<char>(ws, L.scratch);
+
+  if ((rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s))) return rc;
+  if ((rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, expert_map, ids, tw,
+                             local, s)))
+    return rc;
+  if ((rc = moe::launch_align(*p, T, local, bm, sorted_pairs, block_expert, pair_row, num_padded,
+                              at<int32_t>(ws, L.meta), at<int32_t>(ws, L.chunk), s)))
+    return rc;
+  const int rows = static_cast<int>(capacity(*p, T, bm));
+  if ((rc = moe::launch_mlp(*p, T, x, w13, w2, p->intermediate_size, sorted_pairs, num_padded,
+                            block_expert, bm, rows, scratch, y, s)))
+    return rc;
+  if (shared &&
+      (rc = moe::launch_mlp(*p, T, x, shared_w13, shared_w2, p->shared_intermediate_size, nullptr,
+                            nullptr, nullptr, 0, T, scratch, shared_y, s)))
+    return rc;
+  return moe::launch_combine(*p, T, y, pair_row, tw, shared_y, out, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal launchers of the fused MoE forward. Arguments are already validated by the
+// C-ABI layer; every launcher only enqueues kernels on `s` and returns MOE_OK or MOE_EHIP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Tokens handled by one workgroup of the align count/scatter passes.
+constexpr int kAlignChunk = 256;
+
+inline int align_chunks(int64_t T) { return static_cast<int>((T + kAlignChunk - 1) / kAlignChunk); }
+
+// Router logits [T, E] fp32 = x . Wg^T (bias is added by the top-k pass).
+int launch_router_logits(const moe_params& p, int T, const void* x, const void* w_gate,
+                         float* logits, hipStream_t s);
+
+// fp32 softmax, (grouped) top-k, renormalise, scale, expert_map lookup.
+int launch_topk(const moe_params& p, int T, const float* logits, const float* bias,
+                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s);
+
+// Count / scan / scatter of the (token, slot) pairs by local expert.
+// meta: [num_padded(1) | offsets(E_l+1) | counts(E_l)], chunk: [align_chunks(T) * E_l].
+int launch_align(const moe_params& p, int T, const int32_t* topk_local, int block_m,
+                 int32_t* sorted_pairs, int32_t* block_expert, int32_t* pair_row,
+                 int32_t* num_padded, int32_t* meta, int32_t* chunk, hipStream_t s);
+
+// Expert MLP over rows: act = silu(x W1^T) * (x W3^T), y = act W2^T.
+//  sorted (row_map != NULL): rows of the expert-sorted pair list, capacity rows, block_m granule;
+//  dense  (row_map == NULL): the first `rows` tokens with a single weight set.
+int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const void* w2,
+               int inter, const int32_t* row_map, const int32_t* num_padded,
+               const int32_t* block_expert, int block_m, int rows, void* act, void* y,
+               hipStream_t s);
+
+// out[t] = sum_j w[t,j] * y[pair_row[t,j]] (+ shared_y[t]).
+int launch_combine(const moe_params& p, int T, const void* y, const int32_t* pair_row,
+                   const float* topk_w, const void* shared_y, void* out, hipStream_t s);
+
+}  // namespace moe

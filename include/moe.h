@@ -1,0 +1,229 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused Mixture-of-Experts layer forward,
+ * computed on one expert-parallel rank's share of the experts.
+ *
+ * What is computed (per token t of x [T, H]):
+ *   logits  = x[t] . Wg^T (+ logit_bias)        replicated router gate over ALL E experts
+ *   p       = softmax(logits) in fp32
+ *   ids     = top-k of p (plain, or group-limited), ties to the lower expert id
+ *   w       = p[ids] (/ sum if renormalize) * routed_scaling_factor
+ *   out[t]  = sum over slots j whose expert is local of w[j] * MLP_{ids[j]}(x[t])
+ *             (+ the shared expert's MLP(x[t]), weight 1, when its weights are given)
+ *   MLP(x)  = W2 (silu(W1 x) * (W3 x))
+ * Sources: "[Feature] Expert parallelism support" (sglang issue #1435), MixtralMoE.forward
+ * (gate, fp32 softmax, top-k, renormalise, weighted per-expert sum, all-reduce of the
+ * rank's partial sum); "ep_fused_moe_patch.py: EP-aware FusedMoE override for vllm
+ * 0.6.3", _ep_init / _ep_forward (global routing on every rank, local experts at full
+ * intermediate size, renormalize / grouped top-k switches, per-token sum of weighted
+ * rows); "vllm.model_executor.models.transformers.moe", MoEMixin.recursive_replace
+ * (routed_scaling_factor, n_group / topk_group, silu, gate_up_proj (E, 2I, H), shared
+ * experts inside the fused layer); "Expert Parallel" (vllm-omni), Step 5 (shared expert
+ * added on every rank).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, borrowed: the caller owns them, they must
+ *    stay alive until the work queued on `stream` has finished. The library never
+ *    allocates or frees device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work
+ *    on it: no host<->device synchronisation, no host reads of device data, so a call
+ *    can be captured in a HIP graph.
+ *  - Row-major layouts. x [T, H]; Wg [E, H]; w13 [E_l, 2I, H] (rows 0..I-1 = W1 "gate",
+ *    rows I..2I-1 = W3 "up"); w2 [E_l, H, I]; shared_w13 [2 I_s, H]; shared_w2 [H, I_s];
+ *    out [T, H]. x, weights, y and out use `dtype` (fp32 or bf16 bit patterns);
+ *    router logits, probabilities and routing weights are fp32; ids are int32.
+ *  - Return value: MOE_OK (0) or a negative MOE_E* code; nothing is enqueued on error,
+ *    except MOE_EHIP, which reports a failed launch.
+ *  - expert_map [E] int32 holds, for every GLOBAL expert id, its local slot in
+ *    [0, E_l) or -1 when the expert lives on another rank. Its device contents are not
+ *    validated (that would need a sync); slots outside [0, E_l) are treated as -1.
+ *  - T = 0 is a valid no-op.
+ */
+#ifndef EXPERT_MOE_AMD_MOE_H
+#define EXPERT_MOE_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* a parameter or a required pointer is invalid */
+#define MOE_EUNSUPPORTED (-2) /* a valid request this build has no kernel for */
+#define MOE_ENOSPC (-3)       /* the workspace is smaller than moe_workspace_size() */
+#define MOE_EHIP (-4)         /* a HIP launch failed */
+
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/*
+ * Layer parameters, named after the EP-aware FusedMoE constructor (_ep_init on the
+ * ep_fused_moe_patch.py page) and the config fields of MoEMixin.recursive_replace.
+ *  num_experts               E, the GLOBAL expert count the router scores (1..256).
+ *  top_k                     k, experts per token (1..E).
+ *  hidden_size               H, multiple of 64.
+ *  intermediate_size         I of one routed expert at full size (no TP split), multiple of 64.
+ *  renormalize               1: divide the k routing weights by their sum (over all k
+ *                            global picks, before the expert_map mask); 0: keep p.
+ *  use_grouped_topk          1: group-limited routing; E % num_expert_group == 0,
+ *                            1 <= topk_group <= num_expert_group, k <= topk_group*E/G.
+ *                            A group's score is its largest probability.
+ *  routed_scaling_factor     multiplies the routing weights after renormalisation
+ *                            (1.0 = off); never applied to the shared expert.
+ *  num_local_experts         E_l, number of local slots (1..E).
+ *  shared_intermediate_size  I_s of the shared expert MLP (n_shared * I), 0 = none,
+ *                            multiple of 64 otherwise.
+ *  dtype                     MOE_F32 or MOE_BF16 (x, weights, y, out).
+ */
+typedef struct moe_params {
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t hidden_size;
+  int32_t intermediate_size;
+  int32_t renormalize;
+  int32_t use_grouped_topk;
+  int32_t num_expert_group;
+  int32_t topk_group;
+  float routed_scaling_factor;
+  int32_t num_local_experts;
+  int32_t shared_intermediate_size;
+  int32_t dtype;
+} moe_params;
+
+/* ------------------------------------------------------------------ host helpers */
+
+/* Human-readable name of a return code. Never NULL. */
+const char* moe_strerror(int code);
+
+/*
+ * Checks `p` (the rules listed with moe_params). MOE_OK, MOE_EINVAL or MOE_EUNSUPPORTED.
+ */
+int moe_check_params(const moe_params* p);
+
+/*
+ * The per-expert padding granule moe_forward uses for T tokens: the M-tile of the grouped
+ * GEMM that fits the expected rows per local expert. Writes *block_m (16, 32, 64 or 128).
+ */
+int moe_pick_block_m(const moe_params* p, int64_t num_tokens, int32_t* block_m);
+
+/*
+ * Rows of the expert-sorted buffers (sorted_pairs, y) for T tokens and granule block_m:
+ * T*k + E_l*(block_m-1), the worst case over all routings (every pair local). -1 on error.
+ */
+int64_t moe_sorted_capacity(const moe_params* p, int64_t num_tokens, int32_t block_m);
+
+/*
+ * Workspace bytes that moe_forward needs for T tokens (block_m = 0: the granule
+ * moe_forward picks), which is also enough for any single split entry point called with
+ * the same T and block_m. Depends only on host values, so no readback is ever needed.
+ */
+int moe_workspace_size(const moe_params* p, int64_t num_tokens, int32_t block_m, size_t* bytes);
+
+/*
+ * Contiguous expert share of rank `ep_rank` out of `ep_size`: global experts
+ * [rank*E/ep, (rank+1)*E/ep) get slots 0..E/ep-1, all others -1 (per_rank = E/ep_size,
+ * start = ep_rank*per_rank in _ep_init on the ep_fused_moe_patch.py page; "Expert
+ * Parallel" Step 1). MOE_EINVAL if ep_size < 1, ep_size > E (the "more ranks than
+ * experts" error of MixtralMoE), E % ep_size != 0 (the divisibility assert), ep_rank out
+ * of range or map_host NULL. `map_host` is HOST memory of E int32.
+ */
+int moe_make_expert_map(int32_t num_experts, int32_t ep_size, int32_t ep_rank, int32_t* map_host);
+
+/*
+ * Expert-weight bytes per card: n_experts * (2*I*H + H*I) * dtype_bytes * layers, the
+ * per-card memory arithmetic of the ep_fused_moe_patch.py docstring ("Memory layout
+ * comparison"). -1 if any argument is negative.
+ */
+int64_t moe_weight_bytes(int64_t n_experts, int64_t hidden, int64_t inter, int32_t dtype_bytes,
+                         int64_t layers);
+
+/* ------------------------------------------------------------------ device entry points */
+
+/*
+ * Router: logits = x . Wg^T (+ logit_bias), fp32 softmax, plain or grouped top-k,
+ * renormalisation, routed scaling, expert_map lookup (MixtralMoE.forward's gate /
+ * softmax / topk / renormalise; select_experts in _ep_forward Step 1).
+ *  x [T, H] dtype; w_gate [E, H] dtype; logit_bias [E] fp32 or NULL; expert_map [E].
+ *  Outputs [T, k]: topk_ids (global ids, probability descending, ties to the lower id),
+ *  topk_w (fp32), topk_local (expert_map[topk_ids], -1 = not local).
+ *  ws: device scratch of at least moe_workspace_size(p, T, 0) bytes (logits live there).
+ */
+int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+              const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
+              float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Groups the (token, slot) pairs by local expert, stable in pair id p = t*k + j, each
+ * expert's segment padded to a multiple of block_m (the per-expert work list of the
+ * expert loop in MixtralMoE.forward / the sort before fused_experts in _ep_forward).
+ *  topk_local [T, k]: slot of each pair or -1 (may come from the caller's own routing;
+ *    the slots of one token must be distinct, as top-k gives them).
+ *  block_m: 16, 32, 64 or 128.
+ *  Outputs: sorted_pairs [moe_sorted_capacity] (pair ids; -1 in padding; entries past
+ *  *num_padded are left untouched), block_expert [capacity / block_m] (slot owning each
+ *  block_m rows), pair_row [T*k] (row of each pair in sorted order, -1 if not local),
+ *  num_padded [1] (device int32: total padded rows).
+ *  ws: device scratch, at least moe_workspace_size(p, T, block_m) bytes.
+ */
+int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* topk_local,
+                      int32_t block_m, int32_t* sorted_pairs, int32_t* block_expert,
+                      int32_t* pair_row, int32_t* num_padded, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * Grouped expert MLP over the sorted pairs: for each row r < *num_padded with pair
+ * p = sorted_pairs[r] >= 0 and slot e = block_expert[r / block_m],
+ *   y[r] = W2_e (silu(W1_e x[p / k]) * (W3_e x[p / k]))
+ * (MixtralMLP of MixtralMoE; fused_experts with w13 / w2 in _ep_forward Step 3).
+ * Padding rows of y hold unspecified values. y [moe_sorted_capacity, H] dtype.
+ * The routing weight is NOT applied here (moe_combine applies it).
+ *  ws: device scratch, at least moe_workspace_size(p, T, block_m) bytes.
+ */
+int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
+                    const void* w2, const int32_t* sorted_pairs, const int32_t* block_expert,
+                    const int32_t* num_padded, int32_t block_m, void* y, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * Shared expert on every token: shared_y [T, H] = W2s (silu(W1s x) * (W3s x)) with
+ * shared_w13 [2 I_s, H], shared_w2 [H, I_s] ("Expert Parallel" Step 5 shared_mlp;
+ * shared experts of recursive_replace). MOE_EINVAL if p->shared_intermediate_size == 0.
+ *  ws: device scratch, at least moe_workspace_size(p, T, 0) bytes.
+ */
+int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,
+                   const void* shared_w13, const void* shared_w2, void* shared_y, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine back to token order, without atomics:
+ *   out[t] = sum_{j < k, pair_row[t*k+j] >= 0} topk_w[t*k+j] * y[pair_row[t*k+j]]
+ *            (+ shared_y[t] when shared_y != NULL)
+ * accumulated in fp32 in slot order and rounded once to dtype (the per-token scatter-add
+ * of _ep_forward Step 4; "+ shared_mlp" of "Expert Parallel" Step 5). Overwrites out.
+ */
+int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const int32_t* pair_row,
+                const float* topk_w, const void* shared_y, void* out, void* stream);
+
+/*
+ * The whole layer on this share: moe_route -> moe_align_permute -> moe_grouped_mlp
+ * (-> moe_shared_mlp) -> moe_combine, all on `stream`, with the granule of
+ * moe_pick_block_m. out [T, H] = this share's partial sum; summing the outputs of all
+ * disjoint shares (the shared expert passed to exactly one of them) gives the full layer.
+ * A share that receives no pairs writes zeros (plus the shared expert).
+ *  shared_w13 / shared_w2: both NULL (no shared expert on this share) or both given
+ *    (then p->shared_intermediate_size > 0).
+ *  topk_ids_out / topk_w_out: optional [T, k] copies of the routing (NULL = not wanted).
+ *  ws: device scratch of at least moe_workspace_size(p, T, 0) bytes.
+ */
+int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+                const float* logit_bias, const int32_t* expert_map, const void* w13,
+                const void* w2, const void* shared_w13, const void* shared_w2, void* out,
+                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXPERT_MOE_AMD_MOE_H */

@@ -1,0 +1,159 @@
+"""Host-side checks of the C-ABI library (CPU only: nothing here launches a kernel).
+
+The library loads, exports every entry point include/moe.h declares, and its host logic
+(parameter checks, shares, memory arithmetic, workspace sizing, argument errors) behaves
+as the header states. Entry points are only called on paths that return before any HIP
+call (T = 0, invalid arguments, too-small workspaces).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import expert_moe_amd as moe
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a non-NULL device address that the host never dereferences
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(moe.LIB_PATH):
+        from expert_moe_amd.build import build
+        build(verbose=False)
+    return moe.lib()
+
+
+def _params(w: wl.Workload, **over):
+    kw = dict(num_experts=w.num_experts, top_k=w.top_k, hidden_size=w.hidden_size,
+              intermediate_size=w.intermediate_size, renormalize=w.renormalize,
+              use_grouped_topk=w.use_grouped_topk, num_expert_group=w.num_expert_group,
+              topk_group=w.topk_group, routed_scaling_factor=w.routed_scaling_factor,
+              num_local_experts=w.num_local_experts,
+              shared_intermediate_size=w.shared_intermediate_size, dtype=w.dtype)
+    kw.update(over)
+    return moe.make_params(**kw)
+
+
+def test_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\**\s+\**(moe_[a-z_]+)\(", text, re.M))
+    assert declared == set(moe.EXPORTS)
+    h = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared:
+        assert hasattr(h, name), name
+
+
+def test_strerror():
+    assert moe.strerror(0) == "ok"
+    for c in (-1, -2, -3, -4, 7):
+        assert moe.strerror(c)
+
+
+@pytest.mark.parametrize("key", sorted(wl.WORKLOADS))
+def test_workload_params_valid(key):
+    w = wl.WORKLOADS[key]
+    p = _params(w)
+    assert moe.moe_check_params(p) == moe.MOE_OK
+    for T in w.tokens:
+        bm = moe.moe_pick_block_m(p, T)
+        assert bm in (16, 32, 64, 128)
+        assert moe.moe_sorted_capacity(p, T, bm) == T * w.top_k + w.num_local_experts * (bm - 1)
+        assert moe.moe_workspace_size(p, T) > 0
+
+
+def test_param_errors():
+    w = wl.WORKLOADS["dsv2"]
+    E = moe.MOE_EINVAL
+    cases = [
+        (dict(top_k=0), E), (dict(top_k=161), E), (dict(hidden_size=100), E),
+        (dict(intermediate_size=0), E), (dict(renormalize=True, num_local_experts=0), E),
+        (dict(num_local_experts=161), E), (dict(num_expert_group=7), E),
+        (dict(topk_group=9), E), (dict(topk_group=0), E), (dict(top_k=61, topk_group=3), E),
+        (dict(shared_intermediate_size=100), E),
+        (dict(routed_scaling_factor=float("inf")), E),
+        (dict(num_experts=320, num_expert_group=8), moe.MOE_EUNSUPPORTED),
+        (dict(dtype=7), moe.MOE_EUNSUPPORTED),
+    ]
+    for over, want in cases:
+        p = _params(w, **over)
+        if over.get("dtype") == 7:
+            p.dtype = 7
+        assert moe.moe_check_params(p) == want, over
+
+
+def test_expert_map_shares():
+    for key, w in wl.WORKLOADS.items():
+        got = moe.moe_make_expert_map(w.num_experts, w.ep_size, w.ep_rank)
+        assert np.array_equal(got, wl.expert_map(w)), key
+    # every global expert lands in exactly one share, with consecutive slots
+    maps = [moe.moe_make_expert_map(64, 8, r) for r in range(8)]
+    owned = np.stack([m >= 0 for m in maps])
+    assert np.all(owned.sum(axis=0) == 1)
+    for r, m in enumerate(maps):
+        assert m[owned[r]].tolist() == list(range(8))
+    for bad in [(8, 9, 0), (8, 3, 0), (8, 4, 4), (8, 4, -1), (0, 1, 0), (8, 0, 0)]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_make_expert_map(*bad)
+        assert ei.value.code == moe.MOE_EINVAL
+
+
+def test_weight_bytes_matches_page_arithmetic():
+    GiB = 2 ** 30
+    assert moe.moe_weight_bytes(256, 2048, 256, 2, 30) == 22.5 * GiB
+    assert moe.moe_weight_bytes(64, 2048, 512, 2, 30) == 11.25 * GiB
+    assert moe.moe_weight_bytes(256, 2048, 512, 2, 30) == 45 * GiB
+    assert moe.moe_weight_bytes(-1, 1, 1, 1, 1) == -1
+
+
+def test_workspace_grows_with_tokens():
+    p = _params(wl.WORKLOADS["skewed"])
+    sizes = [moe.moe_workspace_size(p, T, 128) for T in (1, 256, 4096, 16384)]
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_size(p, 16, 48)
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_size(p, -1)
+
+
+def test_entry_points_zero_tokens_are_noops():
+    p = _params(wl.WORKLOADS["mixtral"])
+    moe.moe_forward(p, 0, None, None, None, None, None, None, None, None, None, None, None,
+                    None, stream=0)
+    moe.moe_route(p, 0, None, None, None, None, None, None, None, None, stream=0)
+    moe.moe_align_permute(p, 0, None, 16, None, None, None, None, None, stream=0)
+    moe.moe_grouped_mlp(p, 0, None, None, None, None, None, None, 16, None, None, stream=0)
+    moe.moe_combine(p, 0, None, None, None, None, None, stream=0)
+
+
+def test_entry_point_argument_errors():
+    p = _params(wl.WORKLOADS["dsv2"])
+    L = moe.lib()
+    pp = ctypes.byref(p)
+    T = 64
+    ws = moe.moe_workspace_size(p, T)
+    F = FAKE
+    # missing required pointers
+    assert L.moe_forward(pp, T, None, F, None, F, F, F, None, None, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, F, F, None, None, F, F, None, None, F, None, None, F, ws, None) == -1
+    # only one of the two shared-expert pointers
+    assert L.moe_forward(pp, T, F, F, None, F, F, F, F, None, F, None, None, F, ws, None) == -1
+    # workspace too small
+    assert L.moe_forward(pp, T, F, F, None, F, F, F, F, F, F, None, None, F, ws - 1, None) == -3
+    # negative token count
+    assert L.moe_forward(pp, -1, F, F, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
+    # bad block_m for the split entry points
+    assert L.moe_align_permute(pp, T, F, 48, F, F, F, F, F, ws, None) == -1
+    assert L.moe_grouped_mlp(pp, T, F, F, F, F, F, F, 0, F, F, ws, None) == -1
+    assert L.moe_align_permute(pp, T, F, 16, F, F, F, F, F, 8, None) == -3
+    assert L.moe_route(pp, T, F, F, None, F, F, F, F, F, 8, None) == -3
+    # shared MLP on a share without a shared expert
+    p2 = _params(wl.WORKLOADS["ep_share"])
+    assert L.moe_shared_mlp(ctypes.byref(p2), T, F, F, F, F, F, ws, None) == -1
+    # shared expert pointers given but the params say there is none
+    assert L.moe_forward(ctypes.byref(p2), T, F, F, None, F, F, F, F, F, F, None, None, F,
+                         moe.moe_workspace_size(p2, T), None) == -1

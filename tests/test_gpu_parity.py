@@ -1,0 +1,217 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small layers span several tiles with ragged tails and run the oracle on every token; the
+five full-size layers compare routing on every token and outputs on >= 512 seeded tokens
+that cover every local expert (all tokens where the layer is small). The comparison rules
+are those of ``moe_case``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_moe_amd as moe
+import oracle
+import workloads as wl
+from moe_case import (OUT_TOL, Layer, check_routing, dev_tensor, params, reference_routing,
+                      rel_err, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+W = wl.Workload
+SMALL = {
+    # fp32, every expert local, rows per expert ~16 (granule 16)
+    "tiny_ragged": (W("tiny_ragged", 1, "tiny fp32, ragged T", "f32", (37,), 128, 8, 256, 2, True), 37),
+    "tiny": (wl.WORKLOADS["tiny"], 64),
+    # bf16 granule 64: 25 rows per expert
+    "mix_s": (W("mix_s", 11, "small Mixtral-like", "bf16", (100,), 512, 8, 384, 2, True), 100),
+    # EP share of 64 experts, granule 64
+    "ep_s": (W("ep_s", 12, "small EP share", "bf16", (300,), 256, 64, 128, 8, True,
+               ep_size=4, ep_rank=1), 300),
+    # grouped routing, no renormalise, rsf 16, shared expert, H % 128 == 64 (64-row B tiles)
+    "ds_s": (W("ds_s", 13, "small grouped", "bf16", (200,), 320, 32, 192, 6, False,
+               use_grouped_topk=True, num_expert_group=8, topk_group=3,
+               routed_scaling_factor=16.0, ep_size=8, ep_rank=0,
+               shared_intermediate_size=384), 200),
+    # skewed routing with a shared expert: decode-sized and prefill-sized token counts
+    "skew_s1": (W("skew_s", 14, "small skewed", "bf16", (1, 7, 600), 256, 64, 256, 8, True,
+                  ep_size=8, ep_rank=0, shared_intermediate_size=256, zipf_bias=1.2), 1),
+    "skew_s7": (W("skew_s", 14, "small skewed", "bf16", (1, 7, 600), 256, 64, 256, 8, True,
+                  ep_size=8, ep_rank=0, shared_intermediate_size=256, zipf_bias=1.2), 7),
+    "skew_s600": (W("skew_s", 14, "small skewed", "bf16", (1, 7, 600), 256, 64, 256, 8, True,
+                    ep_size=8, ep_rank=0, shared_intermediate_size=256, zipf_bias=1.2), 600),
+    # granule 128: 250 rows per expert, ragged
+    "mix_m": (W("mix_m", 15, "medium Mixtral-like", "bf16", (1000,), 256, 8, 256, 2, True), 1000),
+}
+
+
+def _full_check(layer: Layer, rows=None, with_shared=True):
+    w = layer.w
+    out, ids, tw = layer.forward(with_shared=with_shared)
+    ref = layer.oracle_route()
+    mism, near = check_routing(w, ids, tw, ref)
+    if rows is None:
+        rows = np.arange(layer.T)
+    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows], with_shared)
+    err = rel_err(out[rows], want)
+    print(f"[{w.key} T={layer.T}] rel_err={err:.3e} near_ties={near} exempt_mismatch={mism.size} "
+          f"checked_rows={len(rows)}", flush=True)
+    assert err <= OUT_TOL[w.dtype], err
+    return out, ids, tw
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_forward_small(case):
+    w, T = SMALL[case]
+    _full_check(Layer(w, T))
+
+
+FULL = [(k, T) for k in ("tiny", "mixtral", "ep_share", "dsv2", "skewed")
+        for T in wl.WORKLOADS[k].tokens]
+
+
+@pytest.mark.parametrize("key,T", FULL, ids=[f"{k}-T{T}" for k, T in FULL])
+def test_forward_full_size(key, T):
+    w = wl.WORKLOADS[key]
+    layer = Layer(w, T)
+    out, ids, tw = layer.forward()
+    ref = layer.oracle_route()
+    mism, near = check_routing(w, ids, tw, ref)
+    rows = np.arange(T) if T <= 256 else sample_rows(ids, layer.emap, T)
+    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows])
+    err = rel_err(out[rows], want)
+    print(f"[{key} T={T}] rel_err={err:.3e} near_ties={near} exempt_mismatch={mism.size} "
+          f"rows={len(rows)}", flush=True)
+    assert err <= OUT_TOL[w.dtype], err
+
+
+def test_repeated_calls_bit_identical():
+    w, T = SMALL["ep_s"]
+    layer = Layer(w, T)
+    a = layer.forward()
+    b = layer.forward()
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("case,ep", [("ep_s", 4), ("ds_s", 8), ("skew_s600", 8), ("tiny", 4)])
+def test_share_sum_equals_all_local(case, ep):
+    """Sum of every disjoint share's output (shared expert on rank 0) = the all-local layer."""
+    w0, T = SMALL[case]
+    total = None
+    for r in range(ep):
+        layer = Layer(w0.with_share(ep, r), T)
+        out, _, _ = layer.forward()
+        total = out.astype(np.float64) if total is None else total + out
+    full_w = w0.with_share(1, 0)
+    full = Layer(full_w, T)
+    ref = full.oracle_route()
+    out_full, ids, tw = full.forward()
+    mism, _ = check_routing(full_w, ids, tw, ref)
+    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    want = full.oracle_out(np.arange(T), ids_ref, w_ref)
+    assert rel_err(total, want) <= OUT_TOL[w0.dtype]
+    assert rel_err(total, out_full) <= OUT_TOL[w0.dtype]
+
+
+def test_share_without_local_pairs():
+    """A share that receives no pairs writes zeros, plus the shared expert when it carries it."""
+    w0, T = SMALL["skew_s1"]
+    layer = Layer(w0, T)
+    _, ids, _ = layer.forward()
+    used = set(ids.reshape(-1).tolist())
+    n = w0.num_experts // 8
+    empty = [r for r in range(8) if not used & set(range(r * n, (r + 1) * n))]
+    assert empty, "the skewed single token should leave some share without pairs"
+    r = empty[-1]
+    lone = Layer(w0.with_share(8, r, shared=False), T)
+    out, _, _ = lone.forward()
+    assert np.all(out == 0.0)
+    with_sh = Layer(w0.with_share(8, r, shared=True), T)
+    out2, _, _ = with_sh.forward()
+    want = oracle.gated_mlp(wl.to_f32(with_sh.x), wl.to_f32(with_sh.sw13), wl.to_f32(with_sh.sw2))
+    assert rel_err(out2, want) <= OUT_TOL["bf16"]
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("case", ["ds_s", "tiny_ragged"])
+def test_split_entry_points(case, block_m):
+    """route -> align_permute -> grouped_mlp (-> shared_mlp) -> combine, any granule."""
+    w, T = SMALL[case]
+    layer = Layer(w, T)
+    p = params(w)
+    d = layer.d
+    dev = d["x"].device
+    k, H = w.top_k, w.hidden_size
+    ws = torch.empty(moe.moe_workspace_size(p, T, block_m), dtype=torch.uint8, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    local = torch.empty(T, k, dtype=torch.int32, device=dev)
+    moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws)
+    cap = moe.moe_sorted_capacity(p, T, block_m)
+    sp = torch.full((cap,), 7, dtype=torch.int32, device=dev)
+    be = torch.full((cap // block_m + 1,), -5, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_align_permute(p, T, local, block_m, sp, be, pr, npad, ws)
+    torch.cuda.synchronize()
+    # alignment is integer work: bit-exact against the oracle on the same topk_local
+    a = oracle.align_permute(local.cpu().numpy(), w.num_local_experts, block_m)
+    n = int(npad.item())
+    assert n == a["num_padded"]
+    assert np.array_equal(sp.cpu().numpy()[:n], a["sorted_pairs"])
+    assert np.array_equal(be.cpu().numpy()[:n // block_m], a["block_expert"])
+    assert np.array_equal(pr.cpu().numpy(), a["pair_row"])
+    y = torch.empty(cap, H, dtype=d["x"].dtype, device=dev)
+    moe.moe_grouped_mlp(p, T, d["x"], d["w13"], d["w2"], sp, be, npad, block_m, y, ws)
+    sy = None
+    if d["sw13"] is not None:
+        sy = torch.empty(T, H, dtype=d["x"].dtype, device=dev)
+        moe.moe_shared_mlp(p, T, d["x"], d["sw13"], d["sw2"], sy, ws)
+    out = torch.empty(T, H, dtype=d["x"].dtype, device=dev)
+    moe.moe_combine(p, T, y, pr, tw, sy, out)
+    torch.cuda.synchronize()
+    ids_h, tw_h = ids.cpu().numpy(), tw.cpu().numpy()
+    ref = layer.oracle_route()
+    mism, _ = check_routing(w, ids_h, tw_h, ref)
+    ids_ref, w_ref = reference_routing(ids_h, tw_h, ref, mism)
+    want = layer.oracle_out(np.arange(T), ids_ref, w_ref)
+    assert rel_err(out.float().cpu().numpy(), want) <= OUT_TOL[w.dtype]
+    # y rows of a few pairs against the oracle's expert MLP
+    y_h = y.float().cpu().numpy()
+    rows = [r for r in range(n) if a["sorted_pairs"][r] >= 0][:: max(1, n // 16)]
+    for r in rows:
+        pid = a["sorted_pairs"][r]
+        s = a["block_expert"][r // block_m]
+        want_y = oracle.gated_mlp(wl.to_f32(layer.x[pid // k])[None], wl.to_f32(layer.w13[s]),
+                                  wl.to_f32(layer.w2[s]))[0]
+        assert rel_err(y_h[r], want_y) <= OUT_TOL[w.dtype] * 2
+
+
+def test_external_routing_through_align():
+    """Caller-provided slots (external routing) go through align + MLP + combine."""
+    w, T = SMALL["mix_s"]
+    layer = Layer(w, T)
+    p = params(w)
+    d = layer.d
+    dev = d["x"].device
+    k = w.top_k
+    r = layer.oracle_route()
+    local = dev_tensor(layer.emap[r["ids"]].astype(np.int32))
+    tw = dev_tensor(r["weights"])
+    bm = 64
+    ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
+    cap = moe.moe_sorted_capacity(p, T, bm)
+    sp = torch.empty(cap, dtype=torch.int32, device=dev)
+    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
+    y = torch.empty(cap, w.hidden_size, dtype=d["x"].dtype, device=dev)
+    moe.moe_grouped_mlp(p, T, d["x"], d["w13"], d["w2"], sp, be, npad, bm, y, ws)
+    out = torch.empty(T, w.hidden_size, dtype=d["x"].dtype, device=dev)
+    moe.moe_combine(p, T, y, pr, tw, None, out)
+    torch.cuda.synchronize()
+    want = layer.oracle_out(np.arange(T), r["ids"], r["weights"])
+    assert rel_err(out.float().cpu().numpy(), want) <= OUT_TOL["bf16"]
