@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer forward on one MI355X.
+
+Metric: MoE-layer tokens/s on one GPU, with the dominant kernel's achieved fraction of
+the MI355X roofline (bf16 MFMA peak 2.5 PFLOP/s for large-token shapes, HBM 8 TB/s for
+weight-streaming shapes).
+
+Default workload: the Mixtral-shaped layer (bf16, H 4096, 8 experts of I 14336, top-2
+renormalised softmax routing, every expert local) at 4096 tokens (prefill); the same
+layer at 32 tokens (decode) is reported in the ``decode`` field of the same line. A step
+is one ``moe_forward`` over the batch (router GEMM, softmax/top-k, align/permute, grouped
+gate/up and down GEMMs, combine); inputs are resident in HBM before timing starts.
+
+The dominant kernel's duration comes from HIP events recorded on the launch stream
+around ``moe_expert_gate_up`` in a second timed loop that runs the same kernels through
+the split entry points. The oracle (CPU, float64 expert MLPs) is timed on a bounded
+sample of tokens of the same workload as the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+                       [--tokens T] [--cpu-sample S | --no-cpu-baseline] [--copy-probe]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--tokens", type=int, default=None, help="token count (default: the largest)")
+    ap.add_argument("--decode-tokens", type=int, default=None,
+                    help="second, small token count reported as 'decode' (default: the smallest)")
+    ap.add_argument("--cpu-sample", type=int, default=96, help="tokens the oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Bench:
+    """Device inputs, outputs and workspace of one (workload, T) point."""
+
+    def __init__(self, w, T, host):
+        import torch
+
+        import expert_moe_amd as moe
+        self.w, self.T, self.moe, self.torch = w, T, moe, torch
+        dev = "cuda"
+        self.p = moe.make_params(w.num_experts, w.top_k, w.hidden_size, w.intermediate_size,
+                                 w.renormalize, w.use_grouped_topk, w.num_expert_group,
+                                 w.topk_group, w.routed_scaling_factor, w.num_local_experts,
+                                 w.shared_intermediate_size, w.dtype)
+        self.d = host.device_tensors(T)
+        dt = self.d["x"].dtype
+        k, H = w.top_k, w.hidden_size
+        self.out = torch.empty(T, H, dtype=dt, device=dev)
+        self.ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        self.tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(moe.moe_workspace_size(self.p, T), dtype=torch.uint8, device=dev)
+        # split-path buffers (same kernels as moe_forward)
+        self.bm = moe.moe_pick_block_m(self.p, T)
+        cap = moe.moe_sorted_capacity(self.p, T, self.bm)
+        self.local = torch.empty(T, k, dtype=torch.int32, device=dev)
+        self.sp = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.be = torch.empty(cap // self.bm + 1, dtype=torch.int32, device=dev)
+        self.pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+        self.npad = torch.empty(1, dtype=torch.int32, device=dev)
+        self.act = torch.empty(cap, w.intermediate_size, dtype=dt, device=dev)
+        self.y = torch.empty(cap, H, dtype=dt, device=dev)
+        self.sy = torch.empty(T, H, dtype=dt, device=dev) if w.shared_intermediate_size else None
+        self.sws = torch.empty(moe.moe_workspace_size(self.p, T, self.bm), dtype=torch.uint8,
+                               device=dev)
+
+    def forward(self):
+        d = self.d
+        self.moe.moe_forward(self.p, self.T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
+                             d["w2"], d["sw13"], d["sw2"], self.out, self.ids, self.tw, self.ws)
+
+    def split_step(self, ev=None):
+        """The same kernels as moe_forward through the split entry points; events at stage ends."""
+        m, d, p, T = self.moe, self.d, self.p, self.T
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        m.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], self.ids, self.tw, self.local,
+                    self.sws)
+        rec(1)
+        m.moe_align_permute(p, T, self.local, self.bm, self.sp, self.be, self.pr, self.npad, self.sws)
+        rec(2)
+        m.moe_expert_gate_up(p, T, d["x"], d["w13"], self.sp, self.be, self.npad, self.bm, self.act)
+        rec(3)
+        m.moe_expert_down(p, T, self.act, d["w2"], self.be, self.npad, self.bm, self.y)
+        rec(4)
+        if self.sy is not None:
+            m.moe_shared_mlp(p, T, d["x"], d["sw13"], d["sw2"], self.sy, self.sws)
+        rec(5)
+        m.moe_combine(p, T, self.y, self.pr, self.tw, self.sy, self.out)
+        rec(6)
+
+
+class HostLayer:
+    """Seeded host inputs of the largest token count; device copies per token count."""
+
+    def __init__(self, w, T_max):
+        import workloads as wl
+        self.w = w
+        self.x = wl.x(w, T_max)
+        self.gate = wl.gate(w)
+        self.bias = wl.logit_bias(w)
+        self.emap = wl.expert_map(w)
+        self.w13, self.w2 = wl.local_expert_weights(w)
+        self.sw13, self.sw2 = wl.shared_weights(w)
+        self._dev = None
+
+    def _weights_on_device(self):
+        if self._dev is None:
+            self._dev = {k: _dev(getattr(self, k)) for k in
+                         ("gate", "bias", "emap", "w13", "w2", "sw13", "sw2")}
+        return self._dev
+
+    def device_tensors(self, T):
+        d = dict(self._weights_on_device())
+        d["x"] = _dev(self.x[:T])
+        return d
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def algorithmic(w, T, ids):
+    """Algorithmic work of one step from the actual routing (ids: numpy [T, k])."""
+    import numpy as np
+    import workloads as wl
+    emap = wl.expert_map(w)
+    slots = emap[ids]
+    A = int((slots >= 0).sum())
+    counts = np.bincount(slots[slots >= 0], minlength=w.num_local_experts)
+    touched = int((counts > 0).sum())
+    H, I, E, Is = w.hidden_size, w.intermediate_size, w.num_experts, w.shared_intermediate_size
+    eb = 2 if w.dtype == "bf16" else 4
+    flops = 2 * T * H * E + 6 * A * H * I + 6 * T * H * Is
+    bytes_ = (touched * 3 * H * I + 3 * H * Is + E * H + 2 * T * H) * eb
+    gate_up_flops = 4 * A * H * I
+    gate_up_bytes = (touched * 2 * I * H + T * H + A * I) * eb
+    return {"assignments": A, "touched_experts": touched, "flops": flops, "bytes": bytes_,
+            "gate_up_flops": gate_up_flops, "gate_up_bytes": gate_up_bytes,
+            "rows_per_expert_min": int(counts.min()), "rows_per_expert_max": int(counts.max())}
+
+
+def run_point(host, w, T, steps, warmup):
+    import torch
+    b = Bench(w, T, host)
+    for _ in range(warmup):
+        b.forward()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.forward()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ids = b.ids.cpu().numpy()
+    alg = algorithmic(w, T, ids)
+
+    # second timed loop: same kernels, HIP events on the launch stream at stage ends
+    b.split_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        b.split_step(evs[i])
+    torch.cuda.synchronize()
+    split_ms = (time.perf_counter() - t0) * 1e3 / steps
+    names = ["route", "align", "gate_up", "down", "shared", "combine"]
+    stage = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, n in enumerate(names)}
+    return b, ms, split_ms, stage, alg
+
+
+def roofline(alg, stage_ms, bound):
+    sec = stage_ms["gate_up"] * 1e-3
+    if bound == "mfma":
+        achieved = alg["gate_up_flops"] / sec / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "moe_expert_gate_up (silu(x W1^T) * (x W3^T), grouped bf16 MFMA)",
+                "per_launch": f"4*A*H*I = {alg['gate_up_flops']} FLOP", "avg_ms": round(stage_ms["gate_up"], 4)}
+    achieved = alg["gate_up_bytes"] / sec / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "moe_expert_gate_up (weight-streaming bf16 MFMA)",
+            "per_launch": f"touched w13 + x + act = {alg['gate_up_bytes']} B",
+            "avg_ms": round(stage_ms["gate_up"], 4)}
+
+
+def cpu_baseline(host, w, sample):
+    """The oracle, as it stands, on `sample` tokens of the workload (CPU, float64 MLPs)."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    x = wl.to_f32(host.x[:sample])
+    t0 = time.perf_counter()
+    r = oracle.route(x, wl.to_f32(host.gate), w.top_k, w.renormalize, w.use_grouped_topk,
+                     w.num_expert_group, w.topk_group, w.routed_scaling_factor, host.bias)
+
+    class Lazy:
+        def __init__(self, a):
+            self.a = a
+
+        def __getitem__(self, s):
+            return wl.to_f32(self.a[s])
+
+    sh = (wl.to_f32(host.sw13), wl.to_f32(host.sw2)) if host.sw13 is not None else (None, None)
+    oracle.moe_forward_given_routing(x, r["ids"], r["weights"], host.emap, Lazy(host.w13),
+                                     Lazy(host.w2), sh[0], sh[1])
+    dt = time.perf_counter() - t0
+    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {sample} tokens of the same layer (routing + every local expert MLP "
+                      f"in float64), whole-step time"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: each expert-parallel share is benchmarked on its own GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as wl
+    w = wl.WORKLOADS[args.workload]
+    T = args.tokens or max(w.tokens)
+    Td = args.decode_tokens or min(w.tokens)
+    print(f"[bench] generating inputs for {w.key} (T={T})", file=sys.stderr, flush=True)
+    host = HostLayer(w, max(T, Td))
+    torch.cuda.init()
+    print("[bench] timing", file=sys.stderr, flush=True)
+    b, ms, split_ms, stage, alg = run_point(host, w, T, args.steps, args.warmup)
+    bound = "mfma" if alg["gate_up_flops"] / max(alg["gate_up_bytes"], 1) > 312 else "hbm"
+    res = {
+        "metric": "MoE-layer tokens/s on 1 MI355X",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": f"{w.desc}, T={T}", "tokens": T, "hidden": w.hidden_size,
+                   "experts": w.num_experts, "local_experts": w.num_local_experts,
+                   "intermediate": w.intermediate_size, "top_k": w.top_k,
+                   "shared_intermediate": w.shared_intermediate_size, "block_m": b.bm},
+        "achieved_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
+        "achieved_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "roofline": roofline(alg, stage, bound),
+        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "split_path_ms_per_step": round(split_ms, 4),
+        "work": alg,
+    }
+    del b
+    if Td != T:
+        bd, msd, split_d, stage_d, alg_d = run_point(host, w, Td, max(args.steps, 20), args.warmup)
+        bound_d = "mfma" if alg_d["gate_up_flops"] / max(alg_d["gate_up_bytes"], 1) > 312 else "hbm"
+        res["decode"] = {"tokens": Td, "value": round(Td / (msd * 1e-3), 1), "unit": "tokens/s",
+                         "ms_per_step": round(msd, 4),
+                         "achieved_gbs": round(alg_d["bytes"] / (msd * 1e-3) / 1e9, 1),
+                         "hbm_frac_whole_step": round(alg_d["bytes"] / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "roofline": roofline(alg_d, stage_d, bound_d),
+                         "stages_ms": {k: round(v, 4) for k, v in stage_d.items()}, "work": alg_d}
+        del bd
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = 1 << 30
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(host, w, min(args.cpu_sample, T))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,8 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = (
     "moe_strerror", "moe_check_params", "moe_pick_block_m", "moe_sorted_capacity",
     "moe_workspace_size", "moe_make_expert_map", "moe_weight_bytes", "moe_route",
-    "moe_align_permute", "moe_grouped_mlp", "moe_shared_mlp", "moe_combine", "moe_forward",
+    "moe_align_permute", "moe_grouped_mlp", "moe_expert_gate_up", "moe_expert_down",
+    "moe_shared_mlp", "moe_combine", "moe_forward",
 )
 
 
@@ -81,6 +82,8 @@ _SIGS = {
     "moe_align_permute": ([_P, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_grouped_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                         ctypes.c_int),
+    "moe_expert_gate_up": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
+    "moe_expert_down": ([_P, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "moe_shared_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_combine": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_forward": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -194,6 +197,19 @@ def moe_grouped_mlp(p, num_tokens, x, w13, w2, sorted_pairs, block_expert, num_p
     _check(lib().moe_grouped_mlp(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(w2),
                                  _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
                                  block_m, _ptr(y), wp, wn, _stream(stream)), "moe_grouped_mlp")
+
+
+def moe_expert_gate_up(p, num_tokens, x, w13, sorted_pairs, block_expert, num_padded, block_m,
+                       act, stream=None):
+    _check(lib().moe_expert_gate_up(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13),
+                                    _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
+                                    block_m, _ptr(act), _stream(stream)), "moe_expert_gate_up")
+
+
+def moe_expert_down(p, num_tokens, act, w2, block_expert, num_padded, block_m, y, stream=None):
+    _check(lib().moe_expert_down(ctypes.byref(p), num_tokens, _ptr(act), _ptr(w2),
+                                 _ptr(block_expert), _ptr(num_padded), block_m, _ptr(y),
+                                 _stream(stream)), "moe_expert_down")
 
 
 def moe_shared_mlp(p, num_tokens, x, shared_w13, shared_w2, shared_y, ws, stream=None):

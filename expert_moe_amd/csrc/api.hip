@@ -229,6 +229,35 @@ int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, cons
                          as_stream(stream));
 }
 
+int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
+                       const int32_t* sorted_pairs, const int32_t* block_expert,
+                       const int32_t* num_padded, int32_t block_m, void* act, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x || !w13 || !sorted_pairs || !block_expert || !num_padded || !act) return MOE_EINVAL;
+  const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
+  return moe::launch_gate_up(*p, static_cast<int>(num_tokens), x, w13, p->intermediate_size,
+                             sorted_pairs, num_padded, block_expert, block_m, rows, act,
+                             as_stream(stream));
+}
+
+int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, const void* w2,
+                    const int32_t* block_expert, const int32_t* num_padded, int32_t block_m,
+                    void* y, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (num_tokens == 0) return MOE_OK;
+  if (!act || !w2 || !block_expert || !num_padded || !y) return MOE_EINVAL;
+  const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
+  return moe::launch_down(*p, static_cast<int>(num_tokens), act, w2, p->intermediate_size,
+                          num_padded, block_expert, block_m, rows, y, as_stream(stream));
+}
+
 int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,
                    const void* shared_w13, const void* shared_w2, void* shared_y, void* ws,
                    size_t ws_bytes, void* stream) {

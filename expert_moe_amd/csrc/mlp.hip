@@ -35,71 +35,97 @@ void launch_tile64(const GemmArgs& a, int n_rows_b, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+
+// Rows per tile: the sorted granule when rows are expert-sorted, else by row count.
+int tile_rows(const moe_params& p, bool sorted, int block_m, int rows) {
+  if (p.dtype == MOE_F32) return 16;
+  if (sorted) return block_m <= 32 ? 16 : block_m;
+  return rows <= 64 ? 16 : 128;
+}
+
+GemmArgs base_args(const moe_params& p, int T, const int32_t* num_padded,
+                   const int32_t* block_expert, int block_m, int rows) {
+  GemmArgs a{};
+  a.row_div = p.top_k;
+  a.M_pairs = T * p.top_k;
+  a.M_rows = rows;
+  a.num_padded = num_padded;
+  a.block_expert = block_expert;
+  a.block_m = block_m > 0 ? block_m : 1;
+  return a;
+}
+
+}  // namespace
+
+int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, int inter,
+                   const int32_t* row_map, const int32_t* num_padded,
+                   const int32_t* block_expert, int block_m, int rows, void* act, hipStream_t s) {
+  const int H = p.hidden_size;
+  const int I = inter;
+  // act[r, :] = silu(x[src(r)] W1^T) * (x[src(r)] W3^T), B = w13 [2I, H] per slot.
+  GemmArgs g = base_args(p, T, num_padded, block_expert, block_m, rows);
+  g.A = x;
+  g.row_map = row_map;
+  g.B = w13;
+  g.b_stride = static_cast<int64_t>(2) * I * H;
+  g.K = H;
+  g.N = I;
+  g.N_valid = I;
+  g.C = act;
+  g.ldc = I;
+  const int tr = tile_rows(p, row_map != nullptr, block_m, rows);
+  g.m_blocks = ceil_div(rows, tr);
+  if (p.dtype == MOE_F32)
+    gemm_f32_tile<kSiluMul><<<g.m_blocks * (I / 32), 256, 0, s>>>(g);
+  else if (tr == 16)
+    gemm_bf16_stream<4, kSiluMul><<<g.m_blocks * (I / 32), 256, 0, s>>>(g);
+  else if (tr == 64)
+    launch_tile64<kSiluMul>(g, 2 * I, s);
+  else
+    launch_tile128<kSiluMul>(g, 2 * I, s);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
+                const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
+                void* y, hipStream_t s) {
+  const int H = p.hidden_size;
+  const int I = inter;
+  // y[r, :] = act[r] W2^T, B = w2 [H, I] per slot; act rows are already in order.
+  GemmArgs g = base_args(p, T, num_padded, block_expert, block_m, rows);
+  g.A = act;
+  g.row_map = nullptr;
+  g.B = w2;
+  g.b_stride = static_cast<int64_t>(H) * I;
+  g.K = I;
+  g.N = H;
+  g.N_valid = H;
+  g.C = y;
+  g.ldc = H;
+  const int tr = tile_rows(p, num_padded != nullptr, block_m, rows);
+  g.m_blocks = ceil_div(rows, tr);
+  if (p.dtype == MOE_F32)
+    gemm_f32_tile<kStore><<<g.m_blocks * (H / 64), 256, 0, s>>>(g);
+  else if (tr == 16)
+    gemm_bf16_stream<4, kStore><<<g.m_blocks * (H / 64), 256, 0, s>>>(g);
+  else if (tr == 64)
+    launch_tile64<kStore>(g, H, s);
+  else
+    launch_tile128<kStore>(g, H, s);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const void* w2,
                int inter, const int32_t* row_map, const int32_t* num_padded,
                const int32_t* block_expert, int block_m, int rows, void* act, void* y,
                hipStream_t s) {
-  const int H = p.hidden_size;
-  const int I = inter;
-  // GEMM 1: act[r, :] = silu(x[src(r)] W1^T) * (x[src(r)] W3^T), B = w13 [2I, H] per slot.
-  GemmArgs g1{};
-  g1.A = x;
-  g1.row_map = row_map;
-  g1.row_div = p.top_k;
-  g1.M_pairs = T * p.top_k;
-  g1.M_rows = rows;
-  g1.num_padded = num_padded;
-  g1.block_expert = block_expert;
-  g1.block_m = block_m > 0 ? block_m : 1;
-  g1.B = w13;
-  g1.b_stride = static_cast<int64_t>(2) * I * H;
-  g1.K = H;
-  g1.N = I;
-  g1.N_valid = I;
-  g1.C = act;
-  g1.ldc = I;
-  // GEMM 2: y[r, :] = act[r] W2^T, B = w2 [H, I] per slot; act rows are already in order.
-  GemmArgs g2 = g1;
-  g2.A = act;
-  g2.row_map = nullptr;
-  g2.B = w2;
-  g2.b_stride = static_cast<int64_t>(H) * I;
-  g2.K = I;
-  g2.N = H;
-  g2.N_valid = H;
-  g2.C = y;
-  g2.ldc = H;
-
-  if (p.dtype == MOE_F32) {
-    g1.m_blocks = g2.m_blocks = ceil_div(rows, 16);
-    gemm_f32_tile<kSiluMul><<<g1.m_blocks * (I / 32), 256, 0, s>>>(g1);
-    MOE_LAUNCH_CHECK();
-    gemm_f32_tile<kStore><<<g2.m_blocks * (H / 64), 256, 0, s>>>(g2);
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-  }
-  // Rows per tile: the sorted granule when rows are expert-sorted, else by token count.
-  const int tile_rows = row_map ? (block_m <= 32 ? 16 : block_m) : (rows <= 64 ? 16 : 128);
-  if (tile_rows == 16) {
-    g1.m_blocks = g2.m_blocks = ceil_div(rows, 16);
-    gemm_bf16_stream<4, kSiluMul><<<g1.m_blocks * (I / 32), 256, 0, s>>>(g1);
-    MOE_LAUNCH_CHECK();
-    gemm_bf16_stream<4, kStore><<<g2.m_blocks * (H / 64), 256, 0, s>>>(g2);
-    MOE_LAUNCH_CHECK();
-  } else if (tile_rows == 64) {
-    g1.m_blocks = g2.m_blocks = ceil_div(rows, 64);
-    launch_tile64<kSiluMul>(g1, 2 * I, s);
-    MOE_LAUNCH_CHECK();
-    launch_tile64<kStore>(g2, H, s);
-    MOE_LAUNCH_CHECK();
-  } else {
-    g1.m_blocks = g2.m_blocks = ceil_div(rows, 128);
-    launch_tile128<kSiluMul>(g1, 2 * I, s);
-    MOE_LAUNCH_CHECK();
-    launch_tile128<kStore>(g2, H, s);
-    MOE_LAUNCH_CHECK();
-  }
-  return MOE_OK;
+  int rc = launch_gate_up(p, T, x, w13, inter, row_map, num_padded, block_expert, block_m, rows,
+                          act, s);
+  if (rc) return rc;
+  return launch_down(p, T, act, w2, inter, num_padded, block_expert, block_m, rows, y, s);
 }
 
 }  // namespace moe

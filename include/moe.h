@@ -147,7 +147,8 @@ int64_t moe_weight_bytes(int64_t n_experts, int64_t hidden, int64_t inter, int32
  *  x [T, H] dtype; w_gate [E, H] dtype; logit_bias [E] fp32 or NULL; expert_map [E].
  *  Outputs [T, k]: topk_ids (global ids, probability descending, ties to the lower id),
  *  topk_w (fp32), topk_local (expert_map[topk_ids], -1 = not local).
- *  ws: device scratch of at least moe_workspace_size(p, T, 0) bytes (logits live there).
+ *  ws: device scratch of at least moe_workspace_size(p, T, 0) bytes. On completion its
+ *  first T*E*4 bytes hold the fp32 router logits x . Wg^T [T, E] (without logit_bias).
  */
 int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
               const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
@@ -184,6 +185,22 @@ int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, cons
                     const void* w2, const int32_t* sorted_pairs, const int32_t* block_expert,
                     const int32_t* num_padded, int32_t block_m, void* y, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * The two stages of moe_grouped_mlp, for callers that want them apart (e.g. to time or
+ * overlap them). Same row rules as moe_grouped_mlp.
+ *  moe_expert_gate_up: act[r] = silu(W1_e x[p / k]) * (W3_e x[p / k]), act [capacity, I] dtype
+ *    (the gate/up projection and activation of the expert MLP).
+ *  moe_expert_down:    y[r] = W2_e act[r], y [capacity, H] dtype (the down projection).
+ * Neither needs a workspace.
+ */
+int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
+                       const int32_t* sorted_pairs, const int32_t* block_expert,
+                       const int32_t* num_padded, int32_t block_m, void* act, void* stream);
+
+int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, const void* w2,
+                    const int32_t* block_expert, const int32_t* num_padded, int32_t block_m,
+                    void* y, void* stream);
 
 /*
  * Shared expert on every token: shared_y [T, H] = W2s (silu(W1s x) * (W3s x)) with

@@ -47,7 +47,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "router_logits", "softmax_fp32", "select_experts", "routing_weights", "route",
+    "router_logits", "softmax_fp32", "select_experts", "routing_weights", "route_from_logits",
+    "route",
     "gated_mlp", "moe_forward_given_routing", "moe_forward", "moe_forward_per_token",
     "align_permute", "weight_bytes",
 ]
@@ -141,14 +142,22 @@ def routing_weights(p, ids, renormalize, routed_scaling_factor=1.0):
     return (w * np.float32(routed_scaling_factor)).astype(np.float32)
 
 
-def route(x, w_gate, top_k, renormalize, use_grouped_topk=False, num_expert_group=1,
-          topk_group=1, routed_scaling_factor=1.0, logit_bias=None):
-    """Router: logits -> fp32 softmax -> (grouped) top-k -> weights. Returns a dict."""
-    logits = router_logits(x, w_gate, logit_bias)
+def route_from_logits(logits, top_k, renormalize, use_grouped_topk=False, num_expert_group=1,
+                      topk_group=1, routed_scaling_factor=1.0):
+    """Softmax -> (grouped) top-k -> weights on given fp32 logits (bias already added)."""
     p = softmax_fp32(logits)
     ids, gap, ggap = select_experts(p, top_k, use_grouped_topk, num_expert_group, topk_group)
     w = routing_weights(p, ids, renormalize, routed_scaling_factor)
-    return {"logits": logits, "probs": p, "ids": ids, "weights": w, "gap": gap, "ggap": ggap}
+    return {"logits": np.asarray(logits, np.float32), "probs": p, "ids": ids, "weights": w,
+            "gap": gap, "ggap": ggap}
+
+
+def route(x, w_gate, top_k, renormalize, use_grouped_topk=False, num_expert_group=1,
+          topk_group=1, routed_scaling_factor=1.0, logit_bias=None):
+    """Router: logits -> fp32 softmax -> (grouped) top-k -> weights. Returns a dict."""
+    return route_from_logits(router_logits(x, w_gate, logit_bias), top_k, renormalize,
+                             use_grouped_topk, num_expert_group, topk_group,
+                             routed_scaling_factor)
 
 
 def gated_mlp(x, w13, w2):

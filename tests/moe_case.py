@@ -6,7 +6,10 @@ Comparison rules (fixed in the tests, not tuned to the kernels):
     k-th/(k+1)-th probability gap (or, for grouped routing, last-kept/first-dropped group
     gap) is below 1e-6; those are counted and their outputs are checked against the oracle
     fed the GPU's own ids and weights;
-  * routing weights of matching tokens: |gpu - oracle| <= 1e-6 * max(1, routed_scaling_factor);
+  * routing weights, in two stages derived from the arithmetic (see check_routing): the GPU's
+    fp32 logits against the oracle's correctly rounded ones within the recursive-summation
+    error bound, then the GPU's weights against the oracle's softmax / top-k / renormalise /
+    scale applied to those same GPU logits, |dw| <= 1e-6 * max(1, routed_scaling_factor);
   * outputs: max|out - ref| / max|ref| <= 2e-2 for bf16 and <= 1e-4 for fp32.
 """
 from __future__ import annotations
@@ -82,6 +85,27 @@ class Layer:
         torch.cuda.synchronize()
         return out.float().cpu().numpy(), ids.cpu().numpy(), tw.cpu().numpy()
 
+    def gpu_route(self):
+        """moe_route on the layer: (ids, weights, logits) as numpy arrays."""
+        w, T, d = self.w, self.T, self.d
+        p = params(w)
+        dev = d["x"].device
+        ids = torch.empty(T, w.top_k, dtype=torch.int32, device=dev)
+        tw = torch.empty(T, w.top_k, dtype=torch.float32, device=dev)
+        local = torch.empty(T, w.top_k, dtype=torch.int32, device=dev)
+        ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
+        moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws)
+        torch.cuda.synchronize()
+        logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts)
+        return ids.cpu().numpy(), tw.cpu().numpy(), logits.cpu().numpy()
+
+    def check_routing(self, ids, tw, ref):
+        """Routing rules on the forward's ids/weights, with moe_route's logits for the weights."""
+        r_ids, r_tw, logits = self.gpu_route()
+        assert np.array_equal(r_ids, ids) and np.array_equal(r_tw, tw), \
+            "moe_route and moe_forward disagree"
+        return check_routing(self.w, ids, tw, ref, logits, self.x, self.gate, self.bias)
+
     def oracle_route(self, rows=None):
         w = self.w
         x = wl.to_f32(self.x if rows is None else self.x[rows])
@@ -111,23 +135,47 @@ class _LazyF32:
         return len(self.a)
 
 
-def check_routing(w: wl.Workload, ids, weights, ref):
-    """Apply the routing comparison rules. Returns (exempt_mismatch_rows, n_near_ties)."""
+def check_routing(w: wl.Workload, ids, weights, ref, logits=None, x=None, gate=None, bias=None):
+    """Apply the routing comparison rules. Returns (exempt_mismatch_rows, n_near_ties).
+
+    ids: GPU ids vs the oracle's, as sets, bit-exact except on near-tie tokens.
+    weights (when the GPU logits are given): two stages derived from the arithmetic.
+      1. GPU logits vs the oracle's correctly rounded fp32 logits: recursive-summation bound
+         |dl| <= H * u * sum_h |x_h w_eh| + 2 u |l| (bias add, final rounding), u = 2^-24.
+      2. GPU weights vs the oracle's softmax / top-k / renormalise / scale applied to the GPU's
+         own logits: |dw| <= 1e-6 * max(1, rsf) (exp and summation-order rounding only).
+    """
     near = (ref["gap"] < TIE_GAP) | (ref["ggap"] < TIE_GAP)
     gs = np.sort(ids, axis=1)
     rs = np.sort(ref["ids"], axis=1)
     differ = np.any(gs != rs, axis=1)
     bad = np.nonzero(differ & ~near)[0]
     assert bad.size == 0, f"routing ids differ on {bad.size} tokens with a clear gap, e.g. {bad[:5]}"
-    same = ~differ
-    tol = TIE_GAP * max(1.0, abs(w.routed_scaling_factor))
-    # weights per matched id (slot order may differ only among equal probabilities)
-    o_g = np.argsort(ids[same], axis=1, kind="stable")
-    o_r = np.argsort(ref["ids"][same], axis=1, kind="stable")
-    wg = np.take_along_axis(weights[same], o_g, axis=1)
-    wr = np.take_along_axis(ref["weights"][same], o_r, axis=1)
-    err = np.max(np.abs(wg - wr)) if wg.size else 0.0
-    assert err <= tol, f"routing weights differ by {err} > {tol}"
+    if logits is not None:
+        u = 2.0 ** -24
+        l_gpu = logits.astype(np.float64)
+        if bias is not None:
+            l_gpu = (logits + bias[None, :].astype(np.float32)).astype(np.float64)
+        xs = np.abs(wl.to_f32(x).astype(np.float64))
+        gabs = np.abs(wl.to_f32(gate).astype(np.float64))
+        bound = w.hidden_size * u * (xs @ gabs.T) + 2 * u * np.abs(l_gpu) + 1e-30
+        dl = np.abs(l_gpu - ref["logits"].astype(np.float64))
+        worst = float(np.max(dl / bound))
+        assert worst <= 1.0, f"router logits off by {worst:.3g} x the fp32 summation bound"
+        own = oracle.route_from_logits(l_gpu.astype(np.float32), w.top_k, w.renormalize,
+                                       w.use_grouped_topk, w.num_expert_group, w.topk_group,
+                                       w.routed_scaling_factor)
+        near_own = (own["gap"] < TIE_GAP) | (own["ggap"] < TIE_GAP)
+        same_own = np.all(np.sort(own["ids"], 1) == gs, axis=1)
+        assert np.all(same_own | near_own), "ids differ from the oracle's top-k of the GPU logits"
+        sel = same_own
+        o_g = np.argsort(ids[sel], axis=1, kind="stable")
+        o_r = np.argsort(own["ids"][sel], axis=1, kind="stable")
+        wg = np.take_along_axis(weights[sel], o_g, axis=1)
+        wr = np.take_along_axis(own["weights"][sel], o_r, axis=1)
+        err = float(np.max(np.abs(wg - wr))) if wg.size else 0.0
+        tol = TIE_GAP * max(1.0, abs(w.routed_scaling_factor))
+        assert err <= tol, f"routing weights differ by {err} > {tol} on the same logits"
     return np.nonzero(differ)[0], int(near.sum())
 
 

@@ -48,7 +48,7 @@ def _full_check(layer: Layer, rows=None, with_shared=True):
     w = layer.w
     out, ids, tw = layer.forward(with_shared=with_shared)
     ref = layer.oracle_route()
-    mism, near = check_routing(w, ids, tw, ref)
+    mism, near = layer.check_routing(ids, tw, ref)
     if rows is None:
         rows = np.arange(layer.T)
     ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
@@ -76,7 +76,7 @@ def test_forward_full_size(key, T):
     layer = Layer(w, T)
     out, ids, tw = layer.forward()
     ref = layer.oracle_route()
-    mism, near = check_routing(w, ids, tw, ref)
+    mism, near = layer.check_routing(ids, tw, ref)
     rows = np.arange(T) if T <= 256 else sample_rows(ids, layer.emap, T)
     ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows])
@@ -108,7 +108,7 @@ def test_share_sum_equals_all_local(case, ep):
     full = Layer(full_w, T)
     ref = full.oracle_route()
     out_full, ids, tw = full.forward()
-    mism, _ = check_routing(full_w, ids, tw, ref)
+    mism, _ = full.check_routing(ids, tw, ref)
     ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
     want = full.oracle_out(np.arange(T), ids_ref, w_ref)
     assert rel_err(total, want) <= OUT_TOL[w0.dtype]
@@ -174,7 +174,8 @@ def test_split_entry_points(case, block_m):
     torch.cuda.synchronize()
     ids_h, tw_h = ids.cpu().numpy(), tw.cpu().numpy()
     ref = layer.oracle_route()
-    mism, _ = check_routing(w, ids_h, tw_h, ref)
+    logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts).cpu().numpy()
+    mism, _ = check_routing(w, ids_h, tw_h, ref, logits, layer.x, layer.gate, layer.bias)
     ids_ref, w_ref = reference_routing(ids_h, tw_h, ref, mism)
     want = layer.oracle_out(np.arange(T), ids_ref, w_ref)
     assert rel_err(out.float().cpu().numpy(), want) <= OUT_TOL[w.dtype]

@@ -71,17 +71,19 @@ def _load():
     return _lib
 
 
-def normal(stream, count, std=1.0, start=0, dtype="f32"):
-    """``count`` consecutive draws of a stream (a 3-int tuple), from element ``start``."""
+def normal(stream, count, std=1.0, start=0, dtype="f32", out=None):
+    """``count`` consecutive draws of a stream (a 3-int tuple), from element ``start``.
+
+    ``out``: optional C-contiguous array of ``count`` elements (float32 / uint16) to fill.
+    """
     a, b, c = stream
-    if dtype == "f32":
-        out = np.empty(count, np.float32)
-        _load().wl_normal_f32(a, b, c, start, count, float(std), out.ctypes.data)
-    elif dtype == "bf16":
-        out = np.empty(count, np.uint16)
-        _load().wl_normal_bf16(a, b, c, start, count, float(std), out.ctypes.data)
-    else:
-        raise ValueError(dtype)
+    want = {"f32": np.float32, "bf16": np.uint16}[dtype]
+    if out is None:
+        out = np.empty(count, want)
+    if out.dtype != want or out.size != count or not out.flags.c_contiguous:
+        raise ValueError("out must be a C-contiguous array of the requested type and size")
+    fn = _load().wl_normal_f32 if dtype == "f32" else _load().wl_normal_bf16
+    fn(a, b, c, start, count, float(std), out.ctypes.data)
     return out
 
 
@@ -205,28 +207,44 @@ def logit_bias(w: Workload):
     return (-w.zipf_bias * np.log(e + 1.0)).astype(np.float32)
 
 
-def _mlp_weights(w: Workload, role: int, idx: int, I: int):
+def _storage(w: Workload):
+    return np.uint16 if w.dtype == "bf16" else np.float32
+
+
+def _fill_mlp(w: Workload, role: int, idx: int, I: int, w13: np.ndarray, w2: np.ndarray):
+    """Draw one MLP's weights into w13 [2I, H] (gate rows, then up rows) and w2 [H, I]."""
     H = w.hidden_size
     s1 = 1.0 / math.sqrt(H)
-    g = normal((w.cid, role, 3 * idx + 0), I * H, s1, 0, w.dtype).reshape(I, H)
-    u = normal((w.cid, role, 3 * idx + 1), I * H, s1, 0, w.dtype).reshape(I, H)
-    d = normal((w.cid, role, 3 * idx + 2), H * I, 1.0 / math.sqrt(I), 0, w.dtype).reshape(H, I)
-    return np.concatenate([g, u], axis=0), d
+    normal((w.cid, role, 3 * idx + 0), I * H, s1, 0, w.dtype, out=w13[:I].reshape(-1))
+    normal((w.cid, role, 3 * idx + 1), I * H, s1, 0, w.dtype, out=w13[I:].reshape(-1))
+    normal((w.cid, role, 3 * idx + 2), H * I, 1.0 / math.sqrt(I), 0, w.dtype, out=w2.reshape(-1))
 
 
 def expert_weights(w: Workload, e: int):
     """(w13 [2I, H] = [W1 rows; W3 rows], w2 [H, I]) of GLOBAL expert e."""
-    return _mlp_weights(w, 3, e, w.intermediate_size)
+    I, H = w.intermediate_size, w.hidden_size
+    w13 = np.empty((2 * I, H), _storage(w))
+    w2 = np.empty((H, I), _storage(w))
+    _fill_mlp(w, 3, e, I, w13, w2)
+    return w13, w2
 
 
 def local_expert_weights(w: Workload):
     """Packed weights of the share: w13 [E_l, 2I, H], w2 [E_l, H, I]."""
-    pairs = [expert_weights(w, e) for e in w.local_experts]
-    return np.stack([p[0] for p in pairs]), np.stack([p[1] for p in pairs])
+    I, H, n = w.intermediate_size, w.hidden_size, w.num_local_experts
+    w13 = np.empty((n, 2 * I, H), _storage(w))
+    w2 = np.empty((n, H, I), _storage(w))
+    for s, e in enumerate(w.local_experts):
+        _fill_mlp(w, 3, e, I, w13[s], w2[s])
+    return w13, w2
 
 
 def shared_weights(w: Workload):
     """(sw13 [2 I_s, H], sw2 [H, I_s]) or (None, None) when the share has no shared expert."""
     if not w.shared_intermediate_size:
         return None, None
-    return _mlp_weights(w, 4, 0, w.shared_intermediate_size)
+    I, H = w.shared_intermediate_size, w.hidden_size
+    w13 = np.empty((2 * I, H), _storage(w))
+    w2 = np.empty((H, I), _storage(w))
+    _fill_mlp(w, 4, 0, I, w13, w2)
+    return w13, w2
