@@ -44,7 +44,8 @@ def _parse():
     ap.add_argument("--tokens", type=int, default=None, help="token count (default: the largest)")
     ap.add_argument("--decode-tokens", type=int, default=None,
                     help="second, small token count reported as 'decode' (default: the smallest)")
-    ap.add_argument("--cpu-sample", type=int, default=96, help="tokens the oracle is timed on")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens the oracle is timed on")
+    ap.add_argument("--no-decode", action="store_true", help="skip the small-token-count line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -288,7 +289,7 @@ def main():
         "work": alg,
     }
     del b
-    if Td != T:
+    if Td != T and not args.no_decode:
         bd, msd, split_d, stage_d, alg_d = run_point(host, w, Td, max(args.steps, 20), args.warmup)
         bound_d = "mfma" if alg_d["gate_up_flops"] / max(alg_d["gate_up_bytes"], 1) > 312 else "hbm"
         res["decode"] = {"tokens": Td, "value": round(Td / (msd * 1e-3), 1), "unit": "tokens/s",

@@ -43,12 +43,22 @@ int check_params(const moe_params* p) {
 int check_tokens(const moe_params& p, int64_t T) {
   if (T < 0) return MOE_EINVAL;
   // pair ids t*k+j and sorted rows are int32
-  if (T * p.top_k + static_cast<int64_t>(p.num_local_experts) * 128 >= (int64_t{1} << 31))
+  const int64_t rows = T * p.top_k + static_cast<int64_t>(p.num_local_experts) * 256;
+  if (rows >= (int64_t{1} << 31)) return MOE_EUNSUPPORTED;
+  // the GEMM kernels address each operand (activations, one expert's weights, the sorted
+  // intermediate rows) with 32-bit byte offsets
+  int64_t width = p.hidden_size;
+  if (p.intermediate_size > width) width = p.intermediate_size;
+  if (p.shared_intermediate_size > width) width = p.shared_intermediate_size;
+  const int64_t eb = p.dtype == MOE_F32 ? 4 : 2;
+  if (rows * width * eb >= (int64_t{1} << 32)) return MOE_EUNSUPPORTED;
+  if (int64_t{2} * p.intermediate_size * p.hidden_size * eb >= (int64_t{1} << 32)) return MOE_EUNSUPPORTED;
+  if (int64_t{2} * p.shared_intermediate_size * p.hidden_size * eb >= (int64_t{1} << 32))
     return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
-bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 int pick_block_m(const moe_params& p, int64_t T) {
   // Expected rows per local expert under uniform routing: T*k/E.
@@ -56,7 +66,8 @@ int pick_block_m(const moe_params& p, int64_t T) {
   if (p.dtype == MOE_F32) return 16;
   if (rows <= 12.0) return 16;
   if (rows <= 48.0) return 64;
-  return 128;
+  if (rows < 768.0) return 128;
+  return 256;
 }
 
 int64_t capacity(const moe_params& p, int64_t T, int bm) {

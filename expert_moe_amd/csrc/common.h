@@ -37,6 +37,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
+// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes at `src`
+// land at LDS address lds_base + 16 l; lds_base must be the same for the whole wave. The
+// builtin only exists in the device compilation pass; the host pass (which only needs the
+// kernel's launch stub) sees an empty body.
+__device__ __forceinline__ void lds_load16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#endif
+}
+
 // Plain 16-byte global load.
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 

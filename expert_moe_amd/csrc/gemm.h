@@ -34,8 +34,43 @@ struct GemmArgs {
   int32_t N_valid;             // kStoreF32: valid output columns (B rows past it are clamped)
   void* C;                     // output, row stride ldc elements
   int64_t ldc;
-  int32_t m_blocks;            // grid extent along rows
+  int32_t m_blocks;            // grid extent along rows (the largest possible row-block count)
+  int32_t n_tiles;             // output tiles along the B rows
 };
+
+// s_waitcnt immediate that waits for every outstanding vector memory load (vmcnt = 0) and
+// nothing else (expcnt and lgkmcnt left at their maxima).
+constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
+
+// MI355X dispatches workgroup i to XCD i % 8; each XCD has its own L2.
+constexpr int kXcds = 8;
+// N tiles that run side by side on one XCD and share their A row-block through its L2.
+constexpr int kGroupN = 4;
+
+// XCD-aware tile order. The active tiles (row blocks below the device row count) are cut
+// into kXcds contiguous runs, one per XCD, so that workgroups on one XCD share operands in
+// its L2. Inside a run, tiles go row-block-major within groups of kGroupN N tiles: the row
+// blocks of one expert that read the same weight tile are consecutive and run together.
+// Returns false for workgroups that have no tile (the grid is sized for the worst case).
+__device__ __forceinline__ bool tile_of_block(int bid, int active_m, int n_tiles, int& mb, int& nt) {
+  const int total = active_m * n_tiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int slot = bid / kXcds;
+  if (slot >= per_xcd) return false;
+  const int L = (bid % kXcds) * per_xcd + slot;
+  if (L >= total) return false;
+  const int ng = L / (active_m * kGroupN);
+  const int rem = L - ng * active_m * kGroupN;
+  const int width = min(kGroupN, n_tiles - ng * kGroupN);
+  mb = rem / width;
+  nt = ng * kGroupN + rem % width;
+  return true;
+}
+
+// Grid size for the tile order above.
+inline int tile_grid(int m_blocks, int n_tiles) {
+  return (m_blocks * n_tiles + kXcds - 1) / kXcds * kXcds;
+}
 
 __device__ __forceinline__ int gemm_src_row(const GemmArgs& a, int r) {
   if (a.row_map) {
@@ -53,8 +88,10 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
 // Large-M tile: BM x BNR (B rows) per workgroup of 4 waves (WM x WN), K step 64, two LDS
 // stages, v_mfma_f32_32x32x16_bf16. In kSiluMul the BNR rows are BNR/2 gate rows followed
 // by the BNR/2 matching up rows, so each lane holds gate and up of the same output.
+// RS register stages of global prefetch: 1 = the next K step is in flight while the current
+// one computes; 2 = the step after that too (for small tiles, whose K steps are short).
 // ----------------------------------------------------------------------------------------
-template <int BM, int BNR, int WM, int WN, int MODE>
+template <int BM, int BNR, int WM, int WN, int MODE, int RS = 2>
 __global__ void __launch_bounds__(256) gemm_bf16_tile(GemmArgs a) {
   constexpr int BK = 64;
   constexpr int LDK = BK + 8;  // +16 bytes per LDS row: conflict-free 16-byte fragment reads
@@ -72,10 +109,9 @@ __global__ void __launch_bounds__(256) gemm_bf16_tile(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int mb = blockIdx.x % a.m_blocks;
-  const int nt = blockIdx.x / a.m_blocks;
+  int mb, nt;
+  if (!tile_of_block(blockIdx.x, (gemm_rows_active(a) + BM - 1) / BM, a.n_tiles, mb, nt)) return;
   const int m0 = mb * BM;
-  if (m0 >= gemm_rows_active(a)) return;
   const int slot = a.block_expert ? a.block_expert[m0 / a.block_m] : 0;
   const uint16_t* __restrict__ A = static_cast<const uint16_t*>(a.A);
   const uint16_t* __restrict__ B = static_cast<const uint16_t*>(a.B) + slot * a.b_stride;
@@ -102,14 +138,17 @@ __global__ void __launch_bounds__(256) gemm_bf16_tile(GemmArgs a) {
     pb[i] = B + static_cast<int64_t>(brow) * K + lc * 8;
   }
 
-  uint4 ra[BM / 32], rb[BNR / 32];
-  auto gload = [&](int kt) {
+  // Two register stages: the tile two steps ahead is in flight while one LDS stage is
+  // read by the MFMAs and the other is being filled.
+  uint4 r0a[BM / 32], r0b[BNR / 32];
+  uint4 r1a[RS == 2 ? BM / 32 : 1], r1b[RS == 2 ? BNR / 32 : 1];
+  auto gload = [&](int kt, uint4* ra, uint4* rb) {
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) ra[i] = load16(pa[i] + kt * BK);
 #pragma unroll
     for (int i = 0; i < BNR / 32; ++i) rb[i] = load16(pb[i] + kt * BK);
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const uint4* ra, const uint4* rb) {
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) *reinterpret_cast<uint4*>(&sA[buf][lr + 32 * i][lc * 8]) = ra[i];
 #pragma unroll
@@ -137,30 +176,65 @@ __global__ void __launch_bounds__(256) gemm_bf16_tile(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[TMB], fb[TNB];
+  // One BK step from LDS stage `cur`: the fragments of K slice kk+1 are read while the MFMAs
+  // of slice kk issue (two fragment register sets), so LDS latency hides behind the MFMAs.
+  auto compute = [&](int cur) {
+    bf16x8 fa[2][TMB], fb[2][TNB];
+    auto frags = [&](int kk, int set) {
 #pragma unroll
       for (int i = 0; i < TMB; ++i)
-        fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[cur][wm * TM + i * 32 + fr][kk + fk]));
+        fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[cur][wm * TM + i * 32 + fr][kk + fk]));
 #pragma unroll
       for (int j = 0; j < TNB; ++j)
-        fb[j] = as_bf16x8(*reinterpret_cast<const uint4*>(&sB[cur][brow0[j] + fr][kk + fk]));
+        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(&sB[cur][brow0[j] + fr][kk + fk]));
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) frags((ks + 1) * 16, (ks + 1) & 1);
+      // keep the next slice's LDS reads ahead of this slice's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TMB; ++i)
 #pragma unroll
         for (int j = 0; j < TNB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
+                                                              0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+  };
+
+  const int nk = K / BK;
+  if constexpr (RS == 1) {
+    gload(0, r0a, r0b);
+    sstore(0, r0a, r0b);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) gload(kt + 1, r0a, r0b);
+      compute(kt & 1);
+      if (kt + 1 < nk) sstore((kt + 1) & 1, r0a, r0b);
+      __syncthreads();
+    }
+  } else {
+    // Tile t is loaded into register stage t % 2 two steps before it is computed, written to
+    // LDS stage t % 2 one step before, and read from there. The loop is unrolled by two so
+    // that every register stage index is a compile-time constant.
+    gload(0, r0a, r0b);
+    if (nk > 1) gload(1, r1a, r1b);
+    sstore(0, r0a, r0b);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      if (kt + 2 < nk) gload(kt + 2, r0a, r0b);
+      compute(0);
+      sstore(1, r1a, r1b);
+      __syncthreads();
+      if (kt + 3 < nk) gload(kt + 3, r1a, r1b);
+      compute(1);
+      if (kt + 2 < nk) sstore(0, r0a, r0b);
+      __syncthreads();
+    }
+    if (kt < nk) compute(0);
   }
 
   // Epilogue. acc[i][j][r] sits at tile row wm*TM + i*32 + 8*(r/4) + 4*(lane/32) + r%4 and
@@ -187,6 +261,189 @@ __global__ void __launch_bounds__(256) gemm_bf16_tile(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TNB; ++j) {
           const int col = nt * BNR + brow0[j] + fr;
+          if (col < a.N_valid) C[col] = acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Large-M tile fed by global->LDS loads (gfx950 global_load_lds_dwordx4): each lane's 16 bytes
+// go straight from memory into LDS without passing through registers, so the waves issue
+// only the loads, the LDS fragment reads and the MFMAs. Two LDS stages (separate arrays, the
+// loop unrolled by two so each is addressed statically): the loads of K step t+1 fly while
+// step t computes.
+// LDS rows are the 64 bf16 (128 bytes) of one tile row; the eight 16-byte chunks of row r are
+// stored at chunk ^ sw(r), sw(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of
+// 16 consecutive rows hit distinct banks. One load instruction fills 8 rows (1 KiB, lane l at
+// byte 16 l): lane l loads row 8 j + l / 8, logical chunk (l % 8) ^ sw(row).
+// ----------------------------------------------------------------------------------------
+template <int BM, int BNR, int WM, int WN, int MODE>
+__global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
+  constexpr int BK = 64;
+  constexpr int ROWB = 128;                // bytes of one LDS row
+  constexpr int TM = BM / WM;
+  constexpr int TMB = TM / 32;
+  constexpr int TNR = BNR / WN;
+  constexpr int TNB = TNR / 32;
+  constexpr int NA = BM / 32;              // A load instructions per wave per K step
+  constexpr int NB = BNR / 32;             // B load instructions per wave per K step
+  static_assert(WM * WN == 4, "4 waves");
+  static_assert(TMB >= 1 && TNB >= 1 && NA >= 1 && NB >= 1, "tile too small");
+  static_assert(MODE != kSiluMul || (TNB % 2 == 0), "gate/up pairs");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BNR * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BNR * ROWB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int mb, nt;
+  if (!tile_of_block(blockIdx.x, (gemm_rows_active(a) + BM - 1) / BM, a.n_tiles, mb, nt)) return;
+  const int m0 = mb * BM;
+  const int slot = a.block_expert ? a.block_expert[m0 / a.block_m] : 0;
+  const uint16_t* __restrict__ A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* __restrict__ B = static_cast<const uint16_t*>(a.B) + slot * a.b_stride;
+  const int K = a.K;
+
+  // Load sources: instruction j of this wave fills rows 8 (wave + 4 j) .. +7 of its region.
+  // Kept as 32-bit byte offsets from the (wave-uniform) operand bases: an expert's weights
+  // and the activations are each far below 4 GiB.
+  const int lrow = lane >> 3;
+  const char* const Abase = reinterpret_cast<const char*>(A);
+  const char* const Bbase = reinterpret_cast<const char*>(B);
+  uint32_t oa[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int blk = wave + 4 * j;
+    const int r = 8 * blk + lrow;
+    const int c = (lane & 7) ^ lrow ^ (blk & 1);
+    oa[j] = static_cast<uint32_t>(gemm_src_row(a, m0 + r)) * static_cast<uint32_t>(K * 2) + c * 16;
+  }
+  uint32_t ob[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int blk = wave + 4 * j;
+    const int r = 8 * blk + lrow;
+    const int c = (lane & 7) ^ lrow ^ (blk & 1);
+    int brow;
+    if (MODE == kSiluMul)
+      brow = r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2);
+    else {
+      brow = nt * BNR + r;
+      if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
+    }
+    ob[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16;
+  }
+  auto issue = [&](int kt, uint8_t* dA, uint8_t* dB) {
+    const uint32_t ko = static_cast<uint32_t>(kt) * (BK * 2);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) lds_load16(Abase + (oa[j] + ko), dA + (wave + 4 * j) * 1024);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) lds_load16(Bbase + (ob[j] + ko), dB + (wave + 4 * j) * 1024);
+  };
+
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int fr = lane & 31;
+  // swizzle of the fragment rows (their tile row is a multiple of 32 plus fr)
+  const int sw = (fr & 7) ^ ((fr >> 3) & 1);
+  int coff[BK / 16];  // byte offset of this lane's 16-byte chunk in K slice ks
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) coff[ks] = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+  int arow[TMB], brow0[TNB];
+#pragma unroll
+  for (int i = 0; i < TMB; ++i) arow[i] = (wm * TM + i * 32 + fr) * ROWB;
+#pragma unroll
+  for (int j = 0; j < TNB; ++j) {
+    const int r0 = MODE == kSiluMul
+                       ? (j < TNB / 2 ? wn * (TNR / 2) + j * 32 : BNR / 2 + wn * (TNR / 2) + (j - TNB / 2) * 32)
+                       : wn * TNR + j * 32;
+    brow0[j] = (r0 + fr) * ROWB;
+  }
+
+  f32x16 acc[TMB][TNB];
+#pragma unroll
+  for (int i = 0; i < TMB; ++i)
+#pragma unroll
+    for (int j = 0; j < TNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const uint8_t* sA, const uint8_t* sB) {
+    bf16x8 fa[2][TMB], fb[2][TNB];
+    auto frags = [&](int ks, int set) {
+#pragma unroll
+      for (int i = 0; i < TMB; ++i)
+        fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sA + arow[i] + coff[ks]));
+#pragma unroll
+      for (int j = 0; j < TNB; ++j)
+        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sB + brow0[j] + coff[ks]));
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) frags(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TMB; ++i)
+#pragma unroll
+        for (int j = 0; j < TNB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
+                                                              0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // K step t lives in LDS stage t % 2: wait for this wave's loads of step t, barrier (every
+  // wave's loads landed and every wave is done reading the other stage), issue step t + 1
+  // into the other stage, compute step t.
+  const int nk = K / BK;
+  issue(0, sA0, sB0);
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    issue(kt + 1, sA1, sB1);
+    compute(sA0, sB0);
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    if (kt + 2 < nk) issue(kt + 2, sA0, sB0);
+    compute(sA1, sB1);
+  }
+  if (kt < nk) {
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    compute(sA0, sB0);
+  }
+
+  // Epilogue. acc[i][j][r] sits at tile row wm*TM + i*32 + 8*(r/4) + 4*(lane/32) + r%4 and
+  // tile B row (brow0[j] / ROWB - fr) + lane%32.
+#pragma unroll
+  for (int i = 0; i < TMB; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= a.M_rows) continue;
+      if (MODE == kSiluMul) {
+        uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+#pragma unroll
+        for (int j = 0; j < TNB / 2; ++j) {
+          const int col = nt * (BNR / 2) + wn * (TNR / 2) + j * 32 + fr;
+          C[col] = f32_to_bf16(silu_mul(acc[i][j][r], acc[i][j + TNB / 2][r]));
+        }
+      } else if (MODE == kStore) {
+        uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+#pragma unroll
+        for (int j = 0; j < TNB; ++j) C[nt * BNR + wn * TNR + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
+      } else {
+        float* C = static_cast<float*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+#pragma unroll
+        for (int j = 0; j < TNB; ++j) {
+          const int col = nt * BNR + wn * TNR + j * 32 + fr;
           if (col < a.N_valid) C[col] = acc[i][j][r];
         }
       }

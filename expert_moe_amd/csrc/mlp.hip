@@ -12,25 +12,41 @@ namespace moe {
 
 namespace {
 
+template <int BM, int BNR, int WM, int WN, int MODE>
+void launch_tile(GemmArgs a, int n_rows_b, hipStream_t s) {
+  a.n_tiles = n_rows_b / BNR;
+  gemm_bf16_dma<BM, BNR, WM, WN, MODE><<<tile_grid(a.m_blocks, a.n_tiles), 256, 0, s>>>(a);
+}
+
+template <int MODE>
+void launch_tile256(const GemmArgs& a, int n_rows_b, hipStream_t s) {
+  if (n_rows_b % 256 == 0)
+    launch_tile<256, 256, 2, 2, MODE>(a, n_rows_b, s);
+  else if (n_rows_b % 128 == 0)
+    launch_tile<256, 128, 2, 2, MODE>(a, n_rows_b, s);
+  else
+    launch_tile<256, 64, 4, 1, MODE>(a, n_rows_b, s);
+}
+
 template <int MODE>
 void launch_tile128(const GemmArgs& a, int n_rows_b, hipStream_t s) {
   // n_rows_b: B rows spanned by the whole output (2I for the silu GEMM, H for the store)
   if (n_rows_b % 256 == 0)
-    gemm_bf16_tile<128, 256, 2, 2, MODE><<<a.m_blocks * (n_rows_b / 256), 256, 0, s>>>(a);
+    launch_tile<128, 256, 2, 2, MODE>(a, n_rows_b, s);
   else if (n_rows_b % 128 == 0)
-    gemm_bf16_tile<128, 128, 2, 2, MODE><<<a.m_blocks * (n_rows_b / 128), 256, 0, s>>>(a);
+    launch_tile<128, 128, 2, 2, MODE>(a, n_rows_b, s);
   else
-    gemm_bf16_tile<128, 64, 4, 1, MODE><<<a.m_blocks * (n_rows_b / 64), 256, 0, s>>>(a);
+    launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, s);
 }
 
 template <int MODE>
 void launch_tile64(const GemmArgs& a, int n_rows_b, hipStream_t s) {
   if (n_rows_b % 256 == 0)
-    gemm_bf16_tile<64, 256, 1, 4, MODE><<<a.m_blocks * (n_rows_b / 256), 256, 0, s>>>(a);
+    launch_tile<64, 256, 1, 4, MODE>(a, n_rows_b, s);
   else if (n_rows_b % 128 == 0)
-    gemm_bf16_tile<64, 128, 2, 2, MODE><<<a.m_blocks * (n_rows_b / 128), 256, 0, s>>>(a);
+    launch_tile<64, 128, 2, 2, MODE>(a, n_rows_b, s);
   else if constexpr (MODE != kSiluMul)  // 2I is always a multiple of 128
-    gemm_bf16_tile<64, 64, 2, 2, MODE><<<a.m_blocks * (n_rows_b / 64), 256, 0, s>>>(a);
+    launch_tile<64, 64, 2, 2, MODE>(a, n_rows_b, s);
 }
 
 }  // namespace
@@ -82,8 +98,10 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
     gemm_bf16_stream<4, kSiluMul><<<g.m_blocks * (I / 32), 256, 0, s>>>(g);
   else if (tr == 64)
     launch_tile64<kSiluMul>(g, 2 * I, s);
-  else
+  else if (tr == 128)
     launch_tile128<kSiluMul>(g, 2 * I, s);
+  else
+    launch_tile256<kSiluMul>(g, 2 * I, s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -112,8 +130,10 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
     gemm_bf16_stream<4, kStore><<<g.m_blocks * (H / 64), 256, 0, s>>>(g);
   else if (tr == 64)
     launch_tile64<kStore>(g, H, s);
-  else
+  else if (tr == 128)
     launch_tile128<kStore>(g, H, s);
+  else
+    launch_tile256<kStore>(g, H, s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -172,7 +172,8 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
     gemm_bf16_stream<4, kStoreF32><<<a.m_blocks * n_tiles, 256, 0, s>>>(a);
   } else {
     a.m_blocks = ceil_div(T, 128);
-    gemm_bf16_tile<128, 64, 4, 1, kStoreF32><<<a.m_blocks * n_tiles, 256, 0, s>>>(a);
+    a.n_tiles = n_tiles;
+    gemm_bf16_dma<128, 64, 4, 1, kStoreF32><<<tile_grid(a.m_blocks, n_tiles), 256, 0, s>>>(a);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;

@@ -103,7 +103,7 @@ int moe_check_params(const moe_params* p);
 
 /*
  * The per-expert padding granule moe_forward uses for T tokens: the M-tile of the grouped
- * GEMM that fits the expected rows per local expert. Writes *block_m (16, 32, 64 or 128).
+ * GEMM that fits the expected rows per local expert. Writes *block_m (16, 32, 64, 128 or 256).
  */
 int moe_pick_block_m(const moe_params* p, int64_t num_tokens, int32_t* block_m);
 
@@ -160,7 +160,7 @@ int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void
  * expert loop in MixtralMoE.forward / the sort before fused_experts in _ep_forward).
  *  topk_local [T, k]: slot of each pair or -1 (may come from the caller's own routing;
  *    the slots of one token must be distinct, as top-k gives them).
- *  block_m: 16, 32, 64 or 128.
+ *  block_m: 16, 32, 64, 128 or 256.
  *  Outputs: sorted_pairs [moe_sorted_capacity] (pair ids; -1 in padding; entries past
  *  *num_padded are left untouched), block_expert [capacity / block_m] (slot owning each
  *  block_m rows), pair_row [T*k] (row of each pair in sorted order, -1 if not local),

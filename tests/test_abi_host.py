@@ -61,7 +61,7 @@ def test_workload_params_valid(key):
     assert moe.moe_check_params(p) == moe.MOE_OK
     for T in w.tokens:
         bm = moe.moe_pick_block_m(p, T)
-        assert bm in (16, 32, 64, 128)
+        assert bm in (16, 32, 64, 128, 256)
         assert moe.moe_sorted_capacity(p, T, bm) == T * w.top_k + w.num_local_experts * (bm - 1)
         assert moe.moe_workspace_size(p, T) > 0
 

@@ -134,7 +134,7 @@ def test_share_without_local_pairs():
     assert rel_err(out2, want) <= OUT_TOL["bf16"]
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("case", ["ds_s", "tiny_ragged"])
 def test_split_entry_points(case, block_m):
     """route -> align_permute -> grouped_mlp (-> shared_mlp) -> combine, any granule."""
@@ -149,6 +149,8 @@ def test_split_entry_points(case, block_m):
     tw = torch.empty(T, k, dtype=torch.float32, device=dev)
     local = torch.empty(T, k, dtype=torch.int32, device=dev)
     moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws)
+    # the logits sit at the start of the workspace until the next call reuses it
+    logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts).clone()
     cap = moe.moe_sorted_capacity(p, T, block_m)
     sp = torch.full((cap,), 7, dtype=torch.int32, device=dev)
     be = torch.full((cap // block_m + 1,), -5, dtype=torch.int32, device=dev)
@@ -174,8 +176,8 @@ def test_split_entry_points(case, block_m):
     torch.cuda.synchronize()
     ids_h, tw_h = ids.cpu().numpy(), tw.cpu().numpy()
     ref = layer.oracle_route()
-    logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts).cpu().numpy()
-    mism, _ = check_routing(w, ids_h, tw_h, ref, logits, layer.x, layer.gate, layer.bias)
+    mism, _ = check_routing(w, ids_h, tw_h, ref, logits.cpu().numpy(), layer.x, layer.gate,
+                            layer.bias)
     ids_ref, w_ref = reference_routing(ids_h, tw_h, ref, mism)
     want = layer.oracle_out(np.arange(T), ids_ref, w_ref)
     assert rel_err(out.float().cpu().numpy(), want) <= OUT_TOL[w.dtype]
