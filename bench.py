@@ -33,6 +33,39 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+# Sources that define the dominant (gate/up) kernel; a traffic figure measured with
+# rocprofv3 counters is only reported while these hash to the value recorded with it.
+KERNEL_SOURCES = ("expert_moe_amd/csrc/gemm.h", "expert_moe_amd/csrc/mlp.hip",
+                  "expert_moe_amd/csrc/common.h")
+TRAFFIC_PROFILE = "profiles/mixtral_T4096_hbm_traffic.md"
+
+
+def kernel_fingerprint() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, T: int):
+    """Counter-measured bytes per gate/up launch for the default workload, or None."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if workload != "mixtral" or T != 4096 or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("|", "#", " ")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_fingerprint():
+        return None
+    try:
+        return int(vals["gate_up_traffic_bytes"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _parse():
@@ -44,7 +77,8 @@ def _parse():
     ap.add_argument("--tokens", type=int, default=None, help="token count (default: the largest)")
     ap.add_argument("--decode-tokens", type=int, default=None,
                     help="second, small token count reported as 'decode' (default: the smallest)")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens the oracle is timed on")
+    ap.add_argument("--cpu-sample", type=int, default=4096,
+                    help="tokens the oracle is timed on (capped at the workload's token count)")
     ap.add_argument("--no-decode", action="store_true", help="skip the small-token-count line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -283,7 +317,7 @@ def main():
                    "shared_intermediate": w.shared_intermediate_size, "block_m": b.bm},
         "achieved_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
         "achieved_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
-        "roofline": roofline(alg, stage, bound),
+        "roofline": dict(roofline(alg, stage, bound), traffic=measured_traffic(w.key, T)),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "split_path_ms_per_step": round(split_ms, 4),
         "work": alg,

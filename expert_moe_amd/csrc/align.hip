@@ -7,9 +7,10 @@
 // padded to a multiple of block_m rows so that a GEMM tile never straddles two experts.
 //
 // Three passes, no host synchronisation:
-//   count   : one workgroup per chunk of 256 tokens, LDS histogram of its pairs per slot
+//   count   : one workgroup per chunk of 256 tokens, LDS histogram of its pairs per slot; the
+//             workgroups also fill the whole sorted list with -1 (padding)
 //   scan    : one workgroup; per-slot exclusive scan over chunks (chunk bases), padded
-//             segment sizes, exclusive scan over slots (offsets), block -> slot table, -1 fill
+//             segment sizes, exclusive scan over slots (offsets), block -> slot table
 //   scatter : one workgroup per chunk; each wave marks its 64 tokens per slot in an LDS
 //             64-bit mask; a pair's rank inside its slot is the chunk base plus the number of
 //             marked tokens before it (earlier waves, then earlier lanes), which keeps the
@@ -27,8 +28,11 @@ __device__ __forceinline__ int local_slot(const int32_t* tl, int64_t i, int E_l)
 }
 
 __global__ void __launch_bounds__(256) align_count(const int32_t* __restrict__ tl, int T, int k,
-                                                   int E_l, int32_t* __restrict__ chunk) {
+                                                   int E_l, int32_t* __restrict__ chunk,
+                                                   int32_t* __restrict__ sorted_pairs, int cap) {
   __shared__ int hist[256];
+  // every sorted slot starts as padding (-1); the scatter pass overwrites the real ones
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < cap; i += gridDim.x * 256) sorted_pairs[i] = -1;
   for (int e = threadIdx.x; e < E_l; e += 256) hist[e] = 0;
   __syncthreads();
   const int t = blockIdx.x * kAlignChunk + threadIdx.x;
@@ -44,8 +48,7 @@ __global__ void __launch_bounds__(256) align_count(const int32_t* __restrict__ t
 __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, int nchunks, int E_l,
                                                   int bm, int32_t* __restrict__ meta,
                                                   int32_t* __restrict__ num_padded,
-                                                  int32_t* __restrict__ block_expert,
-                                                  int32_t* __restrict__ sorted_pairs) {
+                                                  int32_t* __restrict__ block_expert) {
   __shared__ int seg[257];
   int32_t* offsets = meta + 1;
   int32_t* counts = meta + 1 + (E_l + 1);
@@ -80,7 +83,6 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
     const int end = seg[e + 1];
     offsets[e] = off;
     for (int b = off / bm; b < end / bm; ++b) block_expert[b] = e;
-    for (int i = off; i < end; ++i) sorted_pairs[i] = -1;
   }
 }
 
@@ -133,10 +135,10 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
   const int E_l = p.num_local_experts;
   const int k = p.top_k;
   const int nchunks = align_chunks(T);
-  align_count<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk);
+  const int cap = T * k + E_l * (block_m - 1);
+  align_count<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, sorted_pairs, cap);
   MOE_LAUNCH_CHECK();
-  align_scan<<<1, 256, 0, s>>>(chunk, nchunks, E_l, block_m, meta, num_padded, block_expert,
-                               sorted_pairs);
+  align_scan<<<1, 256, 0, s>>>(chunk, nchunks, E_l, block_m, meta, num_padded, block_expert);
   MOE_LAUNCH_CHECK();
   align_scatter<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, meta, sorted_pairs, pair_row);
   MOE_LAUNCH_CHECK();

@@ -161,8 +161,8 @@ int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void
  *  topk_local [T, k]: slot of each pair or -1 (may come from the caller's own routing;
  *    the slots of one token must be distinct, as top-k gives them).
  *  block_m: 16, 32, 64, 128 or 256.
- *  Outputs: sorted_pairs [moe_sorted_capacity] (pair ids; -1 in padding; entries past
- *  *num_padded are left untouched), block_expert [capacity / block_m] (slot owning each
+ *  Outputs: sorted_pairs [moe_sorted_capacity] (pair ids; -1 in padding and in every
+ *  entry past *num_padded), block_expert [capacity / block_m] (slot owning each
  *  block_m rows), pair_row [T*k] (row of each pair in sorted order, -1 if not local),
  *  num_padded [1] (device int32: total padded rows).
  *  ws: device scratch, at least moe_workspace_size(p, T, block_m) bytes.
