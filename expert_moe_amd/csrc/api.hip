@@ -64,8 +64,9 @@ int pick_block_m(const moe_params& p, int64_t T) {
   // Expected rows per local expert under uniform routing: T*k/E.
   const double rows = static_cast<double>(T) * p.top_k / p.num_experts;
   if (p.dtype == MOE_F32) return 16;
+  // measured on MI355X: the 128/256-row LDS tiles beat smaller granules as soon as an expert
+  // gets more than a handful of rows (each expert's weights are then streamed once per block)
   if (rows <= 12.0) return 16;
-  if (rows <= 48.0) return 64;
   if (rows < 768.0) return 128;
   return 256;
 }
@@ -107,7 +108,8 @@ Layout layout(const moe_params& p, int64_t T, int bm) {
   L.chunk = take(nch * E_l * 4);
   L.y = take(cap * p.hidden_size * eb);
   L.shared_y = take(p.shared_intermediate_size ? static_cast<size_t>(T) * p.hidden_size * eb : 0);
-  L.route_need = round_up(static_cast<size_t>(T) * p.num_experts * 4);
+  L.route_need = round_up(static_cast<size_t>(moe::router_splits(p, static_cast<int>(T))) * T *
+                          p.num_experts * 4);
   L.align_need = round_up((2 * E_l + 2) * 4) + round_up(nch * E_l * 4);
   L.mlp_need = round_up(cap * p.intermediate_size * eb);
   L.shared_need = round_up(static_cast<size_t>(T) * p.shared_intermediate_size * eb);

@@ -36,7 +36,17 @@ struct GemmArgs {
   int64_t ldc;
   int32_t m_blocks;            // grid extent along rows (the largest possible row-block count)
   int32_t n_tiles;             // output tiles along the B rows
+  int32_t k_splits;            // kStoreF32 only: blockIdx.y takes K range y*K/k_splits.. and
+                               // writes its partial sums to C + y * c_split_stride (0 or 1 = no split)
+  int64_t c_split_stride;
 };
+
+// K range [k0, k0 + klen) of this workgroup (blockIdx.y selects the split).
+__device__ __forceinline__ void k_range(const GemmArgs& a, int& k0, int& klen) {
+  const int s = a.k_splits > 1 ? a.k_splits : 1;
+  klen = a.K / s;
+  k0 = static_cast<int>(blockIdx.y) * klen;
+}
 
 // s_waitcnt immediate that waits for every outstanding vector memory load (vmcnt = 0) and
 // nothing else (expcnt and lgkmcnt left at their maxima).
@@ -85,190 +95,6 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Large-M tile: BM x BNR (B rows) per workgroup of 4 waves (WM x WN), K step 64, two LDS
-// stages, v_mfma_f32_32x32x16_bf16. In kSiluMul the BNR rows are BNR/2 gate rows followed
-// by the BNR/2 matching up rows, so each lane holds gate and up of the same output.
-// RS register stages of global prefetch: 1 = the next K step is in flight while the current
-// one computes; 2 = the step after that too (for small tiles, whose K steps are short).
-// ----------------------------------------------------------------------------------------
-template <int BM, int BNR, int WM, int WN, int MODE, int RS = 2>
-__global__ void __launch_bounds__(256) gemm_bf16_tile(GemmArgs a) {
-  constexpr int BK = 64;
-  constexpr int LDK = BK + 8;  // +16 bytes per LDS row: conflict-free 16-byte fragment reads
-  constexpr int TM = BM / WM;
-  constexpr int TMB = TM / 32;
-  constexpr int TNR = BNR / WN;
-  constexpr int TNB = TNR / 32;
-  static_assert(WM * WN == 4, "4 waves");
-  static_assert(TMB >= 1 && TNB >= 1, "wave tile at least 32x32");
-  static_assert(MODE != kSiluMul || (TNB % 2 == 0), "gate/up pairs");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNR][LDK];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  int mb, nt;
-  if (!tile_of_block(blockIdx.x, (gemm_rows_active(a) + BM - 1) / BM, a.n_tiles, mb, nt)) return;
-  const int m0 = mb * BM;
-  const int slot = a.block_expert ? a.block_expert[m0 / a.block_m] : 0;
-  const uint16_t* __restrict__ A = static_cast<const uint16_t*>(a.A);
-  const uint16_t* __restrict__ B = static_cast<const uint16_t*>(a.B) + slot * a.b_stride;
-  const int K = a.K;
-
-  // Global -> register assignment: 8 threads per 64-element row slice, 32 rows per pass.
-  const int lc = tid & 7;
-  const int lr = tid >> 3;
-  const uint16_t* pa[BM / 32];
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i)
-    pa[i] = A + static_cast<int64_t>(gemm_src_row(a, m0 + lr + 32 * i)) * K + lc * 8;
-  const uint16_t* pb[BNR / 32];
-#pragma unroll
-  for (int i = 0; i < BNR / 32; ++i) {
-    const int r = lr + 32 * i;
-    int brow;
-    if (MODE == kSiluMul)
-      brow = r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2);
-    else {
-      brow = nt * BNR + r;
-      if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
-    }
-    pb[i] = B + static_cast<int64_t>(brow) * K + lc * 8;
-  }
-
-  // Two register stages: the tile two steps ahead is in flight while one LDS stage is
-  // read by the MFMAs and the other is being filled.
-  uint4 r0a[BM / 32], r0b[BNR / 32];
-  uint4 r1a[RS == 2 ? BM / 32 : 1], r1b[RS == 2 ? BNR / 32 : 1];
-  auto gload = [&](int kt, uint4* ra, uint4* rb) {
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) ra[i] = load16(pa[i] + kt * BK);
-#pragma unroll
-    for (int i = 0; i < BNR / 32; ++i) rb[i] = load16(pb[i] + kt * BK);
-  };
-  auto sstore = [&](int buf, const uint4* ra, const uint4* rb) {
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) *reinterpret_cast<uint4*>(&sA[buf][lr + 32 * i][lc * 8]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BNR / 32; ++i) *reinterpret_cast<uint4*>(&sB[buf][lr + 32 * i][lc * 8]) = rb[i];
-  };
-
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-  const int fr = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  int brow0[TNB];
-#pragma unroll
-  for (int j = 0; j < TNB; ++j) {
-    if (MODE == kSiluMul)
-      brow0[j] = j < TNB / 2 ? wn * (TNR / 2) + j * 32 : BNR / 2 + wn * (TNR / 2) + (j - TNB / 2) * 32;
-    else
-      brow0[j] = wn * TNR + j * 32;
-  }
-
-  f32x16 acc[TMB][TNB];
-#pragma unroll
-  for (int i = 0; i < TMB; ++i)
-#pragma unroll
-    for (int j = 0; j < TNB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // One BK step from LDS stage `cur`: the fragments of K slice kk+1 are read while the MFMAs
-  // of slice kk issue (two fragment register sets), so LDS latency hides behind the MFMAs.
-  auto compute = [&](int cur) {
-    bf16x8 fa[2][TMB], fb[2][TNB];
-    auto frags = [&](int kk, int set) {
-#pragma unroll
-      for (int i = 0; i < TMB; ++i)
-        fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[cur][wm * TM + i * 32 + fr][kk + fk]));
-#pragma unroll
-      for (int j = 0; j < TNB; ++j)
-        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(&sB[cur][brow0[j] + fr][kk + fk]));
-    };
-    frags(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) frags((ks + 1) * 16, (ks + 1) & 1);
-      // keep the next slice's LDS reads ahead of this slice's MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < TMB; ++i)
-#pragma unroll
-        for (int j = 0; j < TNB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
-                                                              0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  const int nk = K / BK;
-  if constexpr (RS == 1) {
-    gload(0, r0a, r0b);
-    sstore(0, r0a, r0b);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) gload(kt + 1, r0a, r0b);
-      compute(kt & 1);
-      if (kt + 1 < nk) sstore((kt + 1) & 1, r0a, r0b);
-      __syncthreads();
-    }
-  } else {
-    // Tile t is loaded into register stage t % 2 two steps before it is computed, written to
-    // LDS stage t % 2 one step before, and read from there. The loop is unrolled by two so
-    // that every register stage index is a compile-time constant.
-    gload(0, r0a, r0b);
-    if (nk > 1) gload(1, r1a, r1b);
-    sstore(0, r0a, r0b);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-      if (kt + 2 < nk) gload(kt + 2, r0a, r0b);
-      compute(0);
-      sstore(1, r1a, r1b);
-      __syncthreads();
-      if (kt + 3 < nk) gload(kt + 3, r1a, r1b);
-      compute(1);
-      if (kt + 2 < nk) sstore(0, r0a, r0b);
-      __syncthreads();
-    }
-    if (kt < nk) compute(0);
-  }
-
-  // Epilogue. acc[i][j][r] sits at tile row wm*TM + i*32 + 8*(r/4) + 4*(lane/32) + r%4 and
-  // tile B row brow0[j] + lane%32.
-#pragma unroll
-  for (int i = 0; i < TMB; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= a.M_rows) continue;
-      if (MODE == kSiluMul) {
-        uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
-#pragma unroll
-        for (int j = 0; j < TNB / 2; ++j) {
-          const int col = nt * (BNR / 2) + wn * (TNR / 2) + j * 32 + fr;
-          C[col] = f32_to_bf16(silu_mul(acc[i][j][r], acc[i][j + TNB / 2][r]));
-        }
-      } else if (MODE == kStore) {
-        uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
-#pragma unroll
-        for (int j = 0; j < TNB; ++j) C[nt * BNR + brow0[j] + fr] = f32_to_bf16(acc[i][j][r]);
-      } else {
-        float* C = static_cast<float*>(a.C) + static_cast<int64_t>(row) * a.ldc;
-#pragma unroll
-        for (int j = 0; j < TNB; ++j) {
-          const int col = nt * BNR + brow0[j] + fr;
-          if (col < a.N_valid) C[col] = acc[i][j][r];
-        }
-      }
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------------------
 // Large-M tile fed by global->LDS loads (gfx950 global_load_lds_dwordx4): each lane's 16 bytes
 // go straight from memory into LDS without passing through registers, so the waves issue
 // only the loads, the LDS fragment reads and the MFMAs. Two LDS stages (separate arrays, the
@@ -308,6 +134,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   const uint16_t* __restrict__ A = static_cast<const uint16_t*>(a.A);
   const uint16_t* __restrict__ B = static_cast<const uint16_t*>(a.B) + slot * a.b_stride;
   const int K = a.K;
+  int k0, klen;
+  k_range(a, k0, klen);
 
   // Load sources: instruction j of this wave fills rows 8 (wave + 4 j) .. +7 of its region.
   // Kept as 32-bit byte offsets from the (wave-uniform) operand bases: an expert's weights
@@ -321,7 +149,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
     const int blk = wave + 4 * j;
     const int r = 8 * blk + lrow;
     const int c = (lane & 7) ^ lrow ^ (blk & 1);
-    oa[j] = static_cast<uint32_t>(gemm_src_row(a, m0 + r)) * static_cast<uint32_t>(K * 2) + c * 16;
+    oa[j] = static_cast<uint32_t>(gemm_src_row(a, m0 + r)) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
   }
   uint32_t ob[NB];
 #pragma unroll
@@ -336,7 +164,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
       brow = nt * BNR + r;
       if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
     }
-    ob[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16;
+    ob[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
   }
   auto issue = [&](int kt, uint8_t* dA, uint8_t* dB) {
     const uint32_t ko = static_cast<uint32_t>(kt) * (BK * 2);
@@ -401,7 +229,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   // K step t lives in LDS stage t % 2: wait for this wave's loads of step t, barrier (every
   // wave's loads landed and every wave is done reading the other stage), issue step t + 1
   // into the other stage, compute step t.
-  const int nk = K / BK;
+  const int nk = klen / BK;
   issue(0, sA0, sB0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
@@ -440,7 +268,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TNB; ++j) C[nt * BNR + wn * TNR + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
       } else {
-        float* C = static_cast<float*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+        float* C = static_cast<float*>(a.C) + blockIdx.y * a.c_split_stride +
+                   static_cast<int64_t>(row) * a.ldc;
 #pragma unroll
         for (int j = 0; j < TNB; ++j) {
           const int col = nt * BNR + wn * TNR + j * 32 + fr;
@@ -452,32 +281,38 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Small-M tile for weight streaming: 16 rows x 16*NB B rows per workgroup; the 4 waves
-// split K, each streams its K range of every B row straight from global memory into
-// v_mfma_f32_16x16x32_bf16 operands; partial sums meet in LDS.
+// Weight-streaming tile for small row counts: 16*MB rows x 16*NB B rows per workgroup; the 4
+// waves split K, each streams its K range of every B row and A row straight from global
+// memory into v_mfma_f32_16x16x32_bf16 operands (U K steps in flight); partial sums meet in
+// LDS. Tiles follow the XCD-aware order of the LDS-fed kernel.
 // ----------------------------------------------------------------------------------------
-template <int NB, int MODE>
+template <int NB, int MODE, int MB = 1>
 __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
   constexpr int BNR = 16 * NB;
-  constexpr int U = 4;  // K steps in flight per wave
+  constexpr int U = MB >= 4 ? 2 : 4;  // K steps in flight per wave
   static_assert(MODE != kSiluMul || NB % 2 == 0, "gate/up pairs");
-  __shared__ float red[4][NB][4][64];
+  __shared__ float red[4][MB][NB][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int mb = blockIdx.x % a.m_blocks;
-  const int nt = blockIdx.x / a.m_blocks;
-  const int m0 = mb * 16;
-  if (m0 >= gemm_rows_active(a)) return;
+  int mb, nt;
+  if (!tile_of_block(blockIdx.x, (gemm_rows_active(a) + 16 * MB - 1) / (16 * MB), a.n_tiles, mb, nt))
+    return;
+  const int m0 = mb * 16 * MB;
   const int slot = a.block_expert ? a.block_expert[m0 / a.block_m] : 0;
   const uint16_t* __restrict__ A = static_cast<const uint16_t*>(a.A);
   const uint16_t* __restrict__ B = static_cast<const uint16_t*>(a.B) + slot * a.b_stride;
   const int K = a.K;
   const int q = lane & 15;
   const int kq = (lane >> 4) * 8;
+  int k0, klen;
+  k_range(a, k0, klen);
 
-  const uint16_t* pa = A + static_cast<int64_t>(gemm_src_row(a, m0 + q)) * K + kq;
+  const uint16_t* pa[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+    pa[i] = A + static_cast<int64_t>(gemm_src_row(a, m0 + 16 * i + q)) * K + k0 + kq;
   const uint16_t* pb[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -488,58 +323,71 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
       brow = nt * BNR + nb * 16 + q;
       if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
     }
-    pb[nb] = B + static_cast<int64_t>(brow) * K + kq;
+    pb[nb] = B + static_cast<int64_t>(brow) * K + k0 + kq;
   }
 
-  f32x4 acc[NB];
+  f32x4 acc[MB][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[i][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int steps = K / 32;
+  const int steps = klen / 32;
   const int s0 = steps * wave / 4;
   const int s1 = steps * (wave + 1) / 4;
   int s = s0;
   for (; s + U <= s1; s += U) {
-    uint4 va[U], vb[U][NB];
+    uint4 va[U][MB], vb[U][NB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      va[u] = load16(pa + (s + u) * 32);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16(pb[nb] + (s + u) * 32);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) va[u][i] = load16(pa[i] + (s + u) * 32);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[u]), as_bf16x8(vb[u][nb]),
-                                                          acc[nb], 0, 0, 0);
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[u][i]), as_bf16x8(vb[u][nb]),
+                                                               acc[i][nb], 0, 0, 0);
   }
   for (; s < s1; ++s) {
-    const bf16x8 fa = as_bf16x8(load16(pa + s * 32));
+    bf16x8 fa[MB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, as_bf16x8(load16(pb[nb] + s * 32)),
-                                                        acc[nb], 0, 0, 0);
+    for (int i = 0; i < MB; ++i) fa[i] = as_bf16x8(load16(pa[i] + s * 32));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8 fb = as_bf16x8(load16(pb[nb] + s * 32));
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb, acc[i][nb], 0, 0, 0);
+    }
   }
 
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][nb][r][lane] = acc[nb][r];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][i][nb][r][lane] = acc[i][nb][r];
   __syncthreads();
 
-  // acc[nb][r] of lane l sits at row 4*(l/16) + r, B row nb*16 + l%16.
-  constexpr int NOUT = (MODE == kSiluMul ? NB / 2 : NB) * 4 * 64;
+  // acc[i][nb][r] of lane l sits at row 16 i + 4*(l/16) + r, B row nb*16 + l%16.
+  constexpr int NOUT = MB * (MODE == kSiluMul ? NB / 2 : NB) * 4 * 64;
   for (int idx = tid; idx < NOUT; idx += 256) {
     const int l = idx & 63;
     const int r = (idx >> 6) & 3;
-    const int nb = idx >> 8;
-    const int row = m0 + 4 * (l >> 4) + r;
+    const int nb = (idx >> 8) % (MODE == kSiluMul ? NB / 2 : NB);
+    const int i = (idx >> 8) / (MODE == kSiluMul ? NB / 2 : NB);
+    const int row = m0 + 16 * i + 4 * (l >> 4) + r;
     if (row >= a.M_rows) continue;
-    const float v = red[0][nb][r][l] + red[1][nb][r][l] + red[2][nb][r][l] + red[3][nb][r][l];
+    const float v = red[0][i][nb][r][l] + red[1][i][nb][r][l] + red[2][i][nb][r][l] + red[3][i][nb][r][l];
     if (MODE == kSiluMul) {
       const int nu = nb + NB / 2;
-      const float u = red[0][nu][r][l] + red[1][nu][r][l] + red[2][nu][r][l] + red[3][nu][r][l];
+      const float u = red[0][i][nu][r][l] + red[1][i][nu][r][l] + red[2][i][nu][r][l] + red[3][i][nu][r][l];
       uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
       C[nt * (BNR / 2) + nb * 16 + (l & 15)] = f32_to_bf16(silu_mul(v, u));
     } else if (MODE == kStore) {
@@ -547,7 +395,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
       C[nt * BNR + nb * 16 + (l & 15)] = f32_to_bf16(v);
     } else {
       const int col = nt * BNR + nb * 16 + (l & 15);
-      if (col < a.N_valid) static_cast<float*>(a.C)[static_cast<int64_t>(row) * a.ldc + col] = v;
+      if (col < a.N_valid)
+        static_cast<float*>(a.C)[blockIdx.y * a.c_split_stride + static_cast<int64_t>(row) * a.ldc + col] = v;
     }
   }
 }

@@ -15,12 +15,17 @@ constexpr int kAlignChunk = 256;
 
 inline int align_chunks(int64_t T) { return static_cast<int>((T + kAlignChunk - 1) / kAlignChunk); }
 
-// Router logits [T, E] fp32 = x . Wg^T (bias is added by the top-k pass).
+// Number of K splits of the router logits GEMM for T tokens (enough workgroups to fill the
+// chip when T is small; each split's K range stays a multiple of 256).
+int router_splits(const moe_params& p, int T);
+
+// Router logits: router_splits() partial sums [splits, T, E] fp32 of x . Wg^T.
 int launch_router_logits(const moe_params& p, int T, const void* x, const void* w_gate,
                          float* logits, hipStream_t s);
 
-// fp32 softmax, (grouped) top-k, renormalise, scale, expert_map lookup.
-int launch_topk(const moe_params& p, int T, const float* logits, const float* bias,
+// Sum of the logit partials (written back into partial 0), fp32 softmax, (grouped) top-k,
+// renormalise, scale, expert_map lookup.
+int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
                 const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s);
 
 // Count / scan / scatter of the (token, slot) pairs by local expert.

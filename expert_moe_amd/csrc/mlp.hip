@@ -18,32 +18,41 @@ void launch_tile(GemmArgs a, int n_rows_b, hipStream_t s) {
   gemm_bf16_dma<BM, BNR, WM, WN, MODE><<<tile_grid(a.m_blocks, a.n_tiles), 256, 0, s>>>(a);
 }
 
+// Weight-row tile (BNR) for a launch: the widest of 256 / 128 / 64 that divides n_rows_b and
+// still gives about two workgroups per CU for the expected number of row blocks.
+inline int pick_bnr(int n_rows_b, int est_blocks, bool silu) {
+  constexpr int kWant = 480;
+  if (n_rows_b % 256 == 0 && est_blocks * (n_rows_b / 256) >= kWant) return 256;
+  // gate/up tiles pair gate and up rows: 2I is a multiple of 128, and 128 keeps the pairs
+  if (n_rows_b % 128 == 0 && (est_blocks * (n_rows_b / 128) >= kWant || silu)) return 128;
+  return 64;
+}
+
 template <int MODE>
-void launch_tile256(const GemmArgs& a, int n_rows_b, hipStream_t s) {
-  if (n_rows_b % 256 == 0)
+void launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
+  if (bnr == 256)
     launch_tile<256, 256, 2, 2, MODE>(a, n_rows_b, s);
-  else if (n_rows_b % 128 == 0)
+  else if (bnr == 128)
     launch_tile<256, 128, 2, 2, MODE>(a, n_rows_b, s);
   else
     launch_tile<256, 64, 4, 1, MODE>(a, n_rows_b, s);
 }
 
 template <int MODE>
-void launch_tile128(const GemmArgs& a, int n_rows_b, hipStream_t s) {
-  // n_rows_b: B rows spanned by the whole output (2I for the silu GEMM, H for the store)
-  if (n_rows_b % 256 == 0)
+void launch_tile128(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
+  if (bnr == 256)
     launch_tile<128, 256, 2, 2, MODE>(a, n_rows_b, s);
-  else if (n_rows_b % 128 == 0)
+  else if (bnr == 128)
     launch_tile<128, 128, 2, 2, MODE>(a, n_rows_b, s);
   else
     launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, s);
 }
 
 template <int MODE>
-void launch_tile64(const GemmArgs& a, int n_rows_b, hipStream_t s) {
-  if (n_rows_b % 256 == 0)
+void launch_tile64(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
+  if (bnr == 256)
     launch_tile<64, 256, 1, 4, MODE>(a, n_rows_b, s);
-  else if (n_rows_b % 128 == 0)
+  else if (bnr == 128)
     launch_tile<64, 128, 2, 2, MODE>(a, n_rows_b, s);
   else if constexpr (MODE != kSiluMul)  // 2I is always a multiple of 128
     launch_tile<64, 64, 2, 2, MODE>(a, n_rows_b, s);
@@ -53,11 +62,54 @@ void launch_tile64(const GemmArgs& a, int n_rows_b, hipStream_t s) {
 
 namespace {
 
-// Rows per tile: the sorted granule when rows are expert-sorted, else by row count.
-int tile_rows(const moe_params& p, bool sorted, int block_m, int rows) {
-  if (p.dtype == MOE_F32) return 16;
-  if (sorted) return block_m <= 32 ? 16 : block_m;
-  return rows <= 64 ? 16 : 128;
+// Kernel family and rows per row block of a launch. Expert-sorted rows follow the padding
+// granule (each row block stays inside one expert); dense rows follow the row count.
+//   stream MB=1/2   : 16/32 rows, weights streamed from global memory into MFMA operands
+//   tile 64/128/256 : LDS-fed MFMA tile (measured faster from 64 rows up inside the MoE,
+//                     where the row blocks of one expert share each weight tile in L2)
+struct Plan {
+  bool stream;
+  int rows;  // rows per row block
+};
+
+Plan plan_rows(const moe_params& p, bool sorted, int block_m, int rows) {
+  if (p.dtype == MOE_F32) return {false, 16};
+  const int r = sorted ? block_m : rows;
+  if (r <= 16) return {true, 16};
+  if (r <= 32) return {true, 32};
+  if (sorted) return {false, block_m};
+  return {false, rows <= 1024 ? 64 : 128};
+}
+
+// Row blocks a launch is expected to have: every local expert's expected rows (uniform
+// routing) rounded up to the block, or the dense row count.
+int est_row_blocks(const moe_params& p, int T, bool sorted, int tr, int rows) {
+  if (!sorted) return (rows + tr - 1) / tr;
+  const double per = static_cast<double>(T) * p.top_k / p.num_experts;
+  const int blocks = static_cast<int>(p.num_local_experts * (per / tr + 0.5)) + 1;
+  const int cap = (rows + tr - 1) / tr;
+  return blocks < cap ? blocks : cap;
+}
+
+// Streaming kernel with MB 16-row blocks per workgroup; 32 weight rows per workgroup when 64
+// would leave CUs idle. m_blocks counts row blocks of 16*MB rows.
+template <int MODE, int MB>
+void launch_stream_mb(GemmArgs g, int n_rows_b, int est_blocks, hipStream_t s) {
+  if (est_blocks * (n_rows_b / 64) >= 512 || n_rows_b % 32 != 0) {
+    g.n_tiles = n_rows_b / 64;
+    gemm_bf16_stream<4, MODE, MB><<<tile_grid(g.m_blocks, g.n_tiles), 256, 0, s>>>(g);
+  } else {
+    g.n_tiles = n_rows_b / 32;
+    gemm_bf16_stream<2, MODE, MB><<<tile_grid(g.m_blocks, g.n_tiles), 256, 0, s>>>(g);
+  }
+}
+
+template <int MODE>
+void launch_stream(GemmArgs g, int n_rows_b, int rows_per_block, int est_blocks, hipStream_t s) {
+  if (rows_per_block == 16)
+    launch_stream_mb<MODE, 1>(g, n_rows_b, est_blocks, s);
+  else
+    launch_stream_mb<MODE, 2>(g, n_rows_b, est_blocks, s);
 }
 
 GemmArgs base_args(const moe_params& p, int T, const int32_t* num_padded,
@@ -90,18 +142,21 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
   g.N_valid = I;
   g.C = act;
   g.ldc = I;
-  const int tr = tile_rows(p, row_map != nullptr, block_m, rows);
+  const bool sorted = row_map != nullptr;
+  const Plan pl = plan_rows(p, sorted, block_m, rows);
+  const int tr = pl.rows;
   g.m_blocks = ceil_div(rows, tr);
+  const int est = est_row_blocks(p, T, sorted, tr, rows);
   if (p.dtype == MOE_F32)
     gemm_f32_tile<kSiluMul><<<g.m_blocks * (I / 32), 256, 0, s>>>(g);
-  else if (tr == 16)
-    gemm_bf16_stream<4, kSiluMul><<<g.m_blocks * (I / 32), 256, 0, s>>>(g);
+  else if (pl.stream)
+    launch_stream<kSiluMul>(g, 2 * I, tr, est, s);
   else if (tr == 64)
-    launch_tile64<kSiluMul>(g, 2 * I, s);
+    launch_tile64<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), s);
   else if (tr == 128)
-    launch_tile128<kSiluMul>(g, 2 * I, s);
+    launch_tile128<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), s);
   else
-    launch_tile256<kSiluMul>(g, 2 * I, s);
+    launch_tile256<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -122,18 +177,21 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   g.N_valid = H;
   g.C = y;
   g.ldc = H;
-  const int tr = tile_rows(p, num_padded != nullptr, block_m, rows);
+  const bool sorted = num_padded != nullptr;
+  const Plan pl = plan_rows(p, sorted, block_m, rows);
+  const int tr = pl.rows;
   g.m_blocks = ceil_div(rows, tr);
+  const int est = est_row_blocks(p, T, sorted, tr, rows);
   if (p.dtype == MOE_F32)
     gemm_f32_tile<kStore><<<g.m_blocks * (H / 64), 256, 0, s>>>(g);
-  else if (tr == 16)
-    gemm_bf16_stream<4, kStore><<<g.m_blocks * (H / 64), 256, 0, s>>>(g);
+  else if (pl.stream)
+    launch_stream<kStore>(g, H, tr, est, s);
   else if (tr == 64)
-    launch_tile64<kStore>(g, H, s);
+    launch_tile64<kStore>(g, H, pick_bnr(H, est, false), s);
   else if (tr == 128)
-    launch_tile128<kStore>(g, H, s);
+    launch_tile128<kStore>(g, H, pick_bnr(H, est, false), s);
   else
-    launch_tile256<kStore>(g, H, s);
+    launch_tile256<kStore>(g, H, pick_bnr(H, est, false), s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

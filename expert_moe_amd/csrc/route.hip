@@ -20,7 +20,8 @@ namespace moe {
 namespace {
 
 struct TopkArgs {
-  const float* logits;
+  float* logits;  // [splits, T, E] partial sums; their total is written back to split 0
+  int splits;
   const float* bias;
   const int32_t* emap;
   int32_t* ids;
@@ -71,7 +72,11 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     const int e = lane + 64 * q;
     float l = -INFINITY;
     if (valid && e < E) {
-      l = a.logits[static_cast<int64_t>(t) * E + e];
+      float* lp = a.logits + static_cast<int64_t>(t) * E + e;
+      l = lp[0];
+      const int64_t stride = static_cast<int64_t>(a.T) * E;
+      for (int sp = 1; sp < a.splits; ++sp) l += lp[sp * stride];
+      if (a.splits > 1) lp[0] = l;
       if (a.bias) l += a.bias[e];
     }
     pv[q] = l;
@@ -145,6 +150,16 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
 
 }  // namespace
 
+int router_splits(const moe_params& p, int T) {
+  if (p.dtype == MOE_F32) return 1;
+  const int rows = T <= 64 ? 16 : 128;
+  const int bnr = 64;
+  const int blocks = ((T + rows - 1) / rows) * ((p.num_experts + bnr - 1) / bnr);
+  int sp = 1;
+  while (sp < 16 && blocks * sp < 512 && p.hidden_size % (256 * 2 * sp) == 0) sp *= 2;
+  return sp;
+}
+
 int launch_router_logits(const moe_params& p, int T, const void* x, const void* w_gate,
                          float* logits, hipStream_t s) {
   GemmArgs a{};
@@ -163,26 +178,37 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
   a.N_valid = p.num_experts;
   a.C = logits;
   a.ldc = p.num_experts;
-  const int n_tiles = ceil_div(p.num_experts, 64);
+  const int bnr = 64;
+  const int n_tiles = ceil_div(p.num_experts, bnr);
+  a.k_splits = router_splits(p, T);
+  a.c_split_stride = static_cast<int64_t>(T) * p.num_experts;
   if (p.dtype == MOE_F32) {
     a.m_blocks = ceil_div(T, 16);
     gemm_f32_tile<kStoreF32><<<a.m_blocks * n_tiles, 256, 0, s>>>(a);
   } else if (T <= 64) {
     a.m_blocks = ceil_div(T, 16);
-    gemm_bf16_stream<4, kStoreF32><<<a.m_blocks * n_tiles, 256, 0, s>>>(a);
+    a.n_tiles = n_tiles;
+    gemm_bf16_stream<4, kStoreF32><<<dim3(tile_grid(a.m_blocks, n_tiles), a.k_splits), 256, 0, s>>>(a);
   } else {
     a.m_blocks = ceil_div(T, 128);
     a.n_tiles = n_tiles;
-    gemm_bf16_dma<128, 64, 4, 1, kStoreF32><<<tile_grid(a.m_blocks, n_tiles), 256, 0, s>>>(a);
+    const dim3 grid(tile_grid(a.m_blocks, n_tiles), a.k_splits);
+    if (bnr == 256)
+      gemm_bf16_dma<128, 256, 2, 2, kStoreF32><<<grid, 256, 0, s>>>(a);
+    else if (bnr == 128)
+      gemm_bf16_dma<128, 128, 2, 2, kStoreF32><<<grid, 256, 0, s>>>(a);
+    else
+      gemm_bf16_dma<128, 64, 4, 1, kStoreF32><<<grid, 256, 0, s>>>(a);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
 
-int launch_topk(const moe_params& p, int T, const float* logits, const float* bias,
+int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
                 const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s) {
   TopkArgs a;
   a.logits = logits;
+  a.splits = router_splits(p, T);
   a.bias = bias;
   a.emap = expert_map;
   a.ids = ids;
