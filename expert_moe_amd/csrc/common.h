@@ -37,15 +37,33 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes at `src`
-// land at LDS address lds_base + 16 l; lds_base must be the same for the whole wave. The
-// builtin only exists in the device compilation pass; the host pass (which only needs the
-// kernel's launch stub) sees an empty body.
-__device__ __forceinline__ void lds_load16(const void* src, void* lds_base) {
+// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes at
+// base + voff land at LDS byte address lds_addr + 16 l; base and lds_addr are wave-uniform.
+// Written as inline asm on purpose: the compiler has to assume that such a load may touch
+// both LDS and global memory, and once one is in flight it degrades every later LDS wait to
+// lgkmcnt(0), which serialises the fragment reads of the next K slice with the MFMAs of the
+// current one. The compiler does not see the load, so the caller waits for it explicitly
+// (s_waitcnt vmcnt) before any wave reads the data. M0 carries the LDS address (an operand
+// of the asm, so the compiler writes it); one wait state separates that write from the
+// load. Device pass only (the host pass needs the kernel's launch stub alone).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "{m0}"(lds_addr)
+               : "memory");
 #endif
 }
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  using lds_ptr = const __attribute__((address_space(3))) uint8_t*;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);  // vmcnt(0)
+constexpr int kWaitVmLgkm0 = 0x7 << 4;              // vmcnt(0) lgkmcnt(0)
 
 // Plain 16-byte global load.
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }

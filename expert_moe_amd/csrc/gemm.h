@@ -11,6 +11,8 @@
 // logits.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -47,10 +49,6 @@ __device__ __forceinline__ void k_range(const GemmArgs& a, int& k0, int& klen) {
   klen = a.K / s;
   k0 = static_cast<int>(blockIdx.y) * klen;
 }
-
-// s_waitcnt immediate that waits for every outstanding vector memory load (vmcnt = 0) and
-// nothing else (expcnt and lgkmcnt left at their maxima).
-constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
 
 // MI355X dispatches workgroup i to XCD i % 8; each XCD has its own L2.
 constexpr int kXcds = 8;
@@ -97,9 +95,17 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
 // ----------------------------------------------------------------------------------------
 // Large-M tile fed by global->LDS loads (gfx950 global_load_lds_dwordx4): each lane's 16 bytes
 // go straight from memory into LDS without passing through registers, so the waves issue
-// only the loads, the LDS fragment reads and the MFMAs. Two LDS stages (separate arrays, the
-// loop unrolled by two so each is addressed statically): the loads of K step t+1 fly while
-// step t computes.
+// only the loads, the LDS fragment reads and the MFMAs. 4 waves, K step BK = 64, two LDS
+// stages (separate arrays, addressed statically).
+//
+// Schedule of K step t (stage S = t % 2, the other stage S' holds step t + 1, in flight):
+//   slice 0..2 : read the fragments of slice s+1 from S, then the MFMAs of slice s
+//   sync point : wait for this wave's loads of step t+1 and its slice-3 reads, barrier
+//                (now every load of step t+1 has landed and no wave reads S any more)
+//   slice 3    : read slice 0 of step t+1 from S', then the MFMAs of slice 3 with the loads
+//                of step t+2 into S spread between them
+// so the MFMA pipe keeps working across the step boundary and the loads have a whole step
+// to land.
 // LDS rows are the 64 bf16 (128 bytes) of one tile row; the eight 16-byte chunks of row r are
 // stored at chunk ^ sw(r), sw(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of
 // 16 consecutive rows hit distinct banks. One load instruction fills 8 rows (1 KiB, lane l at
@@ -115,6 +121,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   constexpr int TNB = TNR / 32;
   constexpr int NA = BM / 32;              // A load instructions per wave per K step
   constexpr int NB = BNR / 32;             // B load instructions per wave per K step
+  constexpr int ND = NA + NB;
   static_assert(WM * WN == 4, "4 waves");
   static_assert(TMB >= 1 && TNB >= 1 && NA >= 1 && NB >= 1, "tile too small");
   static_assert(MODE != kSiluMul || (TNB % 2 == 0), "gate/up pairs");
@@ -131,27 +138,24 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   if (!tile_of_block(blockIdx.x, (gemm_rows_active(a) + BM - 1) / BM, a.n_tiles, mb, nt)) return;
   const int m0 = mb * BM;
   const int slot = a.block_expert ? a.block_expert[m0 / a.block_m] : 0;
-  const uint16_t* __restrict__ A = static_cast<const uint16_t*>(a.A);
-  const uint16_t* __restrict__ B = static_cast<const uint16_t*>(a.B) + slot * a.b_stride;
+  const char* const Abase = static_cast<const char*>(a.A);
+  const char* const Bbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.B) + slot * a.b_stride);
   const int K = a.K;
   int k0, klen;
   k_range(a, k0, klen);
 
-  // Load sources: instruction j of this wave fills rows 8 (wave + 4 j) .. +7 of its region.
-  // Kept as 32-bit byte offsets from the (wave-uniform) operand bases: an expert's weights
-  // and the activations are each far below 4 GiB.
+  // Load sources: instruction d < NA of this wave fills A rows 8 (wave + 4 d) .. +7, the
+  // others B rows likewise. Kept as 32-bit byte offsets from the (wave-uniform) operand
+  // bases: an expert's weights and the activations are each far below 4 GiB.
   const int lrow = lane >> 3;
-  const char* const Abase = reinterpret_cast<const char*>(A);
-  const char* const Bbase = reinterpret_cast<const char*>(B);
-  uint32_t oa[NA];
+  uint32_t goff[ND];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
     const int blk = wave + 4 * j;
     const int r = 8 * blk + lrow;
     const int c = (lane & 7) ^ lrow ^ (blk & 1);
-    oa[j] = static_cast<uint32_t>(gemm_src_row(a, m0 + r)) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
+    goff[j] = static_cast<uint32_t>(gemm_src_row(a, m0 + r)) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
   }
-  uint32_t ob[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int blk = wave + 4 * j;
@@ -164,14 +168,17 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
       brow = nt * BNR + r;
       if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
     }
-    ob[j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
+    goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
   }
-  auto issue = [&](int kt, uint8_t* dA, uint8_t* dB) {
-    const uint32_t ko = static_cast<uint32_t>(kt) * (BK * 2);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) lds_load16(Abase + (oa[j] + ko), dA + (wave + 4 * j) * 1024);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) lds_load16(Bbase + (ob[j] + ko), dB + (wave + 4 * j) * 1024);
+  const uint32_t lA[2] = {lds_addr(sA0), lds_addr(sA1)};
+  const uint32_t lB[2] = {lds_addr(sB0), lds_addr(sB1)};
+  // load instruction d of K step kt into stage st
+  auto dma = [&](int d, int kt, int st) {
+    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
+    if (d < NA)
+      dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + 4 * d) * 1024));
+    else
+      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + 4 * (d - NA)) * 1024));
   };
 
   const int wm = wave % WM;
@@ -201,51 +208,96 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](const uint8_t* sA, const uint8_t* sB) {
-    bf16x8 fa[2][TMB], fb[2][TNB];
-    auto frags = [&](int ks, int set) {
+  bf16x8 fa[2][TMB], fb[2][TNB];  // fragments of two K slices
+  auto frags = [&](const uint8_t* sA, const uint8_t* sB, int ks, int set) {
 #pragma unroll
-      for (int i = 0; i < TMB; ++i)
-        fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sA + arow[i] + coff[ks]));
+    for (int i = 0; i < TMB; ++i) fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sA + arow[i] + coff[ks]));
 #pragma unroll
-      for (int j = 0; j < TNB; ++j)
-        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sB + brow0[j] + coff[ks]));
-    };
-    frags(0, 0);
+    for (int j = 0; j < TNB; ++j) fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sB + brow0[j] + coff[ks]));
+  };
+  // MFMAs of one K slice. DM = 0: nothing else; DM = 1 + st: the ND loads of K step kt_dma
+  // into stage st go between them.
+  auto mfmas = [&](int set, auto dm_c, int kt_dma) {
+    constexpr int DM = decltype(dm_c)::value;
+    constexpr int NM = TMB * TNB;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) frags(ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int m = 0; m < NM; ++m) {
+      acc[m / TNB][m % TNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][m / TNB], fb[set][m % TNB],
+                                                                      acc[m / TNB][m % TNB], 0, 0, 0);
+      if constexpr (DM != 0) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < TMB; ++i)
-#pragma unroll
-        for (int j = 0; j < TNB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
-                                                              0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int d = m * ND / NM; d < (m + 1) * ND / NM; ++d) dma(d, kt_dma, DM - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  // K step kt on stage ST. KIND 0: step kt+1 is in flight and step kt+2 gets loaded into
+  // this stage; 1: step kt+1 is in flight and is the last; 2: kt is the last step.
+  auto step = [&](auto st_c, auto kind_c, int kt) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int KIND = decltype(kind_c)::value;
+    const uint8_t* sA = ST ? sA1 : sA0;
+    const uint8_t* sB = ST ? sB1 : sB0;
+    __builtin_amdgcn_sched_barrier(0);
+    frags(sA, sB, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0, C0{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(sA, sB, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1, C0{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(sA, sB, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0, C0{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KIND < 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+      __syncthreads();
+      frags(ST ? sA0 : sA1, ST ? sB0 : sB1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (KIND == 0)
+        mfmas(1, std::integral_constant<int, 1 + ST>{}, kt + 2);
+      else
+        mfmas(1, C0{}, 0);
+    } else {
+      mfmas(1, C0{}, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // K step t lives in LDS stage t % 2: wait for this wave's loads of step t, barrier (every
-  // wave's loads landed and every wave is done reading the other stage), issue step t + 1
-  // into the other stage, compute step t.
+  // Prologue: step 0 landed in stage 0, step 1 in flight into stage 1, slice 0 read.
   const int nk = klen / BK;
-  issue(0, sA0, sB0);
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
-    issue(kt + 1, sA1, sB1);
-    compute(sA0, sB0);
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
-    if (kt + 2 < nk) issue(kt + 2, sA0, sB0);
-    compute(sA1, sB1);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) dma(d, 0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if (nk > 1) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma(d, 1, 1);
   }
-  if (kt < nk) {
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
-    compute(sA0, sB0);
+  frags(sA0, sB0, 0, 0);
+  if (nk == 1) {
+    step(C0{}, C2{}, 0);
+  } else if ((nk & 1) == 0) {
+    for (int kt = 0; kt < nk - 2; kt += 2) {
+      step(C0{}, C0{}, kt);
+      step(C1{}, C0{}, kt + 1);
+    }
+    step(C0{}, C1{}, nk - 2);
+    step(C1{}, C2{}, nk - 1);
+  } else {
+    for (int kt = 0; kt < nk - 3; kt += 2) {
+      step(C0{}, C0{}, kt);
+      step(C1{}, C0{}, kt + 1);
+    }
+    step(C0{}, C0{}, nk - 3);
+    step(C1{}, C1{}, nk - 2);
+    step(C0{}, C2{}, nk - 1);
   }
 
   // Epilogue. acc[i][j][r] sits at tile row wm*TM + i*32 + 8*(r/4) + 4*(lane/32) + r%4 and

@@ -41,6 +41,10 @@ SMALL = {
                     ep_size=8, ep_rank=0, shared_intermediate_size=256, zipf_bias=1.2), 600),
     # granule 128: 250 rows per expert, ragged
     "mix_m": (W("mix_m", 15, "medium Mixtral-like", "bf16", (1000,), 256, 8, 256, 2, True), 1000),
+    # a single 64-wide K step in the router, gate/up and down GEMMs
+    "k64": (W("k64", 16, "one K step", "bf16", (300,), 64, 8, 64, 2, True), 300),
+    # odd numbers of K steps (3 and 5) in 256-row tiles with 128- and 64-row weight tiles
+    "odd_l": (W("odd_l", 17, "odd K steps, large tiles", "bf16", (2400,), 192, 4, 320, 2, True), 2400),
 }
 
 
