@@ -1,5 +1,6 @@
 // C ABI of the fused MoE forward: argument checks, workspace layout, launch order.
 // Declarations and the contract of every entry point are in include/moe.h.
+#include <initializer_list>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -131,6 +132,13 @@ T_* at(void* ws, size_t off) {
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Tensor pointers must be 16-byte aligned (the kernels move 16-byte vectors); NULL passes.
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +203,7 @@ int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void
   if ((rc = check_tokens(*p, num_tokens))) return rc;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w_gate || !expert_map || !topk_ids || !topk_w || !topk_local || !ws) return MOE_EINVAL;
+  if (!aligned16({x, w_gate, ws})) return MOE_EINVAL;
   const Layout L = layout(*p, num_tokens, 16);
   if (ws_bytes < L.route_need) return MOE_ENOSPC;
   const int T = static_cast<int>(num_tokens);
@@ -215,6 +224,7 @@ int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* to
   if (num_tokens == 0) return MOE_OK;
   if (!topk_local || !sorted_pairs || !block_expert || !pair_row || !num_padded || !ws)
     return MOE_EINVAL;
+  if (!aligned16({ws})) return MOE_EINVAL;
   const Layout L = layout(*p, num_tokens, block_m);
   if (ws_bytes < L.align_need) return MOE_ENOSPC;
   int32_t* meta = static_cast<int32_t*>(ws);
@@ -234,6 +244,7 @@ int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, cons
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w13 || !w2 || !sorted_pairs || !block_expert || !num_padded || !y || !ws)
     return MOE_EINVAL;
+  if (!aligned16({x, w13, w2, y, ws})) return MOE_EINVAL;
   const Layout L = layout(*p, num_tokens, block_m);
   if (ws_bytes < L.mlp_need) return MOE_ENOSPC;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
@@ -251,6 +262,7 @@ int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, c
   if (!valid_block_m(block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w13 || !sorted_pairs || !block_expert || !num_padded || !act) return MOE_EINVAL;
+  if (!aligned16({x, w13, act})) return MOE_EINVAL;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_gate_up(*p, static_cast<int>(num_tokens), x, w13, p->intermediate_size,
                              sorted_pairs, num_padded, block_expert, block_m, rows, act,
@@ -266,6 +278,7 @@ int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, co
   if (!valid_block_m(block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!act || !w2 || !block_expert || !num_padded || !y) return MOE_EINVAL;
+  if (!aligned16({act, w2, y})) return MOE_EINVAL;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_down(*p, static_cast<int>(num_tokens), act, w2, p->intermediate_size,
                           num_padded, block_expert, block_m, rows, y, as_stream(stream));
@@ -280,6 +293,7 @@ int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,
   if (p->shared_intermediate_size == 0) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !shared_w13 || !shared_w2 || !shared_y || !ws) return MOE_EINVAL;
+  if (!aligned16({x, shared_w13, shared_w2, shared_y, ws})) return MOE_EINVAL;
   const Layout L = layout(*p, num_tokens, 16);
   if (ws_bytes < L.shared_need) return MOE_ENOSPC;
   const int T = static_cast<int>(num_tokens);
@@ -294,6 +308,7 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
   if ((rc = check_tokens(*p, num_tokens))) return rc;
   if (num_tokens == 0) return MOE_OK;
   if (!y || !pair_row || !topk_w || !out) return MOE_EINVAL;
+  if (!aligned16({y, shared_y, out})) return MOE_EINVAL;
   return moe::launch_combine(*p, static_cast<int>(num_tokens), y, pair_row, topk_w, shared_y, out,
                              as_stream(stream));
 }
@@ -311,6 +326,7 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
   if (shared && p->shared_intermediate_size == 0) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w_gate || !expert_map || !w13 || !w2 || !out || !ws) return MOE_EINVAL;
+  if (!aligned16({x, w_gate, w13, w2, shared_w13, shared_w2, out, ws})) return MOE_EINVAL;
   const int bm = pick_block_m(*p, num_tokens);
   const Layout L = layout(*p, num_tokens, bm);
   if (ws_bytes < L.total) return MOE_ENOSPC;

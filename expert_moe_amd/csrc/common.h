@@ -26,15 +26,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: gfx950
+// v_cvt_pk_bf16_f32, the same rounding as f32_to_bf16 on finite inputs.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// silu(g) * u with silu(g) = g / (1 + e^-g).
+// silu(g) * u with silu(g) = g / (1 + e^-g); the quotient uses the hardware reciprocal
+// (about 1 ulp), far below the bf16 rounding the result gets.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes at

@@ -222,7 +222,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
     constexpr int NM = TMB * TNB;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      acc[m / TNB][m % TNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][m / TNB], fb[set][m % TNB],
+      // weight fragment first: acc holds the transposed block (see the epilogue)
+      acc[m / TNB][m % TNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][m % TNB], fa[set][m / TNB],
                                                                       acc[m / TNB][m % TNB], 0, 0, 0);
       if constexpr (DM != 0) {
         __builtin_amdgcn_sched_barrier(0);
@@ -300,32 +301,64 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
     step(C0{}, C2{}, nk - 1);
   }
 
-  // Epilogue. acc[i][j][r] sits at tile row wm*TM + i*32 + 8*(r/4) + 4*(lane/32) + r%4 and
-  // tile B row (brow0[j] / ROWB - fr) + lane%32.
+  // Epilogue. The MFMAs take the weight fragment as first operand, so acc[i][j] is the
+  // transposed 32x32 block: register r of lane l belongs to output row wm*TM + i*32 + l%32 and
+  // to column 8*(r/4) + 4*(l/32) + r%4 of the block's 32 output columns, i.e. each lane holds
+  // four consecutive columns in each group q = r/4.
+  const int orow = m0 + wm * TM + fr;
+  if constexpr (MODE == kStoreF32) {
 #pragma unroll
-  for (int i = 0; i < TMB; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    for (int i = 0; i < TMB; ++i) {
+      const int row = orow + i * 32;
       if (row >= a.M_rows) continue;
-      if (MODE == kSiluMul) {
-        uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+      float* C = static_cast<float*>(a.C) + blockIdx.y * a.c_split_stride + static_cast<int64_t>(row) * a.ldc;
 #pragma unroll
-        for (int j = 0; j < TNB / 2; ++j) {
-          const int col = nt * (BNR / 2) + wn * (TNR / 2) + j * 32 + fr;
-          C[col] = f32_to_bf16(silu_mul(acc[i][j][r], acc[i][j + TNB / 2][r]));
-        }
-      } else if (MODE == kStore) {
-        uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+      for (int j = 0; j < TNB; ++j)
 #pragma unroll
-        for (int j = 0; j < TNB; ++j) C[nt * BNR + wn * TNR + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
-      } else {
-        float* C = static_cast<float*>(a.C) + blockIdx.y * a.c_split_stride +
-                   static_cast<int64_t>(row) * a.ldc;
-#pragma unroll
-        for (int j = 0; j < TNB; ++j) {
-          const int col = nt * BNR + wn * TNR + j * 32 + fr;
+        for (int r = 0; r < 16; ++r) {
+          const int col = nt * BNR + wn * TNR + j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (col < a.N_valid) C[col] = acc[i][j][r];
+        }
+    }
+  } else {
+    // bf16 out: pack each group's four columns into two dwords, then swap groups between
+    // lanes l and l + 32 (v_permlane32_swap) so that lane l < 32 holds columns 0..7 and
+    // 16..23 of the block and lane l + 32 columns 8..15 and 24..31: two 16-byte stores.
+    constexpr int OUTB = MODE == kSiluMul ? TNB / 2 : TNB;  // 32-column output blocks per wave
+    const int col0 = (MODE == kSiluMul ? nt * (BNR / 2) + wn * (TNR / 2) : nt * BNR + wn * TNR) + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TMB; ++i) {
+      const int row = orow + i * 32;
+      uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc + col0;
+#pragma unroll
+      for (int j = 0; j < OUTB; ++j) {
+        uint32_t p[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float v0, v1;
+            if constexpr (MODE == kSiluMul) {
+              v0 = silu_mul(acc[i][j][4 * q + 2 * h], acc[i][j + TNB / 2][4 * q + 2 * h]);
+              v1 = silu_mul(acc[i][j][4 * q + 2 * h + 1], acc[i][j + TNB / 2][4 * q + 2 * h + 1]);
+            } else {
+              v0 = acc[i][j][4 * q + 2 * h];
+              v1 = acc[i][j][4 * q + 2 * h + 1];
+            }
+            p[q][h] = pack_bf16x2(v0, v1);
+          }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto s01 = __builtin_amdgcn_permlane32_swap(p[0][h], p[1][h], false, false);
+          const auto s23 = __builtin_amdgcn_permlane32_swap(p[2][h], p[3][h], false, false);
+          p[0][h] = s01[0];
+          p[1][h] = s01[1];
+          p[2][h] = s23[0];
+          p[3][h] = s23[1];
+        }
+        if (row < a.M_rows) {
+          *reinterpret_cast<uint4*>(C + j * 32) = uint4{p[0][0], p[0][1], p[1][0], p[1][1]};
+          *reinterpret_cast<uint4*>(C + j * 32 + 16) = uint4{p[2][0], p[2][1], p[3][0], p[3][1]};
         }
       }
     }

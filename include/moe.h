@@ -31,6 +31,8 @@
  *    rows I..2I-1 = W3 "up"); w2 [E_l, H, I]; shared_w13 [2 I_s, H]; shared_w2 [H, I_s];
  *    out [T, H]. x, weights, y and out use `dtype` (fp32 or bf16 bit patterns);
  *    router logits, probabilities and routing weights are fp32; ids are int32.
+ *  - x, weights, y, shared_y, act, out and the workspace must be 16-byte aligned (hipMalloc
+ *    and torch allocations are; kernels move 16-byte vectors), else MOE_EINVAL.
  *  - Return value: MOE_OK (0) or a negative MOE_E* code; nothing is enqueued on error,
  *    except MOE_EHIP, which reports a failed launch.
  *  - expert_map [E] int32 holds, for every GLOBAL expert id, its local slot in

@@ -144,6 +144,11 @@ def test_entry_point_argument_errors():
     assert L.moe_forward(pp, T, F, F, None, F, F, F, F, None, F, None, None, F, ws, None) == -1
     # workspace too small
     assert L.moe_forward(pp, T, F, F, None, F, F, F, F, F, F, None, None, F, ws - 1, None) == -3
+    # tensor pointers that are not 16-byte aligned
+    assert L.moe_forward(pp, T, F + 2, F, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, F, F, None, F, F, F, F, F, F + 8, None, None, F, ws, None) == -1
+    assert L.moe_grouped_mlp(pp, T, F, F, F, F, F, F, 16, F + 4, F, ws, None) == -1
+    assert L.moe_combine(pp, T, F, F, F, F + 2, F, None) == -1
     # negative token count
     assert L.moe_forward(pp, -1, F, F, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
     # bad block_m for the split entry points
