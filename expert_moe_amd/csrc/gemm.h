@@ -88,6 +88,26 @@ __device__ __forceinline__ int gemm_src_row(const GemmArgs& a, int r) {
   return r < a.M_rows ? r : a.M_rows - 1;
 }
 
+// Source rows of N tile rows (each below the device row count) at once: the N pair-list
+// loads are all issued before any is used, one memory round trip instead of N, and the
+// padding / range rule is applied without branches.
+template <int N>
+__device__ __forceinline__ void gemm_src_rows(const GemmArgs& a, const int (&r)[N], int (&src)[N]) {
+  if (a.row_map) {
+    int p[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) p[j] = a.row_map[r[j]];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int q = p[j] < 0 || p[j] >= a.M_pairs ? 0 : p[j];
+      src[j] = static_cast<int>(static_cast<uint32_t>(q) / static_cast<uint32_t>(a.row_div));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) src[j] = min(r[j], a.M_rows - 1);
+  }
+}
+
 __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
   return a.num_padded ? *a.num_padded : a.M_rows;
 }
@@ -149,12 +169,17 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   // bases: an expert's weights and the activations are each far below 4 GiB.
   const int lrow = lane >> 3;
   uint32_t goff[ND];
+  {
+    int rows[NA], src[NA];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int blk = wave + 4 * j;
-    const int r = 8 * blk + lrow;
-    const int c = (lane & 7) ^ lrow ^ (blk & 1);
-    goff[j] = static_cast<uint32_t>(gemm_src_row(a, m0 + r)) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
+    for (int j = 0; j < NA; ++j) rows[j] = m0 + 8 * (wave + 4 * j) + lrow;
+    gemm_src_rows(a, rows, src);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int blk = wave + 4 * j;
+      const int c = (lane & 7) ^ lrow ^ (blk & 1);
+      goff[j] = static_cast<uint32_t>(src[j]) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
+    }
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -395,9 +420,14 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
   k_range(a, k0, klen);
 
   const uint16_t* pa[MB];
+  {
+    int rows[MB], src[MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
-    pa[i] = A + static_cast<int64_t>(gemm_src_row(a, m0 + 16 * i + q)) * K + k0 + kq;
+    for (int i = 0; i < MB; ++i) rows[i] = m0 + 16 * i + q;
+    gemm_src_rows(a, rows, src);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) pa[i] = A + static_cast<int64_t>(src[i]) * K + k0 + kq;
+  }
   const uint16_t* pb[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
