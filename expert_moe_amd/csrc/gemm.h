@@ -115,8 +115,9 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
 // ----------------------------------------------------------------------------------------
 // Large-M tile fed by global->LDS loads (gfx950 global_load_lds_dwordx4): each lane's 16 bytes
 // go straight from memory into LDS without passing through registers, so the waves issue
-// only the loads, the LDS fragment reads and the MFMAs. 4 waves, K step BK = 64, two LDS
-// stages (separate arrays, addressed statically).
+// only the loads, the LDS fragment reads and the MFMAs. 4 or 8 waves (with 8, two per SIMD:
+// one wave's waits are covered by the other's MFMAs), K step BK = 64, two LDS stages
+// (separate arrays, addressed statically).
 //
 // Schedule of K step t (stage S = t % 2, the other stage S' holds step t + 1, in flight):
 //   slice 0..2 : read the fragments of slice s+1 from S, then the MFMAs of slice s
@@ -132,17 +133,18 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
 // byte 16 l): lane l loads row 8 j + l / 8, logical chunk (l % 8) ^ sw(row).
 // ----------------------------------------------------------------------------------------
 template <int BM, int BNR, int WM, int WN, int MODE>
-__global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
+__global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
+  constexpr int NW = WM * WN;              // waves (4, or 8 = two per SIMD)
   constexpr int BK = 64;
   constexpr int ROWB = 128;                // bytes of one LDS row
   constexpr int TM = BM / WM;
   constexpr int TMB = TM / 32;
   constexpr int TNR = BNR / WN;
   constexpr int TNB = TNR / 32;
-  constexpr int NA = BM / 32;              // A load instructions per wave per K step
-  constexpr int NB = BNR / 32;             // B load instructions per wave per K step
+  constexpr int NA = BM / (8 * NW);        // A load instructions per wave per K step
+  constexpr int NB = BNR / (8 * NW);       // B load instructions per wave per K step
   constexpr int ND = NA + NB;
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TMB >= 1 && TNB >= 1 && NA >= 1 && NB >= 1, "tile too small");
   static_assert(MODE != kSiluMul || (TNB % 2 == 0), "gate/up pairs");
 
@@ -164,7 +166,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   int k0, klen;
   k_range(a, k0, klen);
 
-  // Load sources: instruction d < NA of this wave fills A rows 8 (wave + 4 d) .. +7, the
+  // Load sources: instruction d < NA of this wave fills A rows 8 (wave + NW d) .. +7, the
   // others B rows likewise. Kept as 32-bit byte offsets from the (wave-uniform) operand
   // bases: an expert's weights and the activations are each far below 4 GiB.
   const int lrow = lane >> 3;
@@ -172,18 +174,18 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   {
     int rows[NA], src[NA];
 #pragma unroll
-    for (int j = 0; j < NA; ++j) rows[j] = m0 + 8 * (wave + 4 * j) + lrow;
+    for (int j = 0; j < NA; ++j) rows[j] = m0 + 8 * (wave + NW * j) + lrow;
     gemm_src_rows(a, rows, src);
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-      const int blk = wave + 4 * j;
+      const int blk = wave + NW * j;
       const int c = (lane & 7) ^ lrow ^ (blk & 1);
       goff[j] = static_cast<uint32_t>(src[j]) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
     }
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int blk = wave + 4 * j;
+    const int blk = wave + NW * j;
     const int r = 8 * blk + lrow;
     const int c = (lane & 7) ^ lrow ^ (blk & 1);
     int brow;
@@ -201,9 +203,9 @@ __global__ void __launch_bounds__(256) gemm_bf16_dma(GemmArgs a) {
   auto dma = [&](int d, int kt, int st) {
     const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
     if (d < NA)
-      dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + 4 * d) * 1024));
+      dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
     else
-      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + 4 * (d - NA)) * 1024));
+      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024));
   };
 
   const int wm = wave % WM;

@@ -15,7 +15,7 @@ namespace {
 template <int BM, int BNR, int WM, int WN, int MODE>
 void launch_tile(GemmArgs a, int n_rows_b, hipStream_t s) {
   a.n_tiles = n_rows_b / BNR;
-  gemm_bf16_dma<BM, BNR, WM, WN, MODE><<<tile_grid(a.m_blocks, a.n_tiles), 256, 0, s>>>(a);
+  gemm_bf16_dma<BM, BNR, WM, WN, MODE><<<tile_grid(a.m_blocks, a.n_tiles), 64 * WM * WN, 0, s>>>(a);
 }
 
 // Weight-row tile (BNR) for a launch: the widest of 256 / 128 / 64 that divides n_rows_b and
@@ -28,22 +28,24 @@ inline int pick_bnr(int n_rows_b, int est_blocks, bool silu) {
   return 64;
 }
 
+// Wave grids: 8 waves (two per SIMD) wherever the tile splits into 8 blocks of whole MFMA
+// tiles with gate/up pairs; measured faster than 4 on the 256-row tiles.
 template <int MODE>
 void launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
   if (bnr == 256)
-    launch_tile<256, 256, 2, 2, MODE>(a, n_rows_b, s);
+    launch_tile<256, 256, 2, 4, MODE>(a, n_rows_b, s);
   else if (bnr == 128)
-    launch_tile<256, 128, 2, 2, MODE>(a, n_rows_b, s);
+    launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, s);
   else
-    launch_tile<256, 64, 4, 1, MODE>(a, n_rows_b, s);
+    launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, s);
 }
 
 template <int MODE>
 void launch_tile128(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
   if (bnr == 256)
-    launch_tile<128, 256, 2, 2, MODE>(a, n_rows_b, s);
+    launch_tile<128, 256, 2, 4, MODE>(a, n_rows_b, s);
   else if (bnr == 128)
-    launch_tile<128, 128, 2, 2, MODE>(a, n_rows_b, s);
+    launch_tile<128, 128, 4, 2, MODE>(a, n_rows_b, s);
   else
     launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, s);
 }
