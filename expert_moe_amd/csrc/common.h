@@ -68,8 +68,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);  // vmcnt(0)
-constexpr int kWaitVmLgkm0 = 0x7 << 4;              // vmcnt(0) lgkmcnt(0)
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }  // vmcnt(n)
+constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }  // + lgkmcnt(0)
+constexpr int kWaitVm0 = wait_vm(0);
+constexpr int kWaitVmLgkm0 = wait_vm_lgkm0(0);
+
+// Workgroup barrier without the release fence of __syncthreads (which would also wait for
+// every outstanding global->LDS load); callers wait explicitly for what must have landed.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
 
 // Plain 16-byte global load.
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }

@@ -28,6 +28,9 @@ struct GemmArgs {
                                // identity rows past it read the last row
   const int32_t* num_padded;   // device count of rows in use, or NULL (= M_rows)
   const int32_t* block_expert; // sorted rows: slot of each block of block_m rows (NULL = slot 0)
+  const int32_t* valid_map;    // LDS tile: sorted pair list whose -1 entries mark padding rows
+                               // (padding ends each expert's segment); row groups of a tile that
+                               // hold only padding skip their MFMAs. NULL: rows below M_rows are real
   int32_t block_m;             // padding granule of the sorted rows (a multiple of the tile rows)
   const void* B;               // weights of slot s at B + s * b_stride elements, [rows, K]
   int64_t b_stride;
@@ -41,6 +44,10 @@ struct GemmArgs {
   int32_t k_splits;            // kStoreF32 only: blockIdx.y takes K range y*K/k_splits.. and
                                // writes its partial sums to C + y * c_split_stride (0 or 1 = no split)
   int64_t c_split_stride;
+  int32_t tail_mode;           // LDS tile only. 0: every active tile; 1: every active tile but the
+                               // tail (tail_tiles); 2: the quarter tiles (half BM, half BNR) of the
+                               // tail of the tiling with twice this kernel's BM and BNR
+  int32_t n_cu;                // tiles per round (one workgroup per CU) for the tail rule
 };
 
 // K range [k0, k0 + klen) of this workgroup (blockIdx.y selects the split).
@@ -59,20 +66,41 @@ constexpr int kGroupN = 4;
 // into kXcds contiguous runs, one per XCD, so that workgroups on one XCD share operands in
 // its L2. Inside a run, tiles go row-block-major within groups of kGroupN N tiles: the row
 // blocks of one expert that read the same weight tile are consecutive and run together.
-// Returns false for workgroups that have no tile (the grid is sized for the worst case).
-__device__ __forceinline__ bool tile_of_block(int bid, int active_m, int n_tiles, int& mb, int& nt) {
-  const int total = active_m * n_tiles;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int slot = bid / kXcds;
-  if (slot >= per_xcd) return false;
-  const int L = (bid % kXcds) * per_xcd + slot;
-  if (L >= total) return false;
+//
+// Linear tile L -> (row block, N tile).
+__device__ __forceinline__ void tile_coords(int L, int active_m, int n_tiles, int& mb, int& nt) {
   const int ng = L / (active_m * kGroupN);
   const int rem = L - ng * active_m * kGroupN;
   const int width = min(kGroupN, n_tiles - ng * kGroupN);
   mb = rem / width;
   nt = ng * kGroupN + rem % width;
+}
+
+// Workgroup bid -> linear tile of the first `count`, striped over the XCDs; false for
+// workgroups that have no tile (the grid is sized for the worst case).
+__device__ __forceinline__ bool xcd_tile(int bid, int count, int& L) {
+  const int per_xcd = (count + kXcds - 1) / kXcds;
+  const int slot = bid / kXcds;
+  if (slot >= per_xcd) return false;
+  L = (bid % kXcds) * per_xcd + slot;
+  return L < count;
+}
+
+__device__ __forceinline__ bool tile_of_block(int bid, int active_m, int n_tiles, int& mb, int& nt) {
+  int L;
+  if (!xcd_tile(bid, active_m * n_tiles, L)) return false;
+  tile_coords(L, active_m, n_tiles, mb, nt);
   return true;
+}
+
+// Tail balancing. With one workgroup per CU, `total` tiles run in rounds of n_cu; a last
+// partial round of rem tiles takes as long as a full one. When four quarter tiles (half the
+// rows, half the weight rows) per tail tile still fit one round, a second launch of the
+// quarter-tile kernel takes the last rem tiles of the order: no reduction is involved, each
+// output element still has one writer and one K loop.
+__device__ __forceinline__ int tail_tiles(int total, int n_cu) {
+  const int rem = n_cu > 0 ? total % n_cu : 0;
+  return 4 * rem <= n_cu ? rem : 0;
 }
 
 // Grid size for the tile order above.
@@ -112,6 +140,32 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
   return a.num_padded ? *a.num_padded : a.M_rows;
 }
 
+// Tile of this workgroup for a BM-row LDS tile kernel under a.tail_mode.
+template <int BM>
+__device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int& mb, int& nt) {
+  const int rows = gemm_rows_active(a);
+  if (a.tail_mode == 2) {
+    const int am = (rows + 2 * BM - 1) / (2 * BM);
+    const int nb = a.n_tiles / 2;
+    const int total = am * nb;
+    const int rem = tail_tiles(total, a.n_cu);
+    const int u = static_cast<int>(blockIdx.x);
+    if (u >= 4 * rem) return false;
+    int MB, NT;
+    tile_coords(total - rem + u / 4, am, nb, MB, NT);
+    mb = 2 * MB + ((u >> 1) & 1);
+    nt = 2 * NT + (u & 1);
+    return true;
+  }
+  const int am = (rows + BM - 1) / BM;
+  const int total = am * a.n_tiles;
+  const int count = a.tail_mode == 1 ? total - tail_tiles(total, a.n_cu) : total;
+  int L;
+  if (!xcd_tile(static_cast<int>(blockIdx.x), count, L)) return false;
+  tile_coords(L, am, a.n_tiles, mb, nt);
+  return true;
+}
+
 // ----------------------------------------------------------------------------------------
 // Large-M tile fed by global->LDS loads (gfx950 global_load_lds_dwordx4): each lane's 16 bytes
 // go straight from memory into LDS without passing through registers, so the waves issue
@@ -132,7 +186,7 @@ __device__ __forceinline__ int gemm_rows_active(const GemmArgs& a) {
 // 16 consecutive rows hit distinct banks. One load instruction fills 8 rows (1 KiB, lane l at
 // byte 16 l): lane l loads row 8 j + l / 8, logical chunk (l % 8) ^ sw(row).
 // ----------------------------------------------------------------------------------------
-template <int BM, int BNR, int WM, int WN, int MODE>
+template <int BM, int BNR, int WM, int WN, int MODE, int NS = 2>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   constexpr int NW = WM * WN;              // waves (4, or 8 = two per SIMD)
   constexpr int BK = 64;
@@ -147,17 +201,16 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TMB >= 1 && TNB >= 1 && NA >= 1 && NB >= 1, "tile too small");
   static_assert(MODE != kSiluMul || (TNB % 2 == 0), "gate/up pairs");
+  static_assert(NS == 2 || NS == 3, "two or three LDS stages");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * ROWB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BNR * ROWB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * ROWB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BNR * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[NS][BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[NS][BNR * ROWB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int mb, nt;
-  if (!tile_of_block(blockIdx.x, (gemm_rows_active(a) + BM - 1) / BM, a.n_tiles, mb, nt)) return;
+  if (!gemm_tile<BM>(a, mb, nt)) return;
   const int m0 = mb * BM;
   const int slot = a.block_expert ? a.block_expert[m0 / a.block_m] : 0;
   const char* const Abase = static_cast<const char*>(a.A);
@@ -197,8 +250,26 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
     }
     goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
   }
-  const uint32_t lA[2] = {lds_addr(sA0), lds_addr(sA1)};
-  const uint32_t lB[2] = {lds_addr(sB0), lds_addr(sB1)};
+  // Real rows of the tile (a prefix: padding ends each expert's segment). Every tile row is
+  // one of this lane group's DMA rows; lanes with (lane & 7) == 0 count each row once.
+  __shared__ int real_rows[NW];
+  if (a.valid_map) {
+    int rows[NA], pv[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) rows[j] = m0 + 8 * (wave + NW * j) + lrow;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) pv[j] = a.valid_map[rows[j]];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) cnt += __popcll(__ballot((lane & 7) == 0 && pv[j] >= 0));
+    if (lane == 0) real_rows[wave] = cnt;
+  }
+  uint32_t lA[NS], lB[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    lA[st] = lds_addr(sA[st]);
+    lB[st] = lds_addr(sB[st]);
+  }
   // load instruction d of K step kt into stage st
   auto dma = [&](int d, int kt, int st) {
     const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
@@ -208,8 +279,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
       dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024));
   };
 
-  const int wm = wave % WM;
-  const int wn = wave / WM;
+  // wave -> (row group, weight-row group); SIMD s runs waves s and s + 4, which get different
+  // row groups, so a tile whose last rows are padding still keeps every SIMD half busy
+  const int wm = wave / WN;
+  const int wn = wave % WN;
   const int fr = lane & 31;
   // swizzle of the fragment rows (their tile row is a multiple of 32 plus fr)
   const int sw = (fr & 7) ^ ((fr >> 3) & 1);
@@ -236,26 +309,31 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bf16x8 fa[2][TMB], fb[2][TNB];  // fragments of two K slices
-  auto frags = [&](const uint8_t* sA, const uint8_t* sB, int ks, int set) {
+  int nact = TMB;                  // MFMA row blocks of this wave with real rows
+  auto frags = [&](const uint8_t* pA, const uint8_t* pB, int ks, int set) {
 #pragma unroll
-    for (int i = 0; i < TMB; ++i) fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sA + arow[i] + coff[ks]));
+    for (int i = 0; i < TMB; ++i) fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(pA + arow[i] + coff[ks]));
 #pragma unroll
-    for (int j = 0; j < TNB; ++j) fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sB + brow0[j] + coff[ks]));
+    for (int j = 0; j < TNB; ++j) fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(pB + brow0[j] + coff[ks]));
   };
-  // MFMAs of one K slice. DM = 0: nothing else; DM = 1 + st: the ND loads of K step kt_dma
-  // into stage st go between them.
-  auto mfmas = [&](int set, auto dm_c, int kt_dma) {
+  // MFMAs of one K slice. DM = 0: nothing else; DM = 1 + st: loads D0 .. D1-1 of K step
+  // kt_dma into stage st go between them.
+  auto mfmas = [&](int set, auto dm_c, int kt_dma, auto d0_c, auto d1_c) {
     constexpr int DM = decltype(dm_c)::value;
+    constexpr int D0 = decltype(d0_c)::value;
+    constexpr int D1 = decltype(d1_c)::value;
     constexpr int NM = TMB * TNB;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      // weight fragment first: acc holds the transposed block (see the epilogue)
-      acc[m / TNB][m % TNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][m % TNB], fa[set][m / TNB],
-                                                                      acc[m / TNB][m % TNB], 0, 0, 0);
+      // weight fragment first: acc holds the transposed block (see the epilogue); row blocks
+      // of padding only are skipped (their accumulators stay 0)
+      if (m / TNB < nact)
+        acc[m / TNB][m % TNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][m % TNB], fa[set][m / TNB],
+                                                                        acc[m / TNB][m % TNB], 0, 0, 0);
       if constexpr (DM != 0) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int d = m * ND / NM; d < (m + 1) * ND / NM; ++d) dma(d, kt_dma, DM - 1);
+        for (int d = D0 + m * (D1 - D0) / NM; d < D0 + (m + 1) * (D1 - D0) / NM; ++d) dma(d, kt_dma, DM - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -263,69 +341,122 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
-  // K step kt on stage ST. KIND 0: step kt+1 is in flight and step kt+2 gets loaded into
-  // this stage; 1: step kt+1 is in flight and is the last; 2: kt is the last step.
+  using CND = std::integral_constant<int, ND>;
+  // Loads of K step kt+2 and where they go. Two stages: into this step's stage, after the
+  // sync point, all during slice 3. Three stages: into the stage of step kt-1 (free since the
+  // sync point of step kt-1), spread over slices 0..2 of this step, so they have two steps to
+  // land; the sync point then waits for step kt+1 only (vmcnt(ND)).
+  // K step kt on stage ST. KIND 0: step kt+2 gets loaded; 1: step kt+1 is the last;
+  // 2: kt is the last step.
   auto step = [&](auto st_c, auto kind_c, int kt) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int KIND = decltype(kind_c)::value;
-    const uint8_t* sA = ST ? sA1 : sA0;
-    const uint8_t* sB = ST ? sB1 : sB0;
+    constexpr int NX = (ST + 1) % NS;                    // stage of step kt+1
+    constexpr int NL = NS == 3 ? (ST + 2) % NS : ST;     // stage that receives step kt+2
+    using L3 = std::integral_constant<int, (NS == 3 && KIND == 0) ? 1 + NL : 0>;
+    using T1 = std::integral_constant<int, ND / 3>;
+    using T2 = std::integral_constant<int, 2 * ND / 3>;
     __builtin_amdgcn_sched_barrier(0);
-    frags(sA, sB, 1, 1);
+    frags(sA[ST], sB[ST], 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(0, C0{}, 0);
+    mfmas(0, L3{}, kt + 2, C0{}, T1{});
     __builtin_amdgcn_sched_barrier(0);
-    frags(sA, sB, 2, 0);
+    frags(sA[ST], sB[ST], 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(1, C0{}, 0);
+    mfmas(1, L3{}, kt + 2, T1{}, T2{});
     __builtin_amdgcn_sched_barrier(0);
-    frags(sA, sB, 3, 1);
+    frags(sA[ST], sB[ST], 3, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(0, C0{}, 0);
+    mfmas(0, L3{}, kt + 2, T2{}, CND{});
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KIND < 2) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
-      __syncthreads();
-      frags(ST ? sA0 : sA1, ST ? sB0 : sB1, 0, 0);
+      if constexpr (NS == 2) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_s_waitcnt(KIND == 0 ? wait_vm_lgkm0(ND) : kWaitVmLgkm0);
+        wg_barrier();
+      }
+      frags(sA[NX], sB[NX], 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (KIND == 0)
-        mfmas(1, std::integral_constant<int, 1 + ST>{}, kt + 2);
+      if constexpr (NS == 2 && KIND == 0)
+        mfmas(1, std::integral_constant<int, 1 + NL>{}, kt + 2, C0{}, CND{});
       else
-        mfmas(1, C0{}, 0);
+        mfmas(1, C0{}, 0, C0{}, C0{});
     } else {
-      mfmas(1, C0{}, 0);
+      mfmas(1, C0{}, 0, C0{}, C0{});
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Prologue: step 0 landed in stage 0, step 1 in flight into stage 1, slice 0 read.
+  // Prologue: steps 0 and 1 in flight into stages 0 and 1, wait for step 0, slice 0 read.
   const int nk = klen / BK;
 #pragma unroll
   for (int d = 0; d < ND; ++d) dma(d, 0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
   if (nk > 1) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) dma(d, 1, 1);
-  }
-  frags(sA0, sB0, 0, 0);
-  if (nk == 1) {
-    step(C0{}, C2{}, 0);
-  } else if ((nk & 1) == 0) {
-    for (int kt = 0; kt < nk - 2; kt += 2) {
-      step(C0{}, C0{}, kt);
-      step(C1{}, C0{}, kt + 1);
-    }
-    step(C0{}, C1{}, nk - 2);
-    step(C1{}, C2{}, nk - 1);
+    __builtin_amdgcn_s_waitcnt(wait_vm(ND));
   } else {
-    for (int kt = 0; kt < nk - 3; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
+  __syncthreads();
+  {
+    int nreal = a.M_rows - m0;
+    if (a.valid_map) {
+      nreal = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) nreal += real_rows[w];
+    }
+    // MFMA row blocks of this wave that hold at least one real row
+    nact = __builtin_amdgcn_readfirstlane(min(TMB, max(0, (nreal - wm * TM + 31) / 32)));
+  }
+  frags(sA[0], sB[0], 0, 0);
+  if constexpr (NS == 2) {
+    if (nk == 1) {
+      step(C0{}, C2{}, 0);
+    } else if ((nk & 1) == 0) {
+      for (int kt = 0; kt < nk - 2; kt += 2) {
+        step(C0{}, C0{}, kt);
+        step(C1{}, C0{}, kt + 1);
+      }
+      step(C0{}, C1{}, nk - 2);
+      step(C1{}, C2{}, nk - 1);
+    } else {
+      for (int kt = 0; kt < nk - 3; kt += 2) {
+        step(C0{}, C0{}, kt);
+        step(C1{}, C0{}, kt + 1);
+      }
+      step(C0{}, C0{}, nk - 3);
+      step(C1{}, C1{}, nk - 2);
+      step(C0{}, C2{}, nk - 1);
+    }
+  } else {
+    // groups of three loading steps, then a static tail of 2..4 steps (stage of kt: kt % 3)
+    int kt = 0;
+    if (nk >= 2) {
+      for (; kt + 5 <= nk; kt += 3) {
+        step(C0{}, C0{}, kt);
+        step(C1{}, C0{}, kt + 1);
+        step(C2{}, C0{}, kt + 2);
+      }
+    }
+    const int r = nk - kt;
+    if (nk == 1) {
+      step(C0{}, C2{}, 0);
+    } else if (r == 2) {
+      step(C0{}, C1{}, kt);
+      step(C1{}, C2{}, kt + 1);
+    } else if (r == 3) {
+      step(C0{}, C0{}, kt);
+      step(C1{}, C1{}, kt + 1);
+      step(C2{}, C2{}, kt + 2);
+    } else {
       step(C0{}, C0{}, kt);
       step(C1{}, C0{}, kt + 1);
+      step(C2{}, C1{}, kt + 2);
+      step(C0{}, C2{}, kt + 3);
     }
-    step(C0{}, C0{}, nk - 3);
-    step(C1{}, C1{}, nk - 2);
-    step(C0{}, C2{}, nk - 1);
   }
 
   // Epilogue. The MFMAs take the weight fragment as first operand, so acc[i][j] is the

@@ -12,10 +12,59 @@ namespace moe {
 
 namespace {
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <int BM, int BNR, int WM, int WN, int MODE>
+void launch_tile_only(GemmArgs a, int n_rows_b, int tail_mode, hipStream_t s) {
+  a.n_tiles = n_rows_b / BNR;
+  a.tail_mode = tail_mode;
+  a.n_cu = cu_count();
+  const int grid = tail_mode == 2 ? (a.n_cu + kXcds - 1) / kXcds * kXcds : tile_grid(a.m_blocks, a.n_tiles);
+  // Three LDS stages (loads two K steps ahead) wherever they fit in the CU's 160 KB.
+  constexpr size_t kLdsCu = 160 * 1024;
+  constexpr size_t kStage = static_cast<size_t>(BM + BNR) * 128;
+  constexpr int NS = 3 * kStage <= kLdsCu ? 3 : 2;
+  // The quarter tiles of a tail are at most one per CU: reserve more than half of the CU's LDS
+  // (unused) so that the dispatcher cannot stack two on one CU while others stay idle.
+  constexpr size_t kStatic = NS * kStage;
+  const size_t dyn = tail_mode == 2 && kStatic <= kLdsCu / 2 ? kLdsCu / 2 + 1024 - kStatic : 0;
+  gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS><<<grid, 64 * WM * WN, dyn, s>>>(a);
+}
+
+// Quarter tile (half BM, half BNR) and its wave grid for the tail launch; BM2 = 0: none.
+template <int BM, int BNR, int MODE> struct Quarter { static constexpr int BM2 = 0, WM = 0, WN = 0; };
+template <int MODE> struct Quarter<256, 256, MODE> { static constexpr int BM2 = 128, WM = 4, WN = 2; };
+template <int MODE> struct Quarter<128, 256, MODE> { static constexpr int BM2 = 64, WM = 2, WN = 2; };
+template <int MODE> struct Quarter<256, 128, MODE> { static constexpr int BM2 = 128, WM = 4, WN = 1; };
+template <> struct Quarter<128, 128, kStore> { static constexpr int BM2 = 64, WM = 2, WN = 2; };
+
+// A tile launch; when the shape has a quarter tile, the full-size launch leaves the tail of
+// its last round (decided on the device from the row count) to a quarter-tile launch.
 template <int BM, int BNR, int WM, int WN, int MODE>
 void launch_tile(GemmArgs a, int n_rows_b, hipStream_t s) {
-  a.n_tiles = n_rows_b / BNR;
-  gemm_bf16_dma<BM, BNR, WM, WN, MODE><<<tile_grid(a.m_blocks, a.n_tiles), 64 * WM * WN, 0, s>>>(a);
+  using Q = Quarter<BM, BNR, MODE>;
+  if constexpr (Q::BM2 == 0) {
+    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, 0, s);
+  } else {
+    if (cu_count() <= 0) {
+      launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, 0, s);
+      return;
+    }
+    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, 1, s);
+    a.m_blocks = 0;  // unused in tail mode 2
+    launch_tile_only<Q::BM2, BNR / 2, Q::WM, Q::WN, MODE>(a, n_rows_b, 2, s);
+  }
 }
 
 // Weight-row tile (BNR) for a launch: the widest of 256 / 128 / 64 that divides n_rows_b and
@@ -137,6 +186,7 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
   GemmArgs g = base_args(p, T, num_padded, block_expert, block_m, rows);
   g.A = x;
   g.row_map = row_map;
+  g.valid_map = row_map;
   g.B = w13;
   g.b_stride = static_cast<int64_t>(2) * I * H;
   g.K = H;
@@ -164,14 +214,15 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
 }
 
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
-                const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
-                void* y, hipStream_t s) {
+                const int32_t* sorted_pairs, const int32_t* num_padded,
+                const int32_t* block_expert, int block_m, int rows, void* y, hipStream_t s) {
   const int H = p.hidden_size;
   const int I = inter;
   // y[r, :] = act[r] W2^T, B = w2 [H, I] per slot; act rows are already in order.
   GemmArgs g = base_args(p, T, num_padded, block_expert, block_m, rows);
   g.A = act;
   g.row_map = nullptr;
+  g.valid_map = sorted_pairs;
   g.B = w2;
   g.b_stride = static_cast<int64_t>(H) * I;
   g.K = I;
@@ -205,7 +256,7 @@ int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const
   int rc = launch_gate_up(p, T, x, w13, inter, row_map, num_padded, block_expert, block_m, rows,
                           act, s);
   if (rc) return rc;
-  return launch_down(p, T, act, w2, inter, num_padded, block_expert, block_m, rows, y, s);
+  return launch_down(p, T, act, w2, inter, row_map, num_padded, block_expert, block_m, rows, y, s);
 }
 
 }  // namespace moe

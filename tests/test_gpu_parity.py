@@ -222,3 +222,64 @@ def test_external_routing_through_align():
     torch.cuda.synchronize()
     want = layer.oracle_out(np.arange(T), r["ids"], r["weights"])
     assert rel_err(out.float().cpu().numpy(), want) <= OUT_TOL["bf16"]
+
+
+# Routings whose tile counts leave a short last round (at most a quarter of the CUs' worth of
+# tiles), so the expert GEMMs hand the tail to the quarter-tile launch. (H, I, top_k, rows per
+# local expert, block_m) and the tiles expected on a 256-CU MI355X:
+TAIL = {
+    # gate/up 256x256 tiles: 9 row blocks x 64 -> 576 tiles, 64 in the tail
+    "gu_256x256": (256, 8192, 2, (513, 512, 512, 257), 256),
+    # gate/up 128x256 tiles: 17 row blocks x 64 -> 1088 tiles, 64 in the tail
+    "gu_128x256": (256, 8192, 2, (513, 513, 512, 258), 128),
+    # gate/up 256x128 tiles: 17 row blocks x 32 -> 544 tiles, 32 in the tail
+    "gu_256x128": (256, 2048, 1, (1025, 1024, 1024, 1024), 256),
+    # down 256x256 tiles: 17 x 32 -> 544, 32 in the tail
+    "dn_256x256": (8192, 256, 1, (1025, 1024, 1024, 1024), 256),
+    # down 128x256 tiles: 33 x 32 -> 1056, 32 in the tail
+    "dn_128x256": (8192, 256, 1, (1025, 1024, 1024, 1024), 128),
+    # down 256x128 tiles (H = 33 x 128): 17 x 33 -> 561, 49 in the tail
+    "dn_256x128": (4224, 256, 1, (1025, 1024, 1024, 1024), 256),
+    # down 128x128 tiles: 32 x 33 -> 1056, 32 in the tail
+    "dn_128x128": (4224, 256, 1, (1025, 1024, 1024, 896), 128),
+}
+
+
+@pytest.mark.parametrize("case", sorted(TAIL))
+def test_tail_tiles(case):
+    """Expert GEMMs whose last round is split into quarter tiles: every output row vs the oracle."""
+    H, I, k, counts, bm = TAIL[case]
+    E = len(counts)
+    T = sum(counts) // k
+    w = W(f"tail_{case}", 30 + sorted(TAIL).index(case), "tail tiles", "bf16", (T,), H, E, I, k,
+          True)
+    layer = Layer(w, T)
+    p = params(w)
+    d = layer.d
+    dev = d["x"].device
+    # external routing with exactly `counts` pairs per expert, distinct experts per token
+    flat = np.repeat(np.arange(E, dtype=np.int32), counts)
+    ids = np.stack([flat[j * T:(j + 1) * T] for j in range(k)], axis=1)
+    assert all(len(set(r)) == k for r in ids.tolist())
+    rng = np.random.default_rng(7)
+    tw_h = rng.uniform(0.25, 1.0, size=(T, k)).astype(np.float32)
+    local = dev_tensor(ids)
+    tw = dev_tensor(tw_h)
+    ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
+    cap = moe.moe_sorted_capacity(p, T, bm)
+    sp = torch.empty(cap, dtype=torch.int32, device=dev)
+    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
+    y = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+    moe.moe_grouped_mlp(p, T, d["x"], d["w13"], d["w2"], sp, be, npad, bm, y, ws)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    moe.moe_combine(p, T, y, pr, tw, None, out)
+    torch.cuda.synchronize()
+    blocks = sum((c + bm - 1) // bm for c in counts)
+    assert int(npad.item()) == blocks * bm
+    want = layer.oracle_out(np.arange(T), ids, tw_h)
+    err = rel_err(out.float().cpu().numpy(), want)
+    print(f"[{case}] T={T} row_blocks={blocks} rel_err={err:.3e}", flush=True)
+    assert err <= OUT_TOL["bf16"], err
