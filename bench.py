@@ -137,7 +137,7 @@ class Bench:
         rec(2)
         m.moe_expert_gate_up(p, T, d["x"], d["w13"], self.sp, self.be, self.npad, self.bm, self.act)
         rec(3)
-        m.moe_expert_down(p, T, self.act, d["w2"], self.sp, self.be, self.npad, self.bm, self.y)
+        m.moe_expert_down(p, T, self.act, d["w2"], self.be, self.npad, self.bm, self.y)
         rec(4)
         if self.sy is not None:
             m.moe_shared_mlp(p, T, d["x"], d["sw13"], d["sw2"], self.sy, self.sws)

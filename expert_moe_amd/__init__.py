@@ -83,7 +83,7 @@ _SIGS = {
     "moe_grouped_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                         ctypes.c_int),
     "moe_expert_gate_up": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
-    "moe_expert_down": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
+    "moe_expert_down": ([_P, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "moe_shared_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_combine": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_forward": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -206,11 +206,10 @@ def moe_expert_gate_up(p, num_tokens, x, w13, sorted_pairs, block_expert, num_pa
                                     block_m, _ptr(act), _stream(stream)), "moe_expert_gate_up")
 
 
-def moe_expert_down(p, num_tokens, act, w2, sorted_pairs, block_expert, num_padded, block_m, y,
-                    stream=None):
+def moe_expert_down(p, num_tokens, act, w2, block_expert, num_padded, block_m, y, stream=None):
     _check(lib().moe_expert_down(ctypes.byref(p), num_tokens, _ptr(act), _ptr(w2),
-                                 _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
-                                 block_m, _ptr(y), _stream(stream)), "moe_expert_down")
+                                 _ptr(block_expert), _ptr(num_padded), block_m, _ptr(y),
+                                 _stream(stream)), "moe_expert_down")
 
 
 def moe_shared_mlp(p, num_tokens, x, shared_w13, shared_w2, shared_y, ws, stream=None):

@@ -270,8 +270,8 @@ int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, c
 }
 
 int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, const void* w2,
-                    const int32_t* sorted_pairs, const int32_t* block_expert,
-                    const int32_t* num_padded, int32_t block_m, void* y, void* stream) {
+                    const int32_t* block_expert, const int32_t* num_padded, int32_t block_m,
+                    void* y, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
@@ -281,8 +281,7 @@ int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, co
   if (!aligned16({act, w2, y})) return MOE_EINVAL;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_down(*p, static_cast<int>(num_tokens), act, w2, p->intermediate_size,
-                          sorted_pairs, num_padded, block_expert, block_m, rows, y,
-                          as_stream(stream));
+                          nullptr, num_padded, block_expert, block_m, rows, y, as_stream(stream));
 }
 
 int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,

@@ -28,9 +28,8 @@ struct GemmArgs {
                                // identity rows past it read the last row
   const int32_t* num_padded;   // device count of rows in use, or NULL (= M_rows)
   const int32_t* block_expert; // sorted rows: slot of each block of block_m rows (NULL = slot 0)
-  const int32_t* valid_map;    // LDS tile: sorted pair list whose -1 entries mark padding rows
-                               // (padding ends each expert's segment); row groups of a tile that
-                               // hold only padding skip their MFMAs. NULL: rows below M_rows are real
+  const int32_t* valid_map;    // LDS tile with SKIP: the sorted pair list, whose -1 entries mark
+                               // padding rows (padding ends each expert's segment)
   int32_t block_m;             // padding granule of the sorted rows (a multiple of the tile rows)
   const void* B;               // weights of slot s at B + s * b_stride elements, [rows, K]
   int64_t b_stride;
@@ -186,7 +185,7 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int& mb, int& nt) {
 // 16 consecutive rows hit distinct banks. One load instruction fills 8 rows (1 KiB, lane l at
 // byte 16 l): lane l loads row 8 j + l / 8, logical chunk (l % 8) ^ sw(row).
 // ----------------------------------------------------------------------------------------
-template <int BM, int BNR, int WM, int WN, int MODE, int NS = 2>
+template <int BM, int BNR, int WM, int WN, int MODE, int NS = 2, bool SKIP = false>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   constexpr int NW = WM * WN;              // waves (4, or 8 = two per SIMD)
   constexpr int BK = 64;
@@ -250,10 +249,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
     }
     goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
   }
-  // Real rows of the tile (a prefix: padding ends each expert's segment). Every tile row is
-  // one of this lane group's DMA rows; lanes with (lane & 7) == 0 count each row once.
-  __shared__ int real_rows[NW];
-  if (a.valid_map) {
+  // SKIP: real rows of the tile (a prefix, since padding ends each expert's segment). Every
+  // tile row is one of this lane group's DMA rows; lanes with (lane & 7) == 0 count each once.
+  __shared__ int real_rows[SKIP ? NW : 1];
+  if constexpr (SKIP) {
     int rows[NA], pv[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) rows[j] = m0 + 8 * (wave + NW * j) + lrow;
@@ -279,8 +278,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
       dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024));
   };
 
-  // wave -> (row group, weight-row group); SIMD s runs waves s and s + 4, which get different
-  // row groups, so a tile whose last rows are padding still keeps every SIMD half busy
+  // wave -> (row group, weight-row group)
   const int wm = wave / WN;
   const int wn = wave % WN;
   const int fr = lane & 31;
@@ -309,7 +307,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bf16x8 fa[2][TMB], fb[2][TNB];  // fragments of two K slices
-  int nact = TMB;                  // MFMA row blocks of this wave with real rows
+  int nact = TMB;                  // SKIP: MFMA row blocks of this wave with real rows
   auto frags = [&](const uint8_t* pA, const uint8_t* pB, int ks, int set) {
 #pragma unroll
     for (int i = 0; i < TMB; ++i) fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(pA + arow[i] + coff[ks]));
@@ -325,9 +323,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
     constexpr int NM = TMB * TNB;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      // weight fragment first: acc holds the transposed block (see the epilogue); row blocks
-      // of padding only are skipped (their accumulators stay 0)
-      if (m / TNB < nact)
+      // weight fragment first: acc holds the transposed block (see the epilogue). With SKIP,
+      // row blocks of padding only are skipped (their accumulators stay 0): about 3% of the
+      // sorted prefill GEMM; a dense launch keeps the branch-free loop.
+      if (!SKIP || m / TNB < nact)
         acc[m / TNB][m % TNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][m % TNB], fa[set][m / TNB],
                                                                         acc[m / TNB][m % TNB], 0, 0, 0);
       if constexpr (DM != 0) {
@@ -401,14 +400,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
   __syncthreads();
-  {
-    int nreal = a.M_rows - m0;
-    if (a.valid_map) {
-      nreal = 0;
+  if constexpr (SKIP) {
+    int nreal = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) nreal += real_rows[w];
-    }
-    // MFMA row blocks of this wave that hold at least one real row
+    for (int w = 0; w < NW; ++w) nreal += real_rows[w];
     nact = __builtin_amdgcn_readfirstlane(min(TMB, max(0, (nreal - wm * TM + 31) / 32)));
   }
   frags(sA[0], sB[0], 0, 0);

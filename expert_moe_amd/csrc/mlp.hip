@@ -26,20 +26,48 @@ int cu_count() {
 }
 
 template <int BM, int BNR, int WM, int WN, int MODE>
-void launch_tile_only(GemmArgs a, int n_rows_b, int tail_mode, hipStream_t s) {
+void launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, hipStream_t s) {
   a.n_tiles = n_rows_b / BNR;
   a.tail_mode = tail_mode;
   a.n_cu = cu_count();
-  const int grid = tail_mode == 2 ? (a.n_cu + kXcds - 1) / kXcds * kXcds : tile_grid(a.m_blocks, a.n_tiles);
-  // Three LDS stages (loads two K steps ahead) wherever they fit in the CU's 160 KB.
   constexpr size_t kLdsCu = 160 * 1024;
   constexpr size_t kStage = static_cast<size_t>(BM + BNR) * 128;
-  constexpr int NS = 3 * kStage <= kLdsCu ? 3 : 2;
-  // The quarter tiles of a tail are at most one per CU: reserve more than half of the CU's LDS
-  // (unused) so that the dispatcher cannot stack two on one CU while others stay idle.
-  constexpr size_t kStatic = NS * kStage;
-  const size_t dyn = tail_mode == 2 && kStatic <= kLdsCu / 2 ? kLdsCu / 2 + 1024 - kStatic : 0;
-  gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS><<<grid, 64 * WM * WN, dyn, s>>>(a);
+  constexpr int kThreads = 64 * WM * WN;
+  if (tail_mode == 2) {
+    // Quarter tiles of a tail, at most one per CU: three LDS stages (loads two K steps ahead)
+    // where they fit, and more than half of the CU's LDS reserved (unused) so that the
+    // dispatcher cannot stack two on one CU while others stay idle.
+    constexpr int NS = 3 * kStage <= kLdsCu ? 3 : 2;
+    constexpr size_t kStatic = NS * kStage;
+    const size_t dyn = kStatic <= kLdsCu / 2 ? kLdsCu / 2 + 1024 - kStatic : 0;
+    const int grid = (a.n_cu + kXcds - 1) / kXcds * kXcds;
+    if (a.valid_map)
+      gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, true><<<grid, kThreads, dyn, s>>>(a);
+    else
+      gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, false><<<grid, kThreads, dyn, s>>>(a);
+  } else {
+    // Three stages (one workgroup per CU) where two already take more than half of the CU's
+    // LDS, or where the expected tiles fill at most two rounds of the CUs, so that latency and
+    // not occupancy bounds them; otherwise two stages and two or more workgroups per CU.
+    constexpr bool kFits3 = 3 * kStage <= kLdsCu;
+    constexpr bool kBig = 2 * kStage > kLdsCu / 2;
+    const bool few = static_cast<int64_t>(est_blocks) * a.n_tiles <= 2 * static_cast<int64_t>(a.n_cu);
+    const int grid = tile_grid(a.m_blocks, a.n_tiles);
+    constexpr int NS3 = kFits3 ? 3 : 2;
+    const bool deep = kFits3 && (kBig || few);
+    // sorted rows skip padding row groups; dense launches keep the branch-free loop
+    if (a.valid_map) {
+      if (deep)
+        gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, true><<<grid, kThreads, 0, s>>>(a);
+      else
+        gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, true><<<grid, kThreads, 0, s>>>(a);
+    } else {
+      if (deep)
+        gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, false><<<grid, kThreads, 0, s>>>(a);
+      else
+        gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, false><<<grid, kThreads, 0, s>>>(a);
+    }
+  }
 }
 
 // Quarter tile (half BM, half BNR) and its wave grid for the tail launch; BM2 = 0: none.
@@ -52,18 +80,18 @@ template <> struct Quarter<128, 128, kStore> { static constexpr int BM2 = 64, WM
 // A tile launch; when the shape has a quarter tile, the full-size launch leaves the tail of
 // its last round (decided on the device from the row count) to a quarter-tile launch.
 template <int BM, int BNR, int WM, int WN, int MODE>
-void launch_tile(GemmArgs a, int n_rows_b, hipStream_t s) {
+void launch_tile(GemmArgs a, int n_rows_b, int est_blocks, hipStream_t s) {
   using Q = Quarter<BM, BNR, MODE>;
   if constexpr (Q::BM2 == 0) {
-    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, 0, s);
+    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
   } else {
     if (cu_count() <= 0) {
-      launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, 0, s);
+      launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
       return;
     }
-    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, 1, s);
+    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 1, s);
     a.m_blocks = 0;  // unused in tail mode 2
-    launch_tile_only<Q::BM2, BNR / 2, Q::WM, Q::WN, MODE>(a, n_rows_b, 2, s);
+    launch_tile_only<Q::BM2, BNR / 2, Q::WM, Q::WN, MODE>(a, n_rows_b, 4 * est_blocks, 2, s);
   }
 }
 
@@ -80,33 +108,33 @@ inline int pick_bnr(int n_rows_b, int est_blocks, bool silu) {
 // Wave grids: 8 waves (two per SIMD) wherever the tile splits into 8 blocks of whole MFMA
 // tiles with gate/up pairs; measured faster than 4 on the 256-row tiles.
 template <int MODE>
-void launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
+void launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
   if (bnr == 256)
-    launch_tile<256, 256, 2, 4, MODE>(a, n_rows_b, s);
+    launch_tile<256, 256, 2, 4, MODE>(a, n_rows_b, est, s);
   else if (bnr == 128)
-    launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, s);
+    launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, est, s);
   else
-    launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, s);
+    launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, est, s);
 }
 
 template <int MODE>
-void launch_tile128(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
+void launch_tile128(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
   if (bnr == 256)
-    launch_tile<128, 256, 2, 4, MODE>(a, n_rows_b, s);
+    launch_tile<128, 256, 2, 4, MODE>(a, n_rows_b, est, s);
   else if (bnr == 128)
-    launch_tile<128, 128, 4, 2, MODE>(a, n_rows_b, s);
+    launch_tile<128, 128, 4, 2, MODE>(a, n_rows_b, est, s);
   else
-    launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, s);
+    launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, est, s);
 }
 
 template <int MODE>
-void launch_tile64(const GemmArgs& a, int n_rows_b, int bnr, hipStream_t s) {
+void launch_tile64(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
   if (bnr == 256)
-    launch_tile<64, 256, 1, 4, MODE>(a, n_rows_b, s);
+    launch_tile<64, 256, 1, 4, MODE>(a, n_rows_b, est, s);
   else if (bnr == 128)
-    launch_tile<64, 128, 2, 2, MODE>(a, n_rows_b, s);
+    launch_tile<64, 128, 2, 2, MODE>(a, n_rows_b, est, s);
   else if constexpr (MODE != kSiluMul)  // 2I is always a multiple of 128
-    launch_tile<64, 64, 2, 2, MODE>(a, n_rows_b, s);
+    launch_tile<64, 64, 2, 2, MODE>(a, n_rows_b, est, s);
 }
 
 }  // namespace
@@ -204,11 +232,11 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
   else if (pl.stream)
     launch_stream<kSiluMul>(g, 2 * I, tr, est, s);
   else if (tr == 64)
-    launch_tile64<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), s);
+    launch_tile64<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
   else if (tr == 128)
-    launch_tile128<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), s);
+    launch_tile128<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
   else
-    launch_tile256<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), s);
+    launch_tile256<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -240,11 +268,11 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   else if (pl.stream)
     launch_stream<kStore>(g, H, tr, est, s);
   else if (tr == 64)
-    launch_tile64<kStore>(g, H, pick_bnr(H, est, false), s);
+    launch_tile64<kStore>(g, H, pick_bnr(H, est, false), est, s);
   else if (tr == 128)
-    launch_tile128<kStore>(g, H, pick_bnr(H, est, false), s);
+    launch_tile128<kStore>(g, H, pick_bnr(H, est, false), est, s);
   else
-    launch_tile256<kStore>(g, H, pick_bnr(H, est, false), s);
+    launch_tile256<kStore>(g, H, pick_bnr(H, est, false), est, s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

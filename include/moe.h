@@ -194,8 +194,6 @@ int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, cons
  *  moe_expert_gate_up: act[r] = silu(W1_e x[p / k]) * (W3_e x[p / k]), act [capacity, I] dtype
  *    (the gate/up projection and activation of the expert MLP).
  *  moe_expert_down:    y[r] = W2_e act[r], y [capacity, H] dtype (the down projection).
- *    sorted_pairs is optional (NULL allowed): with it, groups of padding rows are skipped;
- *    without it they are computed (their values stay unspecified either way).
  * Neither needs a workspace.
  */
 int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
@@ -203,8 +201,8 @@ int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, c
                        const int32_t* num_padded, int32_t block_m, void* act, void* stream);
 
 int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, const void* w2,
-                    const int32_t* sorted_pairs, const int32_t* block_expert,
-                    const int32_t* num_padded, int32_t block_m, void* y, void* stream);
+                    const int32_t* block_expert, const int32_t* num_padded, int32_t block_m,
+                    void* y, void* stream);
 
 /*
  * Shared expert on every token: shared_y [T, H] = W2s (silu(W1s x) * (W3s x)) with
