@@ -9,7 +9,8 @@
 // Three passes, no host synchronisation:
 //   count   : one workgroup per chunk of 256 tokens, LDS histogram of its pairs per slot; the
 //             workgroups also fill the whole sorted list with -1 (padding)
-//   scan    : one workgroup; per-slot exclusive scan over chunks (chunk bases), padded
+//   scan    : one workgroup; per-slot exclusive scan over chunks (chunk bases, read in
+//             batches of 16), padded
 //             segment sizes, exclusive scan over slots (offsets), block -> slot table
 //   scatter : one workgroup per chunk; each wave marks its 64 tokens per slot in an LDS
 //             64-bit mask; a pair's rank inside its slot is the chunk base plus the number of
@@ -55,11 +56,19 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
   const int e = threadIdx.x;
   int run = 0;
   if (e < E_l) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int64_t i = static_cast<int64_t>(c) * E_l + e;
-      const int v = chunk[i];
-      chunk[i] = run;
-      run += v;
+    // chunk counts in batches: the batch's loads are all issued before its stores, one
+    // memory round trip per batch instead of one per chunk
+    constexpr int kBatch = 16;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < nchunks ? chunk[static_cast<int64_t>(c0 + j) * E_l + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (c0 + j < nchunks) chunk[static_cast<int64_t>(c0 + j) * E_l + e] = run;
+        run += v[j];
+      }
     }
     counts[e] = run;
     seg[e] = (run + bm - 1) / bm * bm;

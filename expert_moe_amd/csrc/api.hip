@@ -281,7 +281,7 @@ int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, co
   if (!aligned16({act, w2, y})) return MOE_EINVAL;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_down(*p, static_cast<int>(num_tokens), act, w2, p->intermediate_size,
-                          nullptr, num_padded, block_expert, block_m, rows, y, as_stream(stream));
+                          num_padded, block_expert, block_m, rows, y, as_stream(stream));
 }
 
 int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,

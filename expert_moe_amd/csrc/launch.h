@@ -38,10 +38,9 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
 int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, int inter,
                    const int32_t* row_map, const int32_t* num_padded,
                    const int32_t* block_expert, int block_m, int rows, void* act, hipStream_t s);
-// sorted_pairs (optional, sorted rows only) lets the LDS tiles skip padding rows.
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
-                const int32_t* sorted_pairs, const int32_t* num_padded,
-                const int32_t* block_expert, int block_m, int rows, void* y, hipStream_t s);
+                const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
+                void* y, hipStream_t s);
 
 // Expert MLP over rows: act = silu(x W1^T) * (x W3^T), y = act W2^T.
 //  sorted (row_map != NULL): rows of the expert-sorted pair list, capacity rows, block_m granule;
