@@ -65,10 +65,11 @@ int pick_block_m(const moe_params& p, int64_t T) {
   // Expected rows per local expert under uniform routing: T*k/E.
   const double rows = static_cast<double>(T) * p.top_k / p.num_experts;
   if (p.dtype == MOE_F32) return 16;
-  // measured on MI355X: the 128/256-row LDS tiles beat smaller granules as soon as an expert
-  // gets more than a handful of rows (each expert's weights are then streamed once per block)
+  // measured on MI355X (granule sweep on every workload): past a handful of rows per expert
+  // the 256-row LDS tile wins, because each expert's weights are streamed once per row block
+  // (EP share 290 -> 276 us, DeepSeek-V2-shaped 747 -> 720 us, skewed T=256 329 -> 312 us
+  // against granule 128)
   if (rows <= 12.0) return 16;
-  if (rows < 768.0) return 128;
   return 256;
 }
 
