@@ -228,6 +228,7 @@ def run_point(host, w, T, steps, warmup):
     split_ms = (time.perf_counter() - t0) * 1e3 / steps
     names = ["route", "align", "gate_up", "down", "shared", "combine"]
     stage = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, n in enumerate(names)}
+
     return b, ms, split_ms, stage, alg
 
 

@@ -6,7 +6,7 @@
 // local are grouped by slot, kept in increasing p inside a slot, and each slot's segment is
 // padded to a multiple of block_m rows so that a GEMM tile never straddles two experts.
 //
-// Three passes, no host synchronisation:
+// Three passes, no host synchronisation (one single-workgroup kernel when T fits one chunk):
 //   count   : one workgroup per chunk of 256 tokens, LDS histogram of its pairs per slot; the
 //             workgroups also fill the whole sorted list with -1 (padding)
 //   scan    : one workgroup; per-slot exclusive scan over chunks (chunk bases, read in
@@ -136,6 +136,79 @@ __global__ void __launch_bounds__(256) align_scatter(const int32_t* __restrict__
   }
 }
 
+// All three passes in one workgroup, for T <= kAlignChunk (one chunk): LDS histogram and
+// per-wave masks, scan, then the scatter. The -1 fill of the sorted list is ordered before the
+// scatter's stores by the barrier (its fence waits for this thread's stores).
+__global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ tl, int T, int k,
+                                                    int E_l, int bm, int cap,
+                                                    int32_t* __restrict__ meta,
+                                                    int32_t* __restrict__ num_padded,
+                                                    int32_t* __restrict__ block_expert,
+                                                    int32_t* __restrict__ sorted_pairs,
+                                                    int32_t* __restrict__ pair_row) {
+  __shared__ int hist[256];
+  __shared__ int seg[257];
+  __shared__ unsigned long long mask[4][256];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  for (int i = tid; i < cap; i += 256) sorted_pairs[i] = -1;
+  for (int e = tid; e < E_l; e += 256) {
+    hist[e] = 0;
+    mask[0][e] = mask[1][e] = mask[2][e] = mask[3][e] = 0ull;
+  }
+  __syncthreads();
+  const bool valid = tid < T;
+  if (valid)
+    for (int j = 0; j < k; ++j) {
+      const int s = local_slot(tl, static_cast<int64_t>(tid) * k + j, E_l);
+      if (s >= 0) {
+        atomicAdd(&hist[s], 1);
+        atomicOr(&mask[wave][s], 1ull << lane);
+      }
+    }
+  __syncthreads();
+  int32_t* offsets = meta + 1;
+  int32_t* counts = meta + 1 + (E_l + 1);
+  for (int e = tid; e < E_l; e += 256) {
+    counts[e] = hist[e];
+    seg[e] = (hist[e] + bm - 1) / bm * bm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < E_l; ++i) {
+      const int v = seg[i];
+      seg[i] = acc;
+      acc += v;
+    }
+    seg[E_l] = acc;
+    offsets[E_l] = acc;
+    meta[0] = acc;
+    *num_padded = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < E_l; e += 256) {
+    offsets[e] = seg[e];
+    for (int b = seg[e] / bm; b < seg[e + 1] / bm; ++b) block_expert[b] = e;
+  }
+  if (!valid) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int64_t pid = static_cast<int64_t>(tid) * k + j;
+    const int s = local_slot(tl, pid, E_l);
+    if (s < 0) {
+      pair_row[pid] = -1;
+      continue;
+    }
+    int before = __popcll(mask[wave][s] & below);
+    for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
+    const int pos = seg[s] + before;
+    sorted_pairs[pos] = static_cast<int32_t>(pid);
+    pair_row[pid] = pos;
+  }
+}
+
 }  // namespace
 
 int launch_align(const moe_params& p, int T, const int32_t* topk_local, int block_m,
@@ -145,6 +218,12 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
   const int k = p.top_k;
   const int nchunks = align_chunks(T);
   const int cap = T * k + E_l * (block_m - 1);
+  if (nchunks == 1) {
+    align_single<<<1, 256, 0, s>>>(topk_local, T, k, E_l, block_m, cap, meta, num_padded, block_expert,
+                                   sorted_pairs, pair_row);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   align_count<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, sorted_pairs, cap);
   MOE_LAUNCH_CHECK();
   align_scan<<<1, 256, 0, s>>>(chunk, nchunks, E_l, block_m, meta, num_padded, block_expert);
