@@ -6,7 +6,8 @@
 // Step 4, scatter-add by token; the weighted accumulation of MixtralMoE.forward) plus the
 // shared expert ("Expert Parallel", Step 5). Each token is gathered by one workgroup, so no
 // two workgroups write the same output and no atomics are needed; the sum is fp32 in slot
-// order, rounded once to the output type.
+// order, rounded once to the output type. The token's local slots are compacted first, so
+// the loads of up to 8 rows are in flight together.
 #include "common.h"
 #include "launch.h"
 
@@ -14,25 +15,54 @@ namespace moe {
 
 namespace {
 
+// The token's local slots, compacted in slot order into LDS (k <= 64: one wave's ballot), so
+// that the row loads of several slots can be in flight together. Returns their number.
+__device__ __forceinline__ int local_slots(const int32_t* __restrict__ pair_row,
+                                           const float* __restrict__ w, int64_t pbase, int k,
+                                           int* s_r, float* s_w, int* s_n) {
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    const int r = j < k ? pair_row[pbase + j] : -1;
+    const float wt = j < k ? w[pbase + j] : 0.f;
+    const unsigned long long m = __ballot(r >= 0);
+    if (r >= 0) {
+      const int pos = __popcll(m & ((1ull << j) - 1ull));
+      s_r[pos] = r;
+      s_w[pos] = wt;
+    }
+    if (j == 0) *s_n = __popcll(m);
+  }
+  __syncthreads();
+  return *s_n;
+}
+
 __global__ void __launch_bounds__(256) combine_bf16(const uint16_t* __restrict__ y,
                                                     const int32_t* __restrict__ pair_row,
                                                     const float* __restrict__ w,
                                                     const uint16_t* __restrict__ shared_y,
                                                     uint16_t* __restrict__ out, int k, int H) {
+  __shared__ int s_r[64];
+  __shared__ float s_w[64];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  const int64_t pbase = static_cast<int64_t>(t) * k;
+  const int n = local_slots(pair_row, w, static_cast<int64_t>(t) * k, k, s_r, s_w, &s_n);
   for (int v = threadIdx.x; v < H / 8; v += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = pair_row[pbase + j];
-      if (r < 0) continue;
-      const float wt = w[pbase + j];
-      const uint4 q = load16(y + static_cast<int64_t>(r) * H + v * 8);
-      const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      uint4 q[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wt * bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
-        acc[2 * i + 1] += wt * bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+      for (int j = 0; j < 8; ++j)
+        if (j0 + j < n) q[j] = load16(y + static_cast<int64_t>(s_r[j0 + j]) * H + v * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j >= n) break;
+        const float wt = s_w[j0 + j];
+        const uint32_t u[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += wt * bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+          acc[2 * i + 1] += wt * bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+        }
       }
     }
     if (shared_y) {
@@ -58,15 +88,16 @@ __global__ void __launch_bounds__(256) combine_f32(const float* __restrict__ y,
                                                    const float* __restrict__ w,
                                                    const float* __restrict__ shared_y,
                                                    float* __restrict__ out, int k, int H) {
+  __shared__ int s_r[64];
+  __shared__ float s_w[64];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  const int64_t pbase = static_cast<int64_t>(t) * k;
+  const int n = local_slots(pair_row, w, static_cast<int64_t>(t) * k, k, s_r, s_w, &s_n);
   for (int v = threadIdx.x; v < H / 4; v += 256) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int r = pair_row[pbase + j];
-      if (r < 0) continue;
-      const float wt = w[pbase + j];
-      const float4 q = *reinterpret_cast<const float4*>(y + static_cast<int64_t>(r) * H + v * 4);
+    for (int j = 0; j < n; ++j) {
+      const float wt = s_w[j];
+      const float4 q = *reinterpret_cast<const float4*>(y + static_cast<int64_t>(s_r[j]) * H + v * 4);
       acc.x += wt * q.x;
       acc.y += wt * q.y;
       acc.z += wt * q.z;
