@@ -31,109 +31,162 @@ struct TopkArgs {
   float rsf;
 };
 
-// (v1, i1) ranks before (v2, i2): larger value, then lower index.
-__device__ __forceinline__ bool ranks_before(float v1, int i1, float v2, int i2) {
-  return v1 > v2 || (v1 == v2 && i1 < i2);
+// Wave-wide reductions as a butterfly of in-register lane exchanges (no LDS crossbar):
+// DPP quad_perm for lane distances 1 and 2, row_half_mirror and row_mirror to join groups of
+// 4 and 8 lanes inside a 16-lane row, then gfx950 v_permlane16_swap / v_permlane32_swap to join
+// rows (each lane ends with the result). The lane layouts of all six were checked with an
+// in-bounds probe on the box.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
+constexpr int kXor1 = 0xB1;        // quad_perm(1, 0, 3, 2)
+constexpr int kXor2 = 0x4E;        // quad_perm(2, 3, 0, 1)
+constexpr int kHalfMirror = 0x141; // row_half_mirror
+constexpr int kMirror = 0x140;     // row_mirror
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(v, m, 64);
-    const int oi = __shfl_xor(i, m, 64);
-    if (ranks_before(ov, oi, v, i)) { v = ov; i = oi; }
+// (a, b) = both values of a pair of lanes 16 (S = 16) or 32 (S = 32) apart.
+template <int S>
+__device__ __forceinline__ void swap_pair(uint32_t x, uint32_t& a, uint32_t& b) {
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
   }
 }
 
+// Op is a commutative, associative combine on the raw 32-bit lanes.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, dpp_partner<kXor1>(v));
+  v = op(v, dpp_partner<kXor2>(v));
+  v = op(v, dpp_partner<kHalfMirror>(v));
+  v = op(v, dpp_partner<kMirror>(v));
+  uint32_t x, y;
+  swap_pair<16>(v, x, y);
+  v = op(x, y);
+  swap_pair<32>(v, x, y);
+  return op(x, y);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  return __uint_as_float(wave_reduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+  }));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  return __uint_as_float(wave_reduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+  }));
 }
 
-// 4 tokens per workgroup (one per wave); E <= 256 so a lane holds experts lane + 64 q.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+
+// Selection key of a probability p in [0, 1]: the bit pattern of a non-negative float is
+// ordered like its value, so key = bits(p) + 1 orders candidates by p and leaves 0 for an
+// expert that may not be chosen (excluded group, or past E). p(key) = float(key - 1).
+__device__ __forceinline__ uint32_t prob_key(float p) { return __float_as_uint(p) + 1u; }
+__device__ __forceinline__ float key_prob(uint32_t k) { return __uint_as_float(k - 1u); }
+
+// 4 tokens per workgroup (one per wave); lane l holds experts l + 64 q for q < NQ, E <= 64 NQ.
+template <int NQ>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
-  __shared__ float sp[4][256];
+  __shared__ float sp[4][64 * NQ];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   const bool valid = t < a.T;
   const int E = a.E;
 
-  float pv[4];
+  float pv[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     const int e = lane + 64 * q;
     float l = -INFINITY;
     if (valid && e < E) {
       float* lp = a.logits + static_cast<int64_t>(t) * E + e;
       l = lp[0];
       const int64_t stride = static_cast<int64_t>(a.T) * E;
-      for (int sp = 1; sp < a.splits; ++sp) l += lp[sp * stride];
+      for (int sk = 1; sk < a.splits; ++sk) l += lp[sk * stride];
       if (a.splits > 1) lp[0] = l;
       if (a.bias) l += a.bias[e];
     }
     pv[q] = l;
   }
-  const float m = wave_max(fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3])));
+  float lmax = pv[0];
+#pragma unroll
+  for (int q = 1; q < NQ; ++q) lmax = fmaxf(lmax, pv[q]);
+  const float m = wave_max(lmax);
   float part = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     pv[q] = (lane + 64 * q < E) ? expf(pv[q] - m) : 0.f;
     part += pv[q];
   }
   const float ssum = wave_sum(part);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) pv[q] = pv[q] / ssum;
+  for (int q = 0; q < NQ; ++q) pv[q] = pv[q] / ssum;
 
-  // Candidate scores: p for candidates, -inf for excluded / absent experts.
-  float cv[4];
+  uint32_t key[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) cv[q] = (lane + 64 * q < E) ? pv[q] : -INFINITY;
+  for (int q = 0; q < NQ; ++q) key[q] = (lane + 64 * q < E) ? prob_key(pv[q]) : 0u;
 
   if (a.grouped) {
+    // group score = largest p of the group's E/G contiguous experts; the topk_group best
+    // groups (ties to the lower group) stay candidates
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NQ; ++q)
       if (lane + 64 * q < E) sp[wave][lane + 64 * q] = pv[q];
     __syncthreads();
     const int gsz = E / a.G;
-    float gs = -INFINITY;
+    float gs = 0.f;
     if (lane < a.G)
       for (int i = 0; i < gsz; ++i) gs = fmaxf(gs, sp[wave][lane * gsz + i]);
+    uint32_t gk = lane < a.G ? prob_key(gs) : 0u;
     uint64_t kept = 0;
     for (int r = 0; r < a.keep; ++r) {
-      float bv = gs;
-      int bi = lane;
-      wave_argmax(bv, bi);
-      kept |= 1ull << bi;
-      if (lane == bi) gs = -INFINITY;
+      const uint32_t best = wave_max_u32(gk);
+      const int g = __builtin_ctzll(__ballot(gk == best));
+      kept |= 1ull << g;
+      if (lane == g) gk = 0u;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int e = lane + 64 * q;
-      if (e < E && !((kept >> (e / gsz)) & 1ull)) cv[q] = -INFINITY;
+      if (e < E && !((kept >> (e / gsz)) & 1ull)) key[q] = 0u;
     }
   }
   if (!valid) return;
 
+  // k rounds: the largest key left, at its lowest expert id (lowest q, then lowest lane)
   int my_id = 0;
   float my_w = 0.f;
   float wsum = 0.f;
   for (int j = 0; j < a.k; ++j) {
-    float bv = cv[0];
-    int bi = lane;
+    uint32_t lk = key[0];
 #pragma unroll
-    for (int q = 1; q < 4; ++q)
-      if (ranks_before(cv[q], lane + 64 * q, bv, bi)) { bv = cv[q]; bi = lane + 64 * q; }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) cv[bi >> 6] = -INFINITY;
-    if (lane == j) { my_id = bi; my_w = bv; }
+    for (int q = 1; q < NQ; ++q) lk = key[q] > lk ? key[q] : lk;
+    const uint32_t best = wave_max_u32(lk);
+    int id = 0;
+#pragma unroll
+    for (int q = NQ - 1; q >= 0; --q) {
+      const uint64_t hit = __ballot(key[q] == best);
+      if (hit) id = 64 * q + __builtin_ctzll(hit);
+    }
+    if ((id & 63) == lane) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if ((id >> 6) == q) key[q] = 0u;
+    }
+    const float bv = key_prob(best);
+    if (lane == j) { my_id = id; my_w = bv; }
     wsum = j == 0 ? bv : wsum + bv;
   }
   if (lane < a.k) {
@@ -223,7 +276,13 @@ int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
   a.keep = p.use_grouped_topk ? p.topk_group : 1;
   a.E_l = p.num_local_experts;
   a.rsf = p.routed_scaling_factor;
-  topk_kernel<<<ceil_div(T, 4), 256, 0, s>>>(a);
+  const int blocks = ceil_div(T, 4);
+  if (a.E <= 64)
+    topk_kernel<1><<<blocks, 256, 0, s>>>(a);
+  else if (a.E <= 128)
+    topk_kernel<2><<<blocks, 256, 0, s>>>(a);
+  else
+    topk_kernel<4><<<blocks, 256, 0, s>>>(a);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
