@@ -5,6 +5,8 @@
 // fused_experts in "ep_fused_moe_patch.py" _ep_forward Step 3). Kernel choice follows the
 // number of rows per tile: the 16-row streaming kernel when few tokens reach each expert
 // (weight-bandwidth bound), the 64/128-row LDS-tiled MFMA kernel otherwise.
+#include <cmath>
+
 #include "gemm.h"
 #include "launch.h"
 
@@ -115,6 +117,31 @@ inline int pick_bnr(int n_rows_b, int est_blocks, bool silu) {
   return 64;
 }
 
+// BNR of a 256-row tile launch (one workgroup per CU): the width whose tiles are expected to
+// finish first, counting rounds of one tile per CU (a tail of at most a quarter round goes to
+// quarter tiles, about 0.6 of a round) times the time of one tile relative to a 128-wide one
+// (measured on the sorted MoE GEMMs: 1.7 for 256, about 0.6 for 64). Ties go to the wider.
+inline int pick_bnr256(int n_rows_b, int est_blocks, bool silu, int n_cu) {
+  if (n_cu <= 0) return pick_bnr(n_rows_b, est_blocks, silu);
+  struct Cand { int bnr; double w; bool quarter; };
+  constexpr Cand cands[3] = {{256, 1.7, true}, {128, 1.0, true}, {64, 0.6, false}};
+  int best = 0;
+  double best_cost = 0.0;
+  for (const Cand& c : cands) {
+    if (n_rows_b % c.bnr != 0 || (silu && c.bnr < 128)) continue;
+    const int64_t tiles = static_cast<int64_t>(est_blocks) * (n_rows_b / c.bnr);
+    const int64_t full = tiles / n_cu;
+    const int64_t rem = tiles % n_cu;
+    const double tail = rem == 0 ? 0.0 : (c.quarter && 4 * rem <= n_cu) ? 0.6 : 1.0;
+    const double cost = (static_cast<double>(full) + tail) * c.w;
+    if (best == 0 || cost < best_cost) {
+      best = c.bnr;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 // Wave grids: 8 waves (two per SIMD) wherever the tile splits into 8 blocks of whole MFMA
 // tiles with gate/up pairs; measured faster than 4 on the 256-row tiles.
 template <int MODE>
@@ -183,13 +210,21 @@ Plan plan_rows(const moe_params& p, bool sorted, int block_m, int rows, int n_ro
   return {false, dense_tile_rows(rows, n_rows_b)};
 }
 
-// Row blocks a launch is expected to have: every local expert's expected rows (uniform
-// routing) rounded up to the block, or the dense row count.
+// Row blocks a launch is expected to have: the dense row count, or for expert-sorted rows
+// every local expert's expected blocks, with the expert's rows taken as the uniform-routing
+// mean spread evenly over +-17.5% (eight points) and weighted by the chance that the expert is
+// routed at all.
 int est_row_blocks(const moe_params& p, int T, bool sorted, int tr, int rows) {
-  if (!sorted) return (rows + tr - 1) / tr;
-  const double per = static_cast<double>(T) * p.top_k / p.num_experts;
-  const int blocks = static_cast<int>(p.num_local_experts * (per / tr + 0.5)) + 1;
   const int cap = (rows + tr - 1) / tr;
+  if (!sorted) return cap;
+  const double per = static_cast<double>(T) * p.top_k / p.num_experts;
+  double b = 0.0;
+  for (int i = 0; i < 8; ++i) {
+    const double c = per * (0.825 + 0.05 * i);
+    b += std::ceil((c > 1.0 ? c : 1.0) / tr);
+  }
+  const double touched = 1.0 - std::exp(-per);
+  const int blocks = static_cast<int>(std::ceil(p.num_local_experts * touched * b / 8.0));
   return blocks < cap ? blocks : cap;
 }
 
@@ -259,7 +294,7 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
   else if (tr == 128)
     launch_tile128<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
   else
-    launch_tile256<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
+    launch_tile256<kSiluMul>(g, 2 * I, pick_bnr256(2 * I, est, true, cu_count()), est, s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -297,7 +332,7 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   else if (tr == 128)
     launch_tile128<kStore>(g, H, pick_bnr(H, est, false), est, s);
   else
-    launch_tile256<kStore>(g, H, pick_bnr(H, est, false), est, s);
+    launch_tile256<kStore>(g, H, pick_bnr256(H, est, false, cu_count()), est, s);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
