@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/moe.h.
 #include <initializer_list>
 #include <math.h>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -81,7 +82,7 @@ int64_t capacity(const moe_params& p, int64_t T, int bm) {
 // regions it owns, placed from offset 0 of the caller's workspace.
 struct Layout {
   size_t topk_ids, topk_w, topk_local, sorted_pairs, block_expert, pair_row, num_padded;
-  size_t meta, chunk, y, shared_y, scratch, total;
+  size_t meta, chunk, y, shared_y, shared_act, scratch, total;
   // sizes of the split entry points' scratch needs
   size_t route_need, align_need, mlp_need, shared_need;
 };
@@ -110,6 +111,8 @@ Layout layout(const moe_params& p, int64_t T, int bm) {
   L.chunk = take(nch * E_l * 4);
   L.y = take(cap * p.hidden_size * eb);
   L.shared_y = take(p.shared_intermediate_size ? static_cast<size_t>(T) * p.hidden_size * eb : 0);
+  // the shared MLP's intermediate rows: its own region, since it runs beside the routed path
+  L.shared_act = take(static_cast<size_t>(T) * p.shared_intermediate_size * eb);
   L.route_need = round_up(static_cast<size_t>(moe::router_splits(p, static_cast<int>(T))) * T *
                           p.num_experts * 4);
   L.align_need = round_up((2 * E_l + 2) * 4) + round_up(nch * E_l * 4);
@@ -117,13 +120,42 @@ Layout layout(const moe_params& p, int64_t T, int bm) {
   L.shared_need = round_up(static_cast<size_t>(T) * p.shared_intermediate_size * eb);
   size_t need = L.route_need;
   if (L.mlp_need > need) need = L.mlp_need;
-  if (L.shared_need > need) need = L.shared_need;
   L.scratch = take(need);
   L.total = o;
   // The split entry points place their own regions at offset 0; forward's total covers
   // each of them because it is at least the scratch region plus the align tables.
   if (L.align_need > L.total) L.total = L.align_need;
   return L;
+}
+
+// Side stream of a device for the shared expert. Its MLP reads only x and its own weights, so
+// it can run beside router, alignment and routed MLP, where its tiles fill the CUs that their
+// launches leave idle (last rounds, few-tile launches). One stream and a fork / join event pair
+// per device, created on first use (default priority, non-blocking); the mutex keeps each
+// caller's record / wait pairs together. Unavailable (creation failed): the caller's stream
+// runs the shared MLP in order.
+struct SideStream {
+  std::mutex mu;
+  bool tried = false;
+  bool ok = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+
+SideStream* side_stream() {
+  static SideStream side[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = side[dev];
+  std::lock_guard<std::mutex> lk(ss.mu);
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return ss.ok ? &ss : nullptr;
 }
 
 template <typename T_>
@@ -343,7 +375,31 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
   int32_t* num_padded = at<int32_t>(ws, L.num_padded);
   void* y = at<char>(ws, L.y);
   void* shared_y = shared ? at<char>(ws, L.shared_y) : nullptr;
+  void* shared_act = at<char>(ws, L.shared_act);
   void* scratch = at<char>(ws, L.scratch);
+  auto shared_mlp = [&](hipStream_t st) {
+    return moe::launch_mlp(*p, T, x, shared_w13, shared_w2, p->shared_intermediate_size, nullptr,
+                           nullptr, nullptr, 0, T, shared_act, shared_y, st);
+  };
+
+  // Shared expert: forked onto the side stream (after everything the caller queued before) when
+  // its gate/up projection is at most four rounds of 256x256 tiles. Measured on MI355X: beside
+  // the routed path it saves 2-8% where that path leaves CUs idle (DeepSeek-V2-shaped T=4096,
+  // skewed T=1 and T=256); two long GEMMs side by side (skewed T=16384, six rounds) lose 1.6%
+  // to cache contention, so those run in order.
+  const int n_cu = moe::device_cu_count();
+  const int64_t shared_tiles = (static_cast<int64_t>(T) + 255) / 256 *
+                               ((2 * static_cast<int64_t>(p->shared_intermediate_size) + 255) / 256);
+  SideStream* side = shared && n_cu > 0 && shared_tiles <= 4 * static_cast<int64_t>(n_cu) ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> lk;
+  if (side) {
+    lk = std::unique_lock<std::mutex>(side->mu);
+    if (hipEventRecord(side->fork, s) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return MOE_EHIP;
+    if ((rc = shared_mlp(side->stream))) return rc;
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_EHIP;
+  }
 
   if ((rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s))) return rc;
   if ((rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, expert_map, ids, tw,
@@ -356,10 +412,11 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
   if ((rc = moe::launch_mlp(*p, T, x, w13, w2, p->intermediate_size, sorted_pairs, num_padded,
                             block_expert, bm, rows, scratch, y, s)))
     return rc;
-  if (shared &&
-      (rc = moe::launch_mlp(*p, T, x, shared_w13, shared_w2, p->shared_intermediate_size, nullptr,
-                            nullptr, nullptr, 0, T, scratch, shared_y, s)))
+  if (side) {
+    if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return MOE_EHIP;
+  } else if (shared && (rc = shared_mlp(s))) {
     return rc;
+  }
   return moe::launch_combine(*p, T, y, pair_row, tw, shared_y, out, s);
 }
 

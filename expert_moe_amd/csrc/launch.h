@@ -50,6 +50,9 @@ int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const
                const int32_t* block_expert, int block_m, int rows, void* act, void* y,
                hipStream_t s);
 
+// Compute units of the current device (cached per device); 0 if the query fails.
+int device_cu_count();
+
 // out[t] = sum_j w[t,j] * y[pair_row[t,j]] (+ shared_y[t]).
 int launch_combine(const moe_params& p, int T, const void* y, const int32_t* pair_row,
                    const float* topk_w, const void* shared_y, void* out, hipStream_t s);

@@ -337,6 +337,8 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   return MOE_OK;
 }
 
+int device_cu_count() { return cu_count(); }
+
 int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const void* w2,
                int inter, const int32_t* row_map, const int32_t* num_padded,
                const int32_t* block_expert, int block_m, int rows, void* act, void* y,

@@ -226,9 +226,16 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
 
 /*
  * The whole layer on this share: moe_route -> moe_align_permute -> moe_grouped_mlp
- * (-> moe_shared_mlp) -> moe_combine, all on `stream`, with the granule of
- * moe_pick_block_m. out [T, H] = this share's partial sum; summing the outputs of all
- * disjoint shares (the shared expert passed to exactly one of them) gives the full layer.
+ * (-> moe_shared_mlp) -> moe_combine, with the granule of moe_pick_block_m. Ordered on
+ * `stream`: it starts after the work queued there before it, and the work queued after it
+ * sees its outputs. When a short shared expert is given (its gate/up projection at most four
+ * rounds of 256x256 tiles), its MLP runs on a library-owned stream of the device (one per
+ * device, created on the first such call, never destroyed), forked from `stream` at the call
+ * and joined back before the combine, so that it overlaps the routed path; the fork and join
+ * are events, so the pattern can also be captured into a HIP graph. Calls from several host
+ * threads on one device are serialised while they enqueue, and their shared-expert MLPs share
+ * that stream. out [T, H] = this share's partial sum; summing the outputs of all disjoint
+ * shares (the shared expert passed to exactly one of them) gives the full layer.
  * A share that receives no pairs writes zeros (plus the shared expert).
  *  shared_w13 / shared_w2: both NULL (no shared expert on this share) or both given
  *    (then p->shared_intermediate_size > 0).

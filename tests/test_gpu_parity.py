@@ -99,6 +99,57 @@ def test_repeated_calls_bit_identical():
         assert np.array_equal(u, v)
 
 
+@pytest.mark.parametrize("case", ["ds_s", "skew_s600"])
+def test_concurrent_callers_match_single_thread(case):
+    """Two host threads calling moe_forward at once, each on its own stream with its own
+    buffers, so that their shared-expert MLPs meet on the library's side stream: every call
+    reproduces the single-thread output and routing bit for bit."""
+    import threading
+    w, T = SMALL[case]
+    layer = Layer(w, T)
+    ref = layer.forward()
+    p = params(w)
+    d = layer.d
+    dev = d["x"].device
+    n_threads, n_calls = 2, 6
+    bufs = []
+    for _ in range(n_threads):
+        bufs.append(dict(
+            st=torch.cuda.Stream(device=dev),
+            out=torch.empty(T, w.hidden_size, dtype=d["x"].dtype, device=dev),
+            ids=torch.empty(T, w.top_k, dtype=torch.int32, device=dev),
+            tw=torch.empty(T, w.top_k, dtype=torch.float32, device=dev),
+            ws=torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    results = [[] for _ in range(n_threads)]
+    errors = []
+
+    def worker(i):
+        b = bufs[i]
+        try:
+            for _ in range(n_calls):
+                moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"],
+                                d["sw13"], d["sw2"], b["out"], b["ids"], b["tw"], b["ws"],
+                                stream=b["st"])
+                b["st"].synchronize()
+                results[i].append((b["out"].float().cpu().numpy(), b["ids"].cpu().numpy(),
+                                   b["tw"].cpu().numpy()))
+        except Exception as e:  # re-raised below in the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(n_threads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(n_threads):
+        assert len(results[i]) == n_calls
+        for got in results[i]:
+            for u, v in zip(got, ref):
+                assert np.array_equal(u, v)
+
+
 @pytest.mark.parametrize("case,ep", [("ep_s", 4), ("ds_s", 8), ("skew_s600", 8), ("tiny", 4)])
 def test_share_sum_equals_all_local(case, ep):
     """Sum of every disjoint share's output (shared expert on rank 0) = the all-local layer."""
