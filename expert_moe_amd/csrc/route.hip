@@ -209,7 +209,7 @@ int router_splits(const moe_params& p, int T) {
   const int bnr = 64;
   const int blocks = ((T + rows - 1) / rows) * ((p.num_experts + bnr - 1) / bnr);
   int sp = 1;
-  while (sp < 16 && blocks * sp < 512 && p.hidden_size % (256 * 2 * sp) == 0) sp *= 2;
+  while (sp < 16 && blocks * sp < 256 && p.hidden_size % (256 * 2 * sp) == 0) sp *= 2;
   return sp;
 }
 
@@ -251,7 +251,9 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
     else if (bnr == 128)
       gemm_bf16_dma<128, 128, 2, 2, kStoreF32><<<grid, 256, 0, s>>>(a);
     else
-      gemm_bf16_dma<128, 64, 4, 1, kStoreF32><<<grid, 256, 0, s>>>(a);
+      // three LDS stages: the loads run two K steps ahead, which this short-K, latency-bound
+      // launch needs (measured: EP share 42 -> 35 us, with splits for about one workgroup per CU)
+      gemm_bf16_dma<128, 64, 4, 1, kStoreF32, 3><<<grid, 256, 0, s>>>(a);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
