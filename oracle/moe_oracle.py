@@ -51,6 +51,7 @@ __all__ = [
     "route",
     "gated_mlp", "moe_forward_given_routing", "moe_forward", "moe_forward_per_token",
     "align_permute", "weight_bytes",
+    "ep_dispatch", "ep_pack", "ep_combine",
 ]
 
 
@@ -299,3 +300,74 @@ def weight_bytes(n_experts, hidden, inter, dtype_bytes, layers=1):
     """
     return int(n_experts) * (2 * int(inter) * int(hidden) + int(hidden) * int(inter)) \
         * int(dtype_bytes) * int(layers)
+
+
+def ep_dispatch(topk_ids, top_k, num_experts, ep_size):
+    """Dispatch plan of the expert-parallel exchange: one send row per (token, destination rank).
+
+    "ep_fused_moe_patch.py", ``_ep_forward`` Step 2: the destination rank of pair (t, j) is
+    ``topk_ids[t, j] // (num_experts / ep_size)`` (contiguous expert shares, as ``_ep_init``
+    sets them up); the work items are ordered by destination rank so that each rank's items
+    are contiguous for the all-to-all, with a per-rank count. Here a token is sent to each of
+    its destination ranks once (the pairs of token t that go to rank r share one row): pair
+    (t, j) owns the row when no earlier slot j' < j of t goes to the same rank. Rows of one
+    rank follow increasing token index.
+
+    Returns ``send_pos`` [T*k] (the row of pair (t, j) when it owns one, else -1),
+    ``send_token`` [n_send], ``counts`` [ep_size] and ``offsets`` [ep_size + 1].
+    """
+    ids = np.asarray(topk_ids, np.int64).reshape(-1, top_k)
+    T = ids.shape[0]
+    per = num_experts // ep_size
+    dest = ids // per
+    owner = np.zeros(ids.shape, bool)
+    for j in range(top_k):
+        owner[:, j] = np.all(dest[:, :j] != dest[:, j:j + 1], axis=1)
+    counts = np.array([int(np.sum(owner & (dest == r))) for r in range(ep_size)], np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    send_pos = np.full(T * top_k, -1, np.int32)
+    send_token = np.zeros(int(offsets[-1]), np.int32)
+    for r in range(ep_size):
+        tt, jj = np.nonzero(owner & (dest == r))  # row-major: increasing token index
+        rows = offsets[r] + np.arange(tt.shape[0])
+        send_pos[tt * top_k + jj] = rows
+        send_token[rows] = tt
+    return {"send_pos": send_pos, "send_token": send_token, "counts": counts.astype(np.int32),
+            "offsets": offsets.astype(np.int32), "n_send": int(offsets[-1])}
+
+
+def ep_pack(plan, x, topk_ids, topk_w, top_k, num_experts, ep_size):
+    """Send buffers of the exchange, in the order of ``ep_dispatch``.
+
+    ``_ep_forward`` Step 2 gathers each work item's hidden row, expert id and routing weight
+    in destination order. A send row carries the token's hidden row, its k routing weights,
+    and its k slots seen from the destination rank: the local expert index
+    ``id - r * (num_experts / ep_size)`` for the slots that rank r owns, -1 for the others
+    (``_ep_forward`` Step 3, ``recv_ids - start_expert``).
+    """
+    ids = np.asarray(topk_ids, np.int64).reshape(-1, top_k)
+    w = np.asarray(topk_w, np.float32).reshape(-1, top_k)
+    per = num_experts // ep_size
+    tok = plan["send_token"].astype(np.int64)
+    rank = np.searchsorted(plan["offsets"], np.arange(tok.shape[0]), side="right") - 1
+    send_x = np.asarray(x)[tok]
+    local = ids[tok] - rank[:, None] * per
+    send_local = np.where((local >= 0) & (local < per), local, -1).astype(np.int32)
+    return {"send_x": send_x, "send_local": send_local, "send_w": w[tok], "rank": rank}
+
+
+def ep_combine(plan, recv_y, top_k):
+    """Unpack of the exchange: out[t] = sum of the rows that token t's ranks sent back.
+
+    ``_ep_forward`` Step 4: each rank returns, for every row it received, that token's
+    weighted result over its own experts; the results go back to token order and are summed
+    per token (the scatter-add). Here the sum runs over token t's send rows in slot order
+    (the order of ``send_pos``), in fp64 on the upcast rows.
+    """
+    pos = plan["send_pos"].reshape(-1, top_k)
+    recv = np.asarray(recv_y, np.float64)
+    out = np.zeros((pos.shape[0], recv.shape[1] if recv.ndim == 2 else 0), np.float64)
+    for j in range(top_k):
+        sel = pos[:, j] >= 0
+        out[sel] += recv[pos[sel, j]]
+    return out

@@ -70,6 +70,14 @@ def test_forward_small(case):
     _full_check(Layer(w, T))
 
 
+@pytest.mark.parametrize("case", ["ds_s", "ep_s"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+def test_forward_decode_sizes(case, T):
+    """Decode-sized calls (one to five tokens, granule 16, weight-streaming kernels): routing and
+    output vs the oracle on every token."""
+    w, _ = SMALL[case]
+    _full_check(Layer(w, T))
+
 FULL = [(k, T) for k in ("tiny", "mixtral", "ep_share", "dsv2", "skewed")
         for T in wl.WORKLOADS[k].tokens]
 

@@ -337,3 +337,103 @@ def test_memory_arithmetic_golden():
     assert vals["full"] == 45 * GiB
     assert vals["ep4"] == vals["full"] // 4 and vals["tp2"] == vals["full"] // 2
     assert abs(vals["ep4"] / GiB - 5.6) > 5  # the printed 5.6 GiB is not reproducible
+
+
+# ---------------------------------------------------------------- NEXT-1 exchange (dispatch / combine)
+def _distinct_ids(T, k, E, seed):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+def _dispatch_brute(ids, E, R):
+    """Rank by rank, token by token: a token goes to rank r once, carried by its first slot
+    whose expert lives on r (written independently of the oracle's vectorised form)."""
+    T, k = ids.shape
+    per = E // R
+    send_pos = [-1] * (T * k)
+    send_token, counts = [], []
+    for r in range(R):
+        c = 0
+        for t in range(T):
+            js = [j for j in range(k) if ids[t, j] // per == r]
+            if js:
+                send_pos[t * k + js[0]] = len(send_token)
+                send_token.append(t)
+                c += 1
+        counts.append(c)
+    return np.array(send_pos), np.array(send_token, dtype=np.int64), np.array(counts)
+
+
+@pytest.mark.parametrize("T,k,E,R", [(1, 1, 2, 2), (5, 2, 4, 2), (7, 3, 8, 4), (6, 4, 8, 8), (9, 2, 6, 3),
+                                     (4, 3, 9, 1)])
+def test_ep_dispatch_brute_force(T, k, E, R):
+    for seed in range(5):
+        ids = _distinct_ids(T, k, E, seed)
+        # repeated experts in one token (external routing) must still give one row per rank
+        if seed == 4 and k > 1:
+            ids[:, 1] = ids[:, 0]
+        plan = oracle.ep_dispatch(ids, k, E, R)
+        pos, tok, cnt = _dispatch_brute(ids, E, R)
+        assert np.array_equal(plan["send_pos"], pos)
+        assert np.array_equal(plan["send_token"], tok)
+        assert np.array_equal(plan["counts"], cnt)
+        assert plan["offsets"][0] == 0 and np.array_equal(np.diff(plan["offsets"]), cnt)
+        assert plan["n_send"] == int(cnt.sum())
+
+
+def test_ep_dispatch_special_cases():
+    ids = _distinct_ids(10, 3, 12, 1)
+    # one rank: every token is sent once, by its first slot, in token order
+    p1 = oracle.ep_dispatch(ids, 3, 12, 1)
+    assert np.array_equal(p1["send_token"], np.arange(10))
+    assert np.array_equal(p1["send_pos"].reshape(10, 3)[:, 0], np.arange(10))
+    assert np.all(p1["send_pos"].reshape(10, 3)[:, 1:] == -1)
+    # one slot per token: every pair owns a row, n_send = T
+    p2 = oracle.ep_dispatch(ids[:, :1], 1, 12, 4)
+    assert p2["n_send"] == 10 and np.all(p2["send_pos"] >= 0)
+    # as many ranks as experts: no two distinct experts share a rank, so every pair owns a row
+    p3 = oracle.ep_dispatch(ids, 3, 12, 12)
+    assert p3["n_send"] == 30 and np.all(p3["send_pos"] >= 0)
+
+
+def test_ep_pack_rows_and_local_slots():
+    T, k, E, R = 13, 3, 12, 4
+    per = E // R
+    ids = _distinct_ids(T, k, E, 2)
+    w = np.random.default_rng(3).uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    x = _rand((T, 5), (901, 0, 0))
+    plan = oracle.ep_dispatch(ids, k, E, R)
+    pk = oracle.ep_pack(plan, x, ids, w, k, E, R)
+    for row, t in enumerate(plan["send_token"]):
+        r = int(np.searchsorted(plan["offsets"], row, side="right") - 1)
+        assert np.array_equal(pk["send_x"][row], x[t])
+        assert np.array_equal(pk["send_w"][row], w[t])
+        # the local slot of each expert seen from rank r: expert_map of that share
+        emap_r = np.full(E, -1)
+        emap_r[r * per:(r + 1) * per] = np.arange(per)
+        assert np.array_equal(pk["send_local"][row], emap_r[ids[t]])
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_ep_exchange_reconstructs_layer(R):
+    """dispatch -> each rank's share of the layer on the rows it received -> combine equals
+    the all-local layer (the expert-parallel share sum, through the exchange)."""
+    E, H, I, T, k = 8, 24, 16, 11, 3
+    x, _, w13, w2, _, _ = _tiny_layer(E=E, H=H, I=I, T=T, seed=3)
+    ids = _distinct_ids(T, k, E, 7)
+    w = np.random.default_rng(8).uniform(0.1, 1.0, (T, k))
+    plan = oracle.ep_dispatch(ids, k, E, R)
+    pk = oracle.ep_pack(plan, x, ids, w.astype(np.float32), k, E, R)
+    per = E // R
+    recv = np.zeros((plan["n_send"], H))
+    for r in range(R):
+        a, b = plan["offsets"][r], plan["offsets"][r + 1]
+        emap_r = np.full(E, -1)
+        emap_r[r * per:(r + 1) * per] = np.arange(per)
+        rows = plan["send_token"][a:b]
+        recv[a:b] = oracle.moe_forward_given_routing(pk["send_x"][a:b], ids[rows], pk["send_w"][a:b],
+                                                     emap_r, w13[r * per:(r + 1) * per],
+                                                     w2[r * per:(r + 1) * per])
+    got = oracle.ep_combine(plan, recv, k)
+    want = oracle.moe_forward_given_routing(x, ids, w.astype(np.float32), np.arange(E), w13, w2)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
