@@ -27,6 +27,7 @@ EXPORTS = (
     "moe_workspace_size", "moe_make_expert_map", "moe_weight_bytes", "moe_route",
     "moe_align_permute", "moe_grouped_mlp", "moe_expert_gate_up", "moe_expert_down",
     "moe_shared_mlp", "moe_combine", "moe_forward",
+    "moe_ep_send_capacity", "moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_combine",
 )
 
 
@@ -88,6 +89,11 @@ _SIGS = {
     "moe_combine": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_forward": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                      _vp], ctypes.c_int),
+    "moe_ep_send_capacity": ([_P, _i64, _i32], _i64),
+    "moe_ep_workspace_size": ([_P, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
+    "moe_ep_dispatch": ([_P, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                        ctypes.c_int),
+    "moe_ep_combine": ([_P, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
 }
 
 
@@ -231,3 +237,31 @@ def moe_forward(p, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, share
                              _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(shared_w13),
                              _ptr(shared_w2), _ptr(out), _ptr(topk_ids_out), _ptr(topk_w_out),
                              wp, wn, _stream(stream)), "moe_forward")
+
+
+def moe_ep_send_capacity(p, num_tokens: int, ep_size: int) -> int:
+    n = lib().moe_ep_send_capacity(ctypes.byref(p), num_tokens, ep_size)
+    if n < 0:
+        raise MoeError(MOE_EINVAL, "moe_ep_send_capacity")
+    return n
+
+
+def moe_ep_workspace_size(p, num_tokens: int, ep_size: int) -> int:
+    n = _sz()
+    _check(lib().moe_ep_workspace_size(ctypes.byref(p), num_tokens, ep_size, ctypes.byref(n)),
+           "moe_ep_workspace_size")
+    return n.value
+
+
+def moe_ep_dispatch(p, num_tokens, ep_size, topk_ids, topk_w, x, send_pos, rank_meta, send_token,
+                    send_x, send_local, send_w, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_ep_dispatch(ctypes.byref(p), num_tokens, ep_size, _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(x), _ptr(send_pos), _ptr(rank_meta), _ptr(send_token),
+                                 _ptr(send_x), _ptr(send_local), _ptr(send_w), wp, wn,
+                                 _stream(stream)), "moe_ep_dispatch")
+
+
+def moe_ep_combine(p, num_tokens, send_pos, recv_y, out, stream=None):
+    _check(lib().moe_ep_combine(ctypes.byref(p), num_tokens, _ptr(send_pos), _ptr(recv_y), _ptr(out),
+                                _stream(stream)), "moe_ep_combine")

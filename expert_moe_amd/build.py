@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libexpert_moe.so")
-SOURCES = ["api.hip", "route.hip", "align.hip", "mlp.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "align.hip", "mlp.hip", "combine.hip", "exchange.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

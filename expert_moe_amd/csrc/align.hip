@@ -91,7 +91,8 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
     const int off = seg[e];
     const int end = seg[e + 1];
     offsets[e] = off;
-    for (int b = off / bm; b < end / bm; ++b) block_expert[b] = e;
+    if (block_expert)  // NULL: no row-block table wanted (the exchange's rank grouping)
+      for (int b = off / bm; b < end / bm; ++b) block_expert[b] = e;
   }
 }
 
@@ -190,7 +191,8 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
   __syncthreads();
   for (int e = tid; e < E_l; e += 256) {
     offsets[e] = seg[e];
-    for (int b = seg[e] / bm; b < seg[e + 1] / bm; ++b) block_expert[b] = e;
+    if (block_expert)
+      for (int b = seg[e] / bm; b < seg[e + 1] / bm; ++b) block_expert[b] = e;
   }
   if (!valid) return;
   const unsigned long long below = (1ull << lane) - 1ull;

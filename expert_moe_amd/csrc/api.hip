@@ -421,3 +421,91 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ expert-parallel exchange
+
+namespace {
+
+int check_ep(const moe_params* p, int32_t ep_size) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (ep_size < 1 || ep_size > 256 || p->num_experts % ep_size != 0) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int64_t ep_rows(const moe_params& p, int64_t T, int32_t ep_size) {
+  return T * (p.top_k < ep_size ? p.top_k : ep_size);
+}
+
+struct EpLayout {
+  size_t rank_of, sorted_pairs, chunk, total;
+};
+
+EpLayout ep_layout(const moe_params& p, int64_t T, int32_t ep_size) {
+  EpLayout L{};
+  const size_t pairs = static_cast<size_t>(T) * p.top_k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.rank_of = take(pairs * 4);
+  L.sorted_pairs = take(pairs * 4);
+  L.chunk = take(static_cast<size_t>(align_chunks(T)) * ep_size * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_ep_send_capacity(const moe_params* p, int64_t num_tokens, int32_t ep_size) {
+  if (check_ep(p, ep_size) || num_tokens < 0) return -1;
+  return ep_rows(*p, num_tokens, ep_size);
+}
+
+int moe_ep_workspace_size(const moe_params* p, int64_t num_tokens, int32_t ep_size, size_t* bytes) {
+  int rc = check_ep(p, ep_size);
+  if (rc) return rc;
+  if (!bytes) return MOE_EINVAL;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  *bytes = ep_layout(*p, num_tokens, ep_size).total;
+  return MOE_OK;
+}
+
+int moe_ep_dispatch(const moe_params* p, int64_t num_tokens, int32_t ep_size,
+                    const int32_t* topk_ids, const float* topk_w, const void* x, int32_t* send_pos,
+                    int32_t* rank_meta, int32_t* send_token, void* send_x, int32_t* send_local,
+                    float* send_w, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_ep(p, ep_size);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (num_tokens == 0) return MOE_OK;
+  if (!topk_ids || !topk_w || !x || !send_pos || !rank_meta || !send_token || !send_x ||
+      !send_local || !send_w || !ws)
+    return MOE_EINVAL;
+  if (!aligned16({x, send_x})) return MOE_EINVAL;
+  const EpLayout L = ep_layout(*p, num_tokens, ep_size);
+  if (ws_bytes < L.total) return MOE_ENOSPC;
+  const moe::EpScratch sc{at<int32_t>(ws, L.rank_of), at<int32_t>(ws, L.sorted_pairs),
+                          at<int32_t>(ws, L.chunk)};
+  return moe::launch_ep_dispatch(*p, static_cast<int>(num_tokens), ep_size, topk_ids, topk_w, x,
+                                 send_pos, rank_meta, send_token, send_x, send_local, send_w, sc,
+                                 as_stream(stream));
+}
+
+int moe_ep_combine(const moe_params* p, int64_t num_tokens, const int32_t* send_pos,
+                   const void* recv_y, void* out, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (num_tokens == 0) return MOE_OK;
+  if (!send_pos || !recv_y || !out) return MOE_EINVAL;
+  if (!aligned16({recv_y, out})) return MOE_EINVAL;
+  return moe::launch_combine(*p, static_cast<int>(num_tokens), recv_y, send_pos, nullptr, nullptr,
+                             out, as_stream(stream));
+}
+
+}  // extern "C"

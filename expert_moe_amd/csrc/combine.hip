@@ -1,6 +1,7 @@
 // Routing-weighted combine back to token order (gfx950), without atomics.
 //
 // out[t] = sum_{j < k, pair_row[t*k+j] >= 0} w[t*k+j] * y[pair_row[t*k+j]] (+ shared_y[t])
+// (w = NULL: weight 1, the unpack of the expert-parallel exchange)
 //
 // The per-token sum of the weighted expert rows ("ep_fused_moe_patch.py", _ep_forward
 // Step 4, scatter-add by token; the weighted accumulation of MixtralMoE.forward) plus the
@@ -23,7 +24,7 @@ __device__ __forceinline__ int local_slots(const int32_t* __restrict__ pair_row,
   if (threadIdx.x < 64) {
     const int j = threadIdx.x;
     const int r = j < k ? pair_row[pbase + j] : -1;
-    const float wt = j < k ? w[pbase + j] : 0.f;
+    const float wt = j < k ? (w ? w[pbase + j] : 1.f) : 0.f;  // no weights: each row counts once
     const unsigned long long m = __ballot(r >= 0);
     if (r >= 0) {
       const int pos = __popcll(m & ((1ull << j) - 1ull));

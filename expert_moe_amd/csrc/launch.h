@@ -28,7 +28,7 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
 int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
                 const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s);
 
-// Count / scan / scatter of the (token, slot) pairs by local expert.
+// Count / scan / scatter of the (token, slot) pairs by local expert (block_expert may be NULL).
 // meta: [num_padded(1) | offsets(E_l+1) | counts(E_l)], chunk: [align_chunks(T) * E_l].
 int launch_align(const moe_params& p, int T, const int32_t* topk_local, int block_m,
                  int32_t* sorted_pairs, int32_t* block_expert, int32_t* pair_row,
@@ -53,7 +53,22 @@ int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const
 // Compute units of the current device (cached per device); 0 if the query fails.
 int device_cu_count();
 
-// out[t] = sum_j w[t,j] * y[pair_row[t,j]] (+ shared_y[t]).
+// Scratch of the exchange dispatch: the owning rank of every pair [T*k], the rank-sorted pair
+// list [T*k], the alignment's chunk counts.
+struct EpScratch {
+  int32_t* rank_of;
+  int32_t* sorted_pairs;
+  int32_t* chunk;
+};
+
+// Dispatch plan and send buffers of the expert-parallel exchange (one row per token and
+// destination rank); rank_meta: [n_send | offsets (ep_size+1) | counts (ep_size)].
+int launch_ep_dispatch(const moe_params& p, int T, int ep_size, const int32_t* ids, const float* w,
+                       const void* x, int32_t* send_pos, int32_t* rank_meta, int32_t* send_token,
+                       void* send_x, int32_t* send_local, float* send_w, const EpScratch& ws,
+                       hipStream_t s);
+
+// out[t] = sum_j w[t,j] * y[pair_row[t,j]] (+ shared_y[t]); w = NULL: weight 1.
 int launch_combine(const moe_params& p, int T, const void* y, const int32_t* pair_row,
                    const float* topk_w, const void* shared_y, void* out, hipStream_t s);
 

@@ -248,6 +248,58 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
                 int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* ------------------------------------------------------------------ expert-parallel exchange */
+/*
+ * The steps on either side of the path when tokens travel to the ranks that own their experts
+ * ("ep_fused_moe_patch.py", _ep_forward Step 2 dispatch and Step 4 combine). Ranks own
+ * contiguous shares of E / ep_size experts (as moe_make_expert_map). A token travels to each
+ * of its destination ranks once: its first slot j whose expert lives on rank r owns the row,
+ * and the row carries all k slots, so the receiving rank applies every one of its experts
+ * that the token picked. On one GPU these are layout transforms; between GPUs each rank's
+ * part of the send buffers is the segment of an all-to-all.
+ *  ep_size: 1..256, dividing p->num_experts; MOE_EINVAL otherwise.
+ */
+
+/* Send rows for T tokens: T * min(k, ep_size) (every token to min(k, ep_size) ranks); -1 on
+ * invalid arguments. */
+int64_t moe_ep_send_capacity(const moe_params* p, int64_t num_tokens, int32_t ep_size);
+
+/* Workspace bytes that moe_ep_dispatch needs for T tokens. */
+int moe_ep_workspace_size(const moe_params* p, int64_t num_tokens, int32_t ep_size,
+                          size_t* bytes);
+
+/*
+ * Dispatch plan and send buffers (Step 2). Rows are grouped by destination rank, rank 0 first,
+ * and follow increasing token index inside a rank; no sort, no host synchronisation. Inputs:
+ * topk_ids / topk_w [T, k] (global expert ids in [0, E); ids outside are not sent) and
+ * x [T, H] (p->dtype). Outputs, device memory, capacity R = moe_ep_send_capacity rows:
+ *  send_pos   [T*k]  the row of pair (t, j) when it owns one, else -1;
+ *  rank_meta  [2*ep_size + 2]  n_send, then the ranks' row offsets (ep_size + 1), then their
+ *             row counts (ep_size): rank r's rows are [offsets[r], offsets[r+1]);
+ *  send_token [R]    the token of each row;
+ *  send_x     [R, H] the token's hidden row (16-byte aligned, as x);
+ *  send_local [R, k] the token's k slots seen from the row's rank: local expert index there,
+ *             or -1 for experts of other ranks (moe_align_permute's topk_local on that rank);
+ *  send_w     [R, k] the token's k routing weights.
+ * Rows past n_send are not written.
+ *  ws: at least moe_ep_workspace_size bytes.
+ */
+int moe_ep_dispatch(const moe_params* p, int64_t num_tokens, int32_t ep_size,
+                    const int32_t* topk_ids, const float* topk_w, const void* x,
+                    int32_t* send_pos, int32_t* rank_meta, int32_t* send_token, void* send_x,
+                    int32_t* send_local, float* send_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine side (Step 4): recv_y [n_send, H] holds, row by row in the order of the dispatch,
+ * the result that row's rank computed for its token (that rank's share of the layer: the
+ * weighted sum over its experts, as moe_combine writes it). Then
+ *   out[t] = sum_{j < k, send_pos[t*k+j] >= 0} recv_y[send_pos[t*k+j]]
+ * accumulated in fp32 in slot order and rounded once to dtype (the per-token scatter-add).
+ * Overwrites out [T, H].
+ */
+int moe_ep_combine(const moe_params* p, int64_t num_tokens, const int32_t* send_pos,
+                   const void* recv_y, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,3 +162,45 @@ def test_entry_point_argument_errors():
     # shared expert pointers given but the params say there is none
     assert L.moe_forward(ctypes.byref(p2), T, F, F, None, F, F, F, F, F, F, None, None, F,
                          moe.moe_workspace_size(p2, T), None) == -1
+
+
+def test_ep_exchange_host_logic():
+    p = _params(wl.WORKLOADS["dsv2"])  # E = 160, k = 6
+    L = moe.lib()
+    pp = ctypes.byref(p)
+    F = FAKE
+    # capacity: every token to min(k, ep_size) ranks
+    assert moe.moe_ep_send_capacity(p, 100, 8) == 600
+    assert moe.moe_ep_send_capacity(p, 100, 4) == 400
+    assert moe.moe_ep_send_capacity(p, 100, 160) == 600
+    assert moe.moe_ep_send_capacity(p, 0, 1) == 0
+    for bad in (0, 3, 320, 257, -1):  # not a divisor of E, or out of range
+        assert L.moe_ep_send_capacity(pp, 100, bad) == -1
+        with pytest.raises(moe.MoeError):
+            moe.moe_ep_workspace_size(p, 100, bad)
+    assert L.moe_ep_send_capacity(pp, -1, 8) == -1
+    sizes = [moe.moe_ep_workspace_size(p, T, 8) for T in (1, 256, 4096, 16384)]
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
+    T = 64
+    ws = moe.moe_ep_workspace_size(p, T, 8)
+    # T = 0 returns before any launch
+    moe.moe_ep_dispatch(p, 0, 8, None, None, None, None, None, None, None, None, None, None,
+                        stream=0)
+    moe.moe_ep_combine(p, 0, None, None, None, stream=0)
+    ok = [F] * 9
+    for i in range(9):  # each required pointer missing
+        args = list(ok)
+        args[i] = None
+        assert L.moe_ep_dispatch(pp, T, 8, *args, F, ws, None) == -1, i
+    args = list(ok)
+    args[2] = F + 2  # x not 16-byte aligned
+    assert L.moe_ep_dispatch(pp, T, 8, *args, F, ws, None) == -1
+    args = list(ok)
+    args[6] = F + 8  # send_x not 16-byte aligned
+    assert L.moe_ep_dispatch(pp, T, 8, *args, F, ws, None) == -1
+    assert L.moe_ep_dispatch(pp, T, 8, *ok, F, ws - 1, None) == -3
+    assert L.moe_ep_dispatch(pp, T, 7, *ok, F, ws, None) == -1
+    assert L.moe_ep_dispatch(pp, -1, 8, *ok, F, ws, None) == -1
+    assert L.moe_ep_combine(pp, T, None, F, F, None) == -1
+    assert L.moe_ep_combine(pp, T, F, F + 2, F, None) == -1
+    assert L.moe_ep_combine(pp, T, F, F, F + 4, None) == -1
