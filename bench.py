@@ -9,7 +9,9 @@ Default workload: the Mixtral-shaped layer (bf16, H 4096, 8 experts of I 14336, 
 renormalised softmax routing, every expert local) at 4096 tokens (prefill); the same
 layer at 32 tokens (decode) is reported in the ``decode`` field of the same line. A step
 is one ``moe_forward`` over the batch (router GEMM, softmax/top-k, align/permute, grouped
-gate/up and down GEMMs, combine); inputs are resident in HBM before timing starts.
+gate/up and down GEMMs, combine); inputs are resident in HBM before timing starts. The
+expert-parallel exchange around the path (dispatch and unpack, at the workload's EP degree)
+is timed on the step's routing and reported in the ``ep_exchange`` field.
 
 The dominant kernel's duration comes from HIP events recorded on the launch stream
 around ``moe_expert_gate_up`` in a second timed loop that runs the same kernels through
@@ -18,6 +20,7 @@ sample of tokens of the same workload as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
                        [--tokens T] [--cpu-sample S | --no-cpu-baseline] [--copy-probe]
+                       [--no-exchange | --exchange-only]
 """
 from __future__ import annotations
 
@@ -81,6 +84,10 @@ def _parse():
                     help="tokens the oracle is timed on (capped at the workload's token count)")
     ap.add_argument("--no-decode", action="store_true", help="skip the small-token-count line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exchange", action="store_true",
+                    help="skip the expert-parallel exchange (dispatch + unpack) measurement")
+    ap.add_argument("--exchange-only", action="store_true",
+                    help="route once, then time only the exchange (for kernel profiles)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -248,6 +255,75 @@ def roofline(alg, stage_ms, bound):
             "avg_ms": round(stage_ms["gate_up"], 4)}
 
 
+def exchange_ep_size(w):
+    """Expert-parallel degree of the exchange measurement: the workload's own, else one expert
+    (Mixtral: eight) per rank, at most eight ranks."""
+    return w.ep_size if w.ep_size > 1 else min(8, w.num_experts)
+
+
+def run_exchange(w, T, ep, x, ids, tw, steps, warmup):
+    """Dispatch and unpack of the expert-parallel exchange on the step's routing, timed with
+    HIP events on the launch stream; algorithmic bytes from the actual send rows."""
+    import numpy as np
+    import torch
+
+    import expert_moe_amd as moe
+    p = moe.make_params(w.num_experts, w.top_k, w.hidden_size, w.intermediate_size, w.renormalize,
+                        w.use_grouped_topk, w.num_expert_group, w.topk_group,
+                        w.routed_scaling_factor, w.num_local_experts, w.shared_intermediate_size,
+                        w.dtype)
+    k, H = w.top_k, w.hidden_size
+    dev, dt = x.device, x.dtype
+    R = max(moe.moe_ep_send_capacity(p, T, ep), 1)
+    send_pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    meta = torch.empty(2 * ep + 2, dtype=torch.int32, device=dev)
+    send_token = torch.empty(R, dtype=torch.int32, device=dev)
+    send_x = torch.empty(R, H, dtype=dt, device=dev)
+    send_local = torch.empty(R, k, dtype=torch.int32, device=dev)
+    send_w = torch.empty(R, k, dtype=torch.float32, device=dev)
+    out = torch.empty(T, H, dtype=dt, device=dev)
+    ws = torch.empty(max(moe.moe_ep_workspace_size(p, T, ep), 1), dtype=torch.uint8, device=dev)
+
+    def dispatch():
+        moe.moe_ep_dispatch(p, T, ep, ids, tw, x, send_pos, meta, send_token, send_x, send_local,
+                            send_w, ws)
+
+    def unpack():  # the returned rows stand in place: send_x plays recv_y
+        moe.moe_ep_combine(p, T, send_pos, send_x, out)
+
+    for _ in range(warmup):
+        dispatch()
+        unpack()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        dispatch()
+        e[1].record()
+        unpack()
+        e[2].record()
+    torch.cuda.synchronize()
+    d_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    c_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    n_send = int(meta[0].item())
+    pos = send_pos.view(T, k).cpu().numpy()
+    senders = int((pos >= 0).any(axis=1).sum())
+    eb = 2 if w.dtype == "bf16" else 4
+    # dispatch: ids/weights in, send_pos out, each sending token's row read once, the send rows
+    # and their metadata written; unpack: send_pos and the returned rows in, the tokens out
+    d_bytes = T * k * 12 + senders * H * eb + n_send * (H * eb + 4 + 8 * k)
+    c_bytes = T * k * 4 + n_send * H * eb + T * H * eb
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    return {"ep_size": ep, "n_send": n_send, "rows_per_token": round(n_send / max(T, 1), 3),
+            "dispatch_ms": round(d_ms, 4), "dispatch_bytes": d_bytes,
+            "dispatch_gbs": round(gbs(d_bytes, d_ms), 1),
+            "dispatch_hbm_frac": round(gbs(d_bytes, d_ms) / PEAK_HBM_GBS, 4),
+            "unpack_ms": round(c_ms, 4), "unpack_bytes": c_bytes,
+            "unpack_gbs": round(gbs(c_bytes, c_ms), 1),
+            "unpack_hbm_frac": round(gbs(c_bytes, c_ms) / PEAK_HBM_GBS, 4),
+            "counts": np.diff(meta[1:ep + 2].cpu().numpy()).tolist()}
+
+
 def cpu_baseline(host, w, sample):
     """The oracle, as it stands, on `sample` tokens of the workload (CPU, float64 MLPs)."""
     import numpy as np
@@ -296,6 +372,14 @@ def main():
     print(f"[bench] generating inputs for {w.key} (T={T})", file=sys.stderr, flush=True)
     host = HostLayer(w, max(T, Td))
     torch.cuda.init()
+    if args.exchange_only:
+        b = Bench(w, T, host)
+        b.forward()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": f"{w.desc}, T={T}",
+                          "ep_exchange": run_exchange(w, T, exchange_ep_size(w), b.d["x"], b.ids,
+                                                      b.tw, args.steps, args.warmup)}))
+        return
     print("[bench] timing", file=sys.stderr, flush=True)
     b, ms, split_ms, stage, alg = run_point(host, w, T, args.steps, args.warmup)
     bound = "mfma" if alg["gate_up_flops"] / max(alg["gate_up_bytes"], 1) > 312 else "hbm"
@@ -323,6 +407,10 @@ def main():
         "split_path_ms_per_step": round(split_ms, 4),
         "work": alg,
     }
+    if not args.no_exchange:
+        print("[bench] timing the expert-parallel exchange", file=sys.stderr, flush=True)
+        res["ep_exchange"] = run_exchange(w, T, exchange_ep_size(w), b.d["x"], b.ids, b.tw,
+                                          max(args.steps, 20), args.warmup)
     del b
     if Td != T and not args.no_decode:
         bd, msd, split_d, stage_d, alg_d = run_point(host, w, Td, max(args.steps, 20), args.warmup)

@@ -9,7 +9,7 @@
 // ride along (the receiving rank applies every one of its experts the token picked, through
 // the k local slots that the send row carries). Ordering and counts come from the alignment
 // passes (keyed by rank instead of local expert, granule 1), so the rows of a rank follow
-// increasing token index without a sort.
+// increasing token index without a sort; the pack then reads each token's hidden row once.
 #include "common.h"
 #include "launch.h"
 
@@ -35,10 +35,11 @@ __global__ void __launch_bounds__(256) ep_owner_rank(const int32_t* __restrict__
   rank_of[i] = r;
 }
 
-// Send row `row` (one workgroup): the token's hidden row, its k routing weights, and its k
-// slots seen from the destination rank (the local expert index there, else -1).
-__global__ void __launch_bounds__(256) ep_pack(const int32_t* __restrict__ sorted_pairs,
-                                               const int32_t* __restrict__ n_send, int k, int E,
+// The send rows of token t (one workgroup per token): its owned slots are compacted in slot
+// order into LDS (k <= 64: one wave's ballot), the hidden row is read once and written to each
+// of them, then each row gets the token's k routing weights and its k slots seen from the
+// row's rank (the local expert index there, else -1).
+__global__ void __launch_bounds__(256) ep_pack(const int32_t* __restrict__ send_pos, int k, int E,
                                                int per, const uint4* __restrict__ x, int row_vec,
                                                const int32_t* __restrict__ ids,
                                                const float* __restrict__ w,
@@ -46,22 +47,40 @@ __global__ void __launch_bounds__(256) ep_pack(const int32_t* __restrict__ sorte
                                                uint4* __restrict__ send_x,
                                                int32_t* __restrict__ send_local,
                                                float* __restrict__ send_w) {
-  const int row = blockIdx.x;
-  if (row >= *n_send) return;
-  const int pair = sorted_pairs[row];
-  const int t = pair / k;
-  const int r = ids[pair] / per;
-  const uint4* src = x + static_cast<int64_t>(t) * row_vec;
-  uint4* dst = send_x + static_cast<int64_t>(row) * row_vec;
-  for (int v = threadIdx.x; v < row_vec; v += 256) dst[v] = src[v];
-  if (threadIdx.x < k) {
+  __shared__ int s_row[64];
+  __shared__ int s_base[64];
+  __shared__ int s_n;
+  const int t = blockIdx.x;
+  const int64_t pbase = static_cast<int64_t>(t) * k;
+  if (threadIdx.x < 64) {
     const int j = threadIdx.x;
-    const int id = ids[static_cast<int64_t>(t) * k + j];
-    const int l = id - r * per;
-    send_local[static_cast<int64_t>(row) * k + j] = (id >= 0 && id < E && l >= 0 && l < per) ? l : -1;
-    send_w[static_cast<int64_t>(row) * k + j] = w[static_cast<int64_t>(t) * k + j];
+    const int row = j < k ? send_pos[pbase + j] : -1;
+    const unsigned long long m = __ballot(row >= 0);
+    if (row >= 0) {
+      const int at = __popcll(m & ((1ull << j) - 1ull));
+      s_row[at] = row;
+      s_base[at] = (ids[pbase + j] / per) * per;  // first global expert of the row's rank
+    }
+    if (j == 0) s_n = __popcll(m);
   }
-  if (threadIdx.x == 0) send_token[row] = t;
+  __syncthreads();
+  const int n = s_n;
+  if (n == 0) return;
+  const uint4* src = x + static_cast<int64_t>(t) * row_vec;
+  for (int v = threadIdx.x; v < row_vec; v += 256) {
+    const uint4 q = src[v];
+    for (int i = 0; i < n; ++i) send_x[static_cast<int64_t>(s_row[i]) * row_vec + v] = q;
+  }
+  for (int e = threadIdx.x; e < n * k; e += 256) {
+    const int i = e / k;
+    const int j = e - i * k;
+    const int64_t o = static_cast<int64_t>(s_row[i]) * k + j;
+    const int id = ids[pbase + j];
+    const int l = id - s_base[i];
+    send_local[o] = (id >= 0 && id < E && l >= 0 && l < per) ? l : -1;
+    send_w[o] = w[pbase + j];
+  }
+  if (threadIdx.x < n) send_token[s_row[threadIdx.x]] = t;
 }
 
 }  // namespace
@@ -83,11 +102,10 @@ int launch_ep_dispatch(const moe_params& p, int T, int ep_size, const int32_t* i
   int rc = launch_align(pr, T, ws.rank_of, 1, ws.sorted_pairs, nullptr, send_pos, rank_meta,
                         rank_meta, ws.chunk, s);
   if (rc) return rc;
-  const int rows = T * (k < ep_size ? k : ep_size);
   const int elt = p.dtype == MOE_F32 ? 4 : 2;
-  ep_pack<<<rows, 256, 0, s>>>(ws.sorted_pairs, rank_meta, k, E, per, static_cast<const uint4*>(x),
-                               p.hidden_size * elt / 16, ids, w, send_token,
-                               static_cast<uint4*>(send_x), send_local, send_w);
+  ep_pack<<<T, 256, 0, s>>>(send_pos, k, E, per, static_cast<const uint4*>(x),
+                            p.hidden_size * elt / 16, ids, w, send_token,
+                            static_cast<uint4*>(send_x), send_local, send_w);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
