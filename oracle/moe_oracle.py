@@ -23,6 +23,10 @@ What it computes is the plain definition of the MoE layer as the pages give it:
   experts that the fused layer adds itself.
 * "Expert Parallel" (vllm-omni design doc), Step 5 forward: the shared expert output is
   added to the routed output on every rank.
+* "vllm.model_executor.models.transformers.moe", ``update_physical_experts_metadata`` and
+  the EPLB settings of ``recursive_replace``: E logical experts are served by
+  E + num_redundant_experts physical ones, each rank holding an equal contiguous share of
+  the physical experts, and the expert map is rebuilt over physical experts.
 
 Precision. Router logits are the fp32 rounding of the exact (fp64-accumulated) dot
 products; softmax, top-k selection and routing weights are fp32, because the pages run
@@ -52,6 +56,7 @@ __all__ = [
     "gated_mlp", "moe_forward_given_routing", "moe_forward", "moe_forward_per_token",
     "align_permute", "weight_bytes",
     "ep_dispatch", "ep_pack", "ep_combine",
+    "eplb_tables", "eplb_local_slots", "moe_forward_given_slots",
 ]
 
 
@@ -370,4 +375,72 @@ def ep_combine(plan, recv_y, top_k):
     for j in range(top_k):
         sel = pos[:, j] >= 0
         out[sel] += recv[pos[sel, j]]
+    return out
+
+
+def eplb_tables(physical_to_logical, num_logical):
+    """Replica tables of a physical placement (expert-parallel load balancing).
+
+    ``update_physical_experts_metadata`` / ``recursive_replace`` (transformers MoE page):
+    the layer has ``num_physical = num_logical + num_redundant`` physical experts, rank r
+    holding physical ids ``[r * P_l, (r + 1) * P_l)``. ``physical_to_logical[q]`` is the
+    logical expert whose weights physical expert q holds. Returns
+    ``logical_to_physical`` [E, max_replicas] (the physical ids holding logical e in
+    increasing order, -1 after the last) and ``replica_count`` [E].
+    """
+    p2l = np.asarray(physical_to_logical, np.int64)
+    reps = [[int(q) for q in np.nonzero(p2l == e)[0]] for e in range(num_logical)]
+    if any(len(r) == 0 for r in reps):
+        raise ValueError("every logical expert needs a replica")
+    width = max(len(r) for r in reps)
+    l2p = np.full((num_logical, width), -1, np.int32)
+    for e, r in enumerate(reps):
+        l2p[e, :len(r)] = r
+    return l2p, np.array([len(r) for r in reps], np.int32)
+
+
+def eplb_local_slots(topk_ids, top_k, logical_to_physical, replica_count, phys_expert_map):
+    """Local slot of every (token, slot) pair under a replicated placement.
+
+    The pages name the redundant experts but give no rule for splitting a logical expert's
+    tokens among its replicas; the reading here is round robin by token index: token t's
+    pair with logical expert e goes to replica ``t mod replica_count[e]`` (deterministic,
+    and an even split over consecutive tokens). That physical expert's entry of the share's
+    physical expert map gives the local slot (-1 when another rank holds it).
+    """
+    ids = np.asarray(topk_ids, np.int64).reshape(-1, top_k)
+    T = ids.shape[0]
+    cnt = np.asarray(replica_count, np.int64)
+    l2p = np.asarray(logical_to_physical, np.int64)
+    pmap = np.asarray(phys_expert_map, np.int64)
+    out = np.full(ids.shape, -1, np.int32)
+    for t in range(T):
+        for j in range(top_k):
+            e = ids[t, j]
+            q = l2p[e, t % cnt[e]]
+            out[t, j] = pmap[q]
+    return out
+
+
+def moe_forward_given_slots(x, slots, weights, w13_local, w2_local, shared_w13=None,
+                            shared_w2=None):
+    """One share's output [T, H] (fp64) given each pair's local slot (-1: not this share).
+
+    The same sum as ``moe_forward_given_routing`` with the slot of each pair given directly
+    (a replicated placement picks the slot per token, not per logical expert).
+    """
+    x64 = np.asarray(x, np.float64)
+    T, H = x64.shape
+    sl = np.asarray(slots)
+    wts = np.asarray(weights, np.float64)
+    out = np.zeros((T, H), np.float64)
+    for s in range(int(sl.max(initial=-1)) + 1):
+        hit = sl == s
+        rows = np.nonzero(hit.any(axis=1))[0]
+        if rows.size == 0:
+            continue
+        w_tok = (wts * hit).sum(axis=1)
+        out[rows] += w_tok[rows, None] * gated_mlp(x64[rows], w13_local[s], w2_local[s])
+    if shared_w13 is not None:
+        out += gated_mlp(x64, shared_w13, shared_w2)
     return out

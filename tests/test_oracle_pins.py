@@ -437,3 +437,96 @@ def test_ep_exchange_reconstructs_layer(R):
     got = oracle.ep_combine(plan, recv, k)
     want = oracle.moe_forward_given_routing(x, ids, w.astype(np.float32), np.arange(E), w13, w2)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- EPLB (replicated experts)
+def test_eplb_tables_hand_example():
+    """8 physical experts serving 4 logical ones (placement worked by hand)."""
+    l2p, cnt = oracle.eplb_tables([0, 1, 2, 3, 0, 2, 0, 1], 4)
+    assert l2p.tolist() == [[0, 4, 6], [1, 7, -1], [2, 5, -1], [3, -1, -1]]
+    assert cnt.tolist() == [3, 2, 2, 1]
+    with pytest.raises(ValueError):
+        oracle.eplb_tables([0, 1, 1, 0], 3)  # logical expert 2 has no replica
+
+
+def test_eplb_local_slots_hand_example():
+    """Round robin by token index over the replicas, worked by hand for two ranks of 4
+    physical experts (rank 0: logical 0 1 2 3; rank 1: logical 0 2 0 1)."""
+    l2p, cnt = oracle.eplb_tables([0, 1, 2, 3, 0, 2, 0, 1], 4)
+    ids = np.array([[0, 3], [0, 1], [2, 0], [1, 2]])
+    r0 = np.array([0, 1, 2, 3, -1, -1, -1, -1])
+    r1 = np.array([-1, -1, -1, -1, 0, 1, 2, 3])
+    assert oracle.eplb_local_slots(ids, 2, l2p, cnt, r0).tolist() == \
+        [[0, 3], [-1, -1], [2, -1], [-1, -1]]
+    assert oracle.eplb_local_slots(ids, 2, l2p, cnt, r1).tolist() == \
+        [[-1, -1], [0, 3], [-1, 2], [3, 1]]
+
+
+def test_eplb_identity_placement_is_the_plain_map():
+    """No redundant experts and the identity placement: the slots are expert_map[ids]."""
+    E, k, T = 16, 4, 50
+    ids = _distinct_ids(T, k, E, 21)
+    l2p, cnt = oracle.eplb_tables(np.arange(E), E)
+    for R, r in [(1, 0), (4, 1), (4, 3), (16, 5)]:
+        per = E // R
+        emap = np.full(E, -1)
+        emap[r * per:(r + 1) * per] = np.arange(per)
+        assert np.array_equal(oracle.eplb_local_slots(ids, k, l2p, cnt, emap), emap[ids])
+
+
+def test_eplb_split_is_even_over_consecutive_tokens():
+    """Consecutive tokens that all pick one logical expert are spread over its replicas with
+    counts that differ by at most one."""
+    l2p, cnt = oracle.eplb_tables([0, 1, 0, 0, 1, 2, 0, 2, 3], 4)  # logical 0: 4 replicas
+    T = 103
+    ids = np.zeros((T, 1), np.int64)
+    pmap = np.arange(9)  # one rank holds all physical experts; slot = physical id
+    slots = oracle.eplb_local_slots(ids, 1, l2p, cnt, pmap).ravel()
+    per_rep = np.bincount(slots, minlength=9)[[0, 2, 3, 6]]
+    assert per_rep.sum() == T and per_rep.max() - per_rep.min() <= 1
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+def test_eplb_share_sum_equals_all_local(R):
+    """Every pair lands on exactly one replica, whose weights are its logical expert's: the
+    shares of a replicated placement sum to the all-local layer."""
+    E, H, I, T, k = 8, 24, 16, 23, 3
+    x, _, w13, w2, sw13, sw2 = _tiny_layer(E=E, H=H, I=I, T=T, seed=5, shared_I=8)
+    ids = _distinct_ids(T, k, E, 9)
+    w = np.random.default_rng(10).uniform(0.1, 1.0, (T, k))
+    p2l = np.concatenate([np.arange(E), [0, 0, 3, 5]])  # 12 physical experts
+    rng = np.random.default_rng(11)
+    p2l = p2l[rng.permutation(p2l.size)]
+    P = p2l.size
+    l2p, cnt = oracle.eplb_tables(p2l, E)
+    per = P // R
+    total = np.zeros((T, H))
+    for r in range(R):
+        pmap = np.full(P, -1)
+        pmap[r * per:(r + 1) * per] = np.arange(per)
+        slots = oracle.eplb_local_slots(ids, k, l2p, cnt, pmap)
+        mine = p2l[r * per:(r + 1) * per]
+        sh = (sw13, sw2) if r == 0 else (None, None)
+        total += oracle.moe_forward_given_slots(x, slots, w, w13[mine], w2[mine], *sh)
+    want = oracle.moe_forward_given_routing(x, ids, w, np.arange(E), w13, w2, sw13, sw2)
+    assert np.allclose(total, want, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_given_slots_matches_per_expert_form():
+    """With the slots of a plain expert map, the slot form is the per-expert loop."""
+    E, H, I, T, k = 8, 24, 16, 13, 2
+    x, _, w13, w2, _, _ = _tiny_layer(E=E, H=H, I=I, T=T, seed=6)
+    ids = _distinct_ids(T, k, E, 12)
+    w = np.random.default_rng(13).uniform(0.1, 1.0, (T, k))
+    emap = np.array([-1, 0, -1, 1, 2, -1, 3, -1])
+    loc = [1, 3, 4, 6]
+    got = oracle.moe_forward_given_slots(x, emap[ids], w, w13[loc], w2[loc])
+    want = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            s = emap[ids[t, j]]
+            if s >= 0:
+                h = w13[loc[s]] @ x[t]
+                a = h[:I] / (1 + np.exp(-h[:I])) * h[I:]
+                want[t] += w[t, j] * (w2[loc[s]] @ a)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
