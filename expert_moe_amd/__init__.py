@@ -28,6 +28,7 @@ EXPORTS = (
     "moe_align_permute", "moe_grouped_mlp", "moe_expert_gate_up", "moe_expert_down",
     "moe_shared_mlp", "moe_combine", "moe_forward",
     "moe_ep_send_capacity", "moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_combine",
+    "moe_eplb_tables", "moe_route_eplb", "moe_forward_eplb",
 )
 
 
@@ -53,6 +54,25 @@ class moe_params(ctypes.Structure):
         ("shared_intermediate_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class moe_eplb(ctypes.Structure):
+    """Mirror of ``struct moe_eplb`` in include/moe.h (device table pointers as integers)."""
+    _fields_ = [
+        ("num_physical_experts", ctypes.c_int32),
+        ("max_replicas", ctypes.c_int32),
+        ("logical_to_physical", ctypes.c_void_p),
+        ("replica_count", ctypes.c_void_p),
+    ]
+
+
+def make_eplb(num_physical_experts, max_replicas, logical_to_physical, replica_count):
+    """A ``moe_eplb`` over device tables (tensors or raw addresses). The returned struct holds
+    references to tensor arguments, so they live as long as it does."""
+    e = moe_eplb(num_physical_experts, max_replicas, _ptr(logical_to_physical),
+                 _ptr(replica_count))
+    e._tables = (logical_to_physical, replica_count)
+    return e
 
 
 def make_params(num_experts, top_k, hidden_size, intermediate_size, renormalize=True,
@@ -94,6 +114,11 @@ _SIGS = {
     "moe_ep_dispatch": ([_P, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                         ctypes.c_int),
     "moe_ep_combine": ([_P, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_eplb_tables": ([_i32, _i32, _vp, _i32, _vp, _vp], ctypes.c_int),
+    "moe_route_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                       ctypes.c_int),
+    "moe_forward_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -265,3 +290,35 @@ def moe_ep_dispatch(p, num_tokens, ep_size, topk_ids, topk_w, x, send_pos, rank_
 def moe_ep_combine(p, num_tokens, send_pos, recv_y, out, stream=None):
     _check(lib().moe_ep_combine(ctypes.byref(p), num_tokens, _ptr(send_pos), _ptr(recv_y), _ptr(out),
                                 _stream(stream)), "moe_ep_combine")
+
+
+def moe_eplb_tables(num_logical: int, physical_to_logical, max_replicas: int | None = None):
+    """Host helper: (logical_to_physical [E, max_replicas], replica_count [E]) as numpy int32."""
+    import numpy as np
+    p2l = np.ascontiguousarray(np.asarray(physical_to_logical, np.int32))
+    if max_replicas is None:
+        max_replicas = int(np.bincount(p2l[p2l >= 0], minlength=1).max()) if p2l.size else 1
+    l2p = np.empty((max(num_logical, 1), max(max_replicas, 1)), np.int32)
+    cnt = np.empty(max(num_logical, 1), np.int32)
+    _check(lib().moe_eplb_tables(num_logical, p2l.size, p2l.ctypes.data, max_replicas,
+                                 l2p.ctypes.data, cnt.ctypes.data), "moe_eplb_tables")
+    return l2p, cnt
+
+
+def moe_route_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
+                   topk_local, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_route_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
+                                _ptr(w_gate), _ptr(logit_bias), _ptr(expert_map), _ptr(topk_ids),
+                                _ptr(topk_w), _ptr(topk_local), wp, wn, _stream(stream)),
+           "moe_route_eplb")
+
+
+def moe_forward_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
+                     shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_forward_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
+                                  _ptr(w_gate), _ptr(logit_bias), _ptr(expert_map), _ptr(w13),
+                                  _ptr(w2), _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
+                                  _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
+           "moe_forward_eplb")

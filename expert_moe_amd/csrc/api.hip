@@ -13,6 +13,7 @@ namespace {
 using moe::align_chunks;
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxPhysical = 4096;  // physical experts of a replicated placement
 
 inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -35,7 +36,9 @@ int check_params(const moe_params* p) {
     if (G > 64) return MOE_EUNSUPPORTED;
   }
   if (!isfinite(p->routed_scaling_factor)) return MOE_EINVAL;
-  if (p->num_local_experts < 1 || p->num_local_experts > E) return MOE_EINVAL;
+  // a share may hold more slots than there are logical experts (replicas of a placement)
+  if (p->num_local_experts < 1) return MOE_EINVAL;
+  if (p->num_local_experts > 256) return MOE_EUNSUPPORTED;
   if (p->shared_intermediate_size < 0) return MOE_EINVAL;
   if (p->shared_intermediate_size > 0 && !mult64(p->shared_intermediate_size)) return MOE_EINVAL;
   if (E > 256 || p->top_k > 64) return MOE_EUNSUPPORTED;
@@ -228,9 +231,11 @@ int64_t moe_weight_bytes(int64_t n_experts, int64_t hidden, int64_t inter, int32
   return n_experts * (2 * inter * hidden + hidden * inter) * dtype_bytes * layers;
 }
 
-int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
-              const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
-              float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
+// moe_route with an optional replicated placement (eplb = NULL: the expert map is by expert id)
+static int route_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num_tokens,
+                      const void* x, const void* w_gate, const float* logit_bias,
+                      const int32_t* expert_map, int32_t* topk_ids, float* topk_w,
+                      int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
@@ -243,7 +248,14 @@ int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void
   float* logits = static_cast<float*>(ws);
   if ((rc = moe::launch_router_logits(*p, T, x, w_gate, logits, as_stream(stream)))) return rc;
   return moe::launch_topk(*p, T, logits, logit_bias, expert_map, topk_ids, topk_w, topk_local,
-                          as_stream(stream));
+                          as_stream(stream), eplb);
+}
+
+int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+              const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
+              float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
+  return route_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
+                    topk_local, ws, ws_bytes, stream);
 }
 
 int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* topk_local,
@@ -346,11 +358,13 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
                              as_stream(stream));
 }
 
-int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
-                const float* logit_bias, const int32_t* expert_map, const void* w13,
-                const void* w2, const void* shared_w13, const void* shared_w2, void* out,
-                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                void* stream) {
+// moe_forward with an optional replicated placement (eplb = NULL: the expert map is by expert id)
+static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num_tokens,
+                        const void* x, const void* w_gate, const float* logit_bias,
+                        const int32_t* expert_map, const void* w13, const void* w2,
+                        const void* shared_w13, const void* shared_w2, void* out,
+                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                        void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
@@ -403,7 +417,7 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
 
   if ((rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s))) return rc;
   if ((rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, expert_map, ids, tw,
-                             local, s)))
+                             local, s, eplb)))
     return rc;
   if ((rc = moe::launch_align(*p, T, local, bm, sorted_pairs, block_expert, pair_row, num_padded,
                               at<int32_t>(ws, L.meta), at<int32_t>(ws, L.chunk), s)))
@@ -418,6 +432,80 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
     return rc;
   }
   return moe::launch_combine(*p, T, y, pair_row, tw, shared_y, out, s);
+}
+
+int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+                const float* logit_bias, const int32_t* expert_map, const void* w13,
+                const void* w2, const void* shared_w13, const void* shared_w2, void* out,
+                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  return forward_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2,
+                      shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ replicated experts
+
+namespace {
+
+int check_eplb(const moe_params* p, const moe_eplb* e, moe::EplbMap* out) {
+  if (!p || !e) return MOE_EINVAL;
+  if (e->num_physical_experts < p->num_experts || e->num_physical_experts > kMaxPhysical)
+    return MOE_EINVAL;
+  if (e->max_replicas < 1 || e->max_replicas > e->num_physical_experts) return MOE_EINVAL;
+  if (!e->logical_to_physical || !e->replica_count) return MOE_EINVAL;
+  out->l2p = e->logical_to_physical;
+  out->cnt = e->replica_count;
+  out->max_rep = e->max_replicas;
+  out->P = e->num_physical_experts;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_eplb_tables(int32_t num_logical, int32_t num_physical, const int32_t* physical_to_logical,
+                    int32_t max_replicas, int32_t* logical_to_physical, int32_t* replica_count) {
+  if (num_logical < 1 || num_physical < num_logical || num_physical > kMaxPhysical ||
+      max_replicas < 1 || !physical_to_logical || !logical_to_physical || !replica_count)
+    return MOE_EINVAL;
+  for (int e = 0; e < num_logical; ++e) replica_count[e] = 0;
+  for (int64_t i = 0; i < static_cast<int64_t>(num_logical) * max_replicas; ++i)
+    logical_to_physical[i] = -1;
+  for (int q = 0; q < num_physical; ++q) {
+    const int e = physical_to_logical[q];
+    if (e < 0 || e >= num_logical) return MOE_EINVAL;
+    if (replica_count[e] == max_replicas) return MOE_EINVAL;
+    logical_to_physical[static_cast<int64_t>(e) * max_replicas + replica_count[e]++] = q;
+  }
+  for (int e = 0; e < num_logical; ++e)
+    if (replica_count[e] == 0) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
+                   const void* w_gate, const float* logit_bias, const int32_t* expert_map,
+                   int32_t* topk_ids, float* topk_w, int32_t* topk_local, void* ws,
+                   size_t ws_bytes, void* stream) {
+  moe::EplbMap m;
+  int rc = check_eplb(p, eplb, &m);
+  if (rc) return rc;
+  return route_impl(p, &m, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
+                    topk_local, ws, ws_bytes, stream);
+}
+
+int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
+                     const void* w_gate, const float* logit_bias, const int32_t* expert_map,
+                     const void* w13, const void* w2, const void* shared_w13,
+                     const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  moe::EplbMap m;
+  int rc = check_eplb(p, eplb, &m);
+  if (rc) return rc;
+  return forward_impl(p, &m, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
+                      shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -23,10 +23,21 @@ int router_splits(const moe_params& p, int T);
 int launch_router_logits(const moe_params& p, int T, const void* x, const void* w_gate,
                          float* logits, hipStream_t s);
 
+// Replicated experts: logical expert e is served by the physical experts
+// l2p[e * max_rep + i], i < cnt[e]; the expert map is then indexed by physical id (P entries).
+struct EplbMap {
+  const int32_t* l2p;
+  const int32_t* cnt;
+  int max_rep;
+  int P;
+};
+
 // Sum of the logit partials (written back into partial 0), fp32 softmax, (grouped) top-k,
-// renormalise, scale, expert_map lookup.
+// renormalise, scale, expert_map lookup (through the replica of token t, t mod cnt[e], when
+// eplb is given).
 int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
-                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s);
+                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s,
+                const EplbMap* eplb = nullptr);
 
 // Count / scan / scatter of the (token, slot) pairs by local expert (block_expert may be NULL).
 // meta: [num_padded(1) | offsets(E_l+1) | counts(E_l)], chunk: [align_chunks(T) * E_l].

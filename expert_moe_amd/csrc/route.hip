@@ -24,6 +24,9 @@ struct TopkArgs {
   int splits;
   const float* bias;
   const int32_t* emap;
+  const int32_t* l2p;  // replicated experts: [E, max_rep] physical ids, or NULL
+  const int32_t* cnt;  // [E] replica counts
+  int max_rep, P;
   int32_t* ids;
   float* w;
   int32_t* local;
@@ -196,7 +199,17 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     const int64_t o = static_cast<int64_t>(t) * a.k + lane;
     a.ids[o] = my_id;
     a.w[o] = w;
-    int s = a.emap[my_id];
+    int s = -1;
+    if (a.l2p == nullptr) {
+      s = a.emap[my_id];
+    } else {
+      // replica t mod cnt of the logical expert (entries outside the tables' ranges: not local)
+      const int c = a.cnt[my_id];
+      if (c >= 1 && c <= a.max_rep) {
+        const int q = a.l2p[static_cast<int64_t>(my_id) * a.max_rep + t % c];
+        if (q >= 0 && q < a.P) s = a.emap[q];
+      }
+    }
     a.local[o] = (s >= 0 && s < a.E_l) ? s : -1;
   }
 }
@@ -260,12 +273,17 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
 }
 
 int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
-                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s) {
+                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s,
+                const EplbMap* eplb) {
   TopkArgs a;
   a.logits = logits;
   a.splits = router_splits(p, T);
   a.bias = bias;
   a.emap = expert_map;
+  a.l2p = eplb ? eplb->l2p : nullptr;
+  a.cnt = eplb ? eplb->cnt : nullptr;
+  a.max_rep = eplb ? eplb->max_rep : 0;
+  a.P = eplb ? eplb->P : 0;
   a.ids = ids;
   a.w = w;
   a.local = local;

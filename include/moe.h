@@ -73,7 +73,8 @@ extern "C" {
  *                            A group's score is its largest probability.
  *  routed_scaling_factor     multiplies the routing weights after renormalisation
  *                            (1.0 = off); never applied to the shared expert.
- *  num_local_experts         E_l, number of local slots (1..E).
+ *  num_local_experts         E_l, number of local slots (1..256; more than E only for a
+ *                            replicated placement, see moe_eplb; above 256: MOE_EUNSUPPORTED).
  *  shared_intermediate_size  I_s of the shared expert MLP (n_shared * I), 0 = none,
  *                            multiple of 64 otherwise.
  *  dtype                     MOE_F32 or MOE_BF16 (x, weights, y, out).
@@ -247,6 +248,63 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
                 const void* w2, const void* shared_w13, const void* shared_w2, void* out,
                 int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* ------------------------------------------------------------------ replicated experts */
+/*
+ * Expert-parallel load balancing ("vllm.model_executor.models.transformers.moe",
+ * update_physical_experts_metadata and the EPLB settings of recursive_replace): E logical
+ * experts are served by P = E + num_redundant_experts physical experts, each rank holding
+ * an equal contiguous share of the physical ids, and the expert map is rebuilt over physical
+ * experts. The pages give no rule for splitting a logical expert's tokens among its
+ * replicas; here token t's pair with logical expert e goes to replica (t mod
+ * replica_count[e]) of e, so consecutive tokens spread evenly over the replicas.
+ *  num_physical_experts  P, num_experts <= P <= 4096; expert_map then has P entries
+ *                        (local slot of each physical expert on this share, -1 elsewhere);
+ *                        p->num_local_experts counts the share's physical experts.
+ *  max_replicas          row length of logical_to_physical, 1..P.
+ *  logical_to_physical   device int32 [E, max_replicas]: physical ids of logical e's replicas
+ *                        in entries 0 .. replica_count[e]-1.
+ *  replica_count         device int32 [E], 1..max_replicas.
+ * Table entries outside those ranges make the pair non-local (no out-of-range access).
+ * The tables are only read; the caller owns them.
+ */
+typedef struct moe_eplb {
+  int32_t num_physical_experts;
+  int32_t max_replicas;
+  const int32_t* logical_to_physical;
+  const int32_t* replica_count;
+} moe_eplb;
+
+/*
+ * Host helper: the replica tables of a placement. physical_to_logical (host [P]) names the
+ * logical expert each physical expert holds; writes logical_to_physical (host
+ * [E * max_replicas], replicas in increasing physical id, -1 after the last) and
+ * replica_count (host [E]). MOE_EINVAL when an id is out of range, a logical expert has no
+ * replica or more than max_replicas.
+ */
+int moe_eplb_tables(int32_t num_logical, int32_t num_physical, const int32_t* physical_to_logical,
+                    int32_t max_replicas, int32_t* logical_to_physical, int32_t* replica_count);
+
+/*
+ * moe_route with a replicated placement: topk_ids are the logical experts the router picked
+ * (as moe_route), topk_local the local slot of the replica each pair goes to. Arguments and
+ * errors as moe_route; eplb as above (MOE_EINVAL when it breaks the rules above).
+ */
+int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
+                   const void* w_gate, const float* logit_bias, const int32_t* expert_map,
+                   int32_t* topk_ids, float* topk_w, int32_t* topk_local, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward with a replicated placement: w13 / w2 hold the share's physical experts (slot s
+ * = local physical expert s, a copy of its logical expert's weights). Arguments, workspace
+ * and errors as moe_forward.
+ */
+int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
+                     const void* w_gate, const float* logit_bias, const int32_t* expert_map,
+                     const void* w13, const void* w2, const void* shared_w13,
+                     const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ expert-parallel exchange */
 /*

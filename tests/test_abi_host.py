@@ -72,7 +72,7 @@ def test_param_errors():
     cases = [
         (dict(top_k=0), E), (dict(top_k=161), E), (dict(hidden_size=100), E),
         (dict(intermediate_size=0), E), (dict(renormalize=True, num_local_experts=0), E),
-        (dict(num_local_experts=161), E), (dict(num_expert_group=7), E),
+        (dict(num_local_experts=257), moe.MOE_EUNSUPPORTED), (dict(num_expert_group=7), E),
         (dict(topk_group=9), E), (dict(topk_group=0), E), (dict(top_k=61, topk_group=3), E),
         (dict(shared_intermediate_size=100), E),
         (dict(routed_scaling_factor=float("inf")), E),
@@ -204,3 +204,44 @@ def test_ep_exchange_host_logic():
     assert L.moe_ep_combine(pp, T, None, F, F, None) == -1
     assert L.moe_ep_combine(pp, T, F, F + 2, F, None) == -1
     assert L.moe_ep_combine(pp, T, F, F, F + 4, None) == -1
+
+
+def test_eplb_tables_and_argument_errors():
+    import oracle
+    # tables: the host helper agrees with the oracle on a shuffled placement
+    rng = np.random.default_rng(3)
+    p2l = np.concatenate([np.arange(16), [0, 0, 5, 9, 9, 9]]).astype(np.int32)
+    p2l = p2l[rng.permutation(p2l.size)]
+    l2p, cnt = moe.moe_eplb_tables(16, p2l)
+    w_l2p, w_cnt = oracle.eplb_tables(p2l, 16)
+    assert np.array_equal(cnt, w_cnt) and np.array_equal(l2p, w_l2p)
+    for bad_p2l, E in [([0, 1, 1], 3), ([0, 1, 3], 3), ([0, -1, 1], 3), ([0, 1], 3)]:
+        with pytest.raises(moe.MoeError):
+            moe.moe_eplb_tables(E, bad_p2l)
+    with pytest.raises(moe.MoeError):  # logical 0 has 3 replicas, max_replicas 2
+        moe.moe_eplb_tables(2, [0, 0, 0, 1], max_replicas=2)
+    # entry points: invalid placements are rejected on the host, T = 0 is a no-op
+    w = wl.WORKLOADS["ep_share"]  # E = 256
+    p = _params(w)
+    L = moe.lib()
+    F = FAKE
+    T = 32
+    ws = moe.moe_workspace_size(p, T)
+    good = moe.moe_eplb(264, 2, F, F)
+    for e in [moe.moe_eplb(255, 2, F, F), moe.moe_eplb(4097, 2, F, F), moe.moe_eplb(264, 0, F, F),
+              moe.moe_eplb(264, 265, F, F), moe.moe_eplb(264, 2, None, F),
+              moe.moe_eplb(264, 2, F, None)]:
+        assert L.moe_route_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, F, F, F, F, F,
+                                ws, None) == -1
+        assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, F, F, F, None,
+                                  None, F, None, None, F, ws, None) == -1
+    assert L.moe_route_eplb(ctypes.byref(p), None, T, F, F, None, F, F, F, F, F, ws, None) == -1
+    assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(good), T, F, F, None, F, F, F, None,
+                              None, F, None, None, F, ws - 1, None) == -3
+    moe.moe_route_eplb(p, good, 0, None, None, None, None, None, None, None, None, stream=0)
+    moe.moe_forward_eplb(p, good, 0, None, None, None, None, None, None, None, None, None, None,
+                         None, None, stream=0)
+    # a share of a replicated placement may hold more slots than there are logical experts
+    p2 = _params(wl.WORKLOADS["tiny"], num_local_experts=12)
+    assert moe.moe_check_params(p2) == moe.MOE_OK
+    assert moe.moe_workspace_size(p2, 64) > 0

@@ -248,3 +248,32 @@ def shared_weights(w: Workload):
     w2 = np.empty((H, I), _storage(w))
     _fill_mlp(w, 4, 0, I, w13, w2)
     return w13, w2
+
+
+def eplb_placement(loads, num_physical: int, ep_size: int) -> np.ndarray:
+    """A replicated placement for given per-expert loads (an input of the layer, like the
+    expert map): physical_to_logical [num_physical], rank r holding ids r*P_l .. (r+1)*P_l-1.
+
+    Greedy: each redundant replica goes to the expert with the most load per replica; then
+    the replicas, heaviest first, go to the least-loaded rank with a free slot that does not
+    already hold that expert (if any such rank exists).
+    """
+    loads = np.asarray(loads, np.float64)
+    E = loads.shape[0]
+    if num_physical < E or num_physical % ep_size:
+        raise ValueError("num_physical must be >= E and divisible by ep_size")
+    reps = np.ones(E, np.int64)
+    for _ in range(num_physical - E):
+        reps[int(np.argmax(loads / reps))] += 1
+    items = sorted(((loads[e] / reps[e], e) for e in range(E) for _ in range(reps[e])),
+                   key=lambda it: (-it[0], it[1]))
+    per = num_physical // ep_size
+    slots = [[] for _ in range(ep_size)]
+    total = np.zeros(ep_size)
+    for ld, e in items:
+        free = [r for r in range(ep_size) if len(slots[r]) < per]
+        fresh = [r for r in free if e not in slots[r]] or free
+        r = min(fresh, key=lambda q: (total[q], q))
+        slots[r].append(e)
+        total[r] += ld
+    return np.array([e for r in range(ep_size) for e in slots[r]], np.int32)
