@@ -20,7 +20,7 @@ sample of tokens of the same workload as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
                        [--tokens T] [--cpu-sample S | --no-cpu-baseline] [--copy-probe]
-                       [--no-exchange | --exchange-only]
+                       [--no-exchange | --exchange-only | --eplb R]
 """
 from __future__ import annotations
 
@@ -88,6 +88,9 @@ def _parse():
                     help="skip the expert-parallel exchange (dispatch + unpack) measurement")
     ap.add_argument("--exchange-only", action="store_true",
                     help="route once, then time only the exchange (for kernel profiles)")
+    ap.add_argument("--eplb", type=int, default=0, metavar="R",
+                    help="only: per-rank layer times of the workload's EP group, plain shares "
+                         "and with R redundant replicated experts")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -324,6 +327,98 @@ def run_exchange(w, T, ep, x, ids, tw, steps, warmup):
             "counts": np.diff(meta[1:ep + 2].cpu().numpy()).tolist()}
 
 
+def run_eplb(host, w, T, extra, steps, warmup):
+    """Load balance of an expert-parallel group with and without replicated experts.
+
+    Every rank's share of the routed experts (no shared expert) runs in turn on all T tokens,
+    first with the plain contiguous shares, then with `extra` redundant replicas placed from
+    the step's own expert loads; the group's step time is the slowest rank's."""
+    import numpy as np
+    import torch
+
+    import expert_moe_amd as moe
+    import workloads as wl
+    ep, E, k, H = w.ep_size, w.num_experts, w.top_k, w.hidden_size
+    dev = "cuda"
+    x = _dev(host.x[:T])
+    gate = _dev(host.gate)
+    bias = _dev(host.bias)
+    dt = x.dtype
+    out = torch.empty(T, H, dtype=dt, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    cache = {}
+
+    def expert(e):  # device weights of logical expert e (drawn once)
+        if e not in cache:
+            a, b = wl.expert_weights(w, e)
+            cache[e] = (_dev(a), _dev(b))
+        return cache[e]
+
+    def time_share(p, emap, w13, w2, eplb=None):
+        ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
+
+        def call():
+            if eplb is None:
+                moe.moe_forward(p, T, x, gate, bias, emap, w13, w2, None, None, out, ids, tw, ws)
+            else:
+                moe.moe_forward_eplb(p, eplb, T, x, gate, bias, emap, w13, w2, None, None, out,
+                                     ids, tw, ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def params(n_local):
+        return moe.make_params(E, k, H, w.intermediate_size, w.renormalize, w.use_grouped_topk,
+                               w.num_expert_group, w.topk_group, w.routed_scaling_factor, n_local,
+                               0, w.dtype)
+
+    per = E // ep
+    plain_ms, plain_pairs = [], []
+    for r in range(ep):
+        emap = torch.from_numpy(moe.moe_make_expert_map(E, ep, r)).to(dev)
+        w13 = torch.stack([expert(e)[0] for e in range(r * per, (r + 1) * per)])
+        w2 = torch.stack([expert(e)[1] for e in range(r * per, (r + 1) * per)])
+        plain_ms.append(time_share(params(per), emap, w13, w2))
+        del w13, w2
+    ids_h = ids.cpu().numpy()
+    loads = np.bincount(ids_h.ravel(), minlength=E)
+    plain_pairs = [int(loads[r * per:(r + 1) * per].sum()) for r in range(ep)]
+    P = E + extra
+    p2l = wl.eplb_placement(loads + 1.0, P, ep)
+    l2p, cnt = moe.moe_eplb_tables(E, p2l)
+    eplb = moe.make_eplb(P, l2p.shape[1], torch.from_numpy(l2p).to(dev),
+                         torch.from_numpy(cnt).to(dev))
+    pp = P // ep
+    eplb_ms, eplb_pairs = [], []
+    for r in range(ep):
+        pmap = np.full(P, -1, np.int32)
+        pmap[r * pp:(r + 1) * pp] = np.arange(pp)
+        w13 = torch.stack([expert(int(e))[0] for e in p2l[r * pp:(r + 1) * pp]])
+        w2 = torch.stack([expert(int(e))[1] for e in p2l[r * pp:(r + 1) * pp]])
+        eplb_ms.append(time_share(params(pp), torch.from_numpy(pmap).to(dev), w13, w2, eplb))
+        # pairs that landed on this rank (replica t mod count of each pair's logical expert)
+        t = np.arange(T)[:, None]
+        phys = l2p[ids_h, t % cnt[ids_h]]
+        eplb_pairs.append(int(((phys >= r * pp) & (phys < (r + 1) * pp)).sum()))
+        del w13, w2
+    return {"ep_size": ep, "redundant_experts": extra, "physical_experts": P,
+            "placement": p2l.tolist(),
+            "rank_ms_plain": [round(v, 4) for v in plain_ms],
+            "rank_ms_eplb": [round(v, 4) for v in eplb_ms],
+            "group_ms_plain": round(max(plain_ms), 4), "group_ms_eplb": round(max(eplb_ms), 4),
+            "rank_pairs_plain": plain_pairs, "rank_pairs_eplb": eplb_pairs,
+            "note": "routed experts only (no shared expert); each rank's share runs on all T "
+                    "tokens in turn on one GPU; group time = slowest rank"}
+
+
 def cpu_baseline(host, w, sample):
     """The oracle, as it stands, on `sample` tokens of the workload (CPU, float64 MLPs)."""
     import numpy as np
@@ -372,6 +467,10 @@ def main():
     print(f"[bench] generating inputs for {w.key} (T={T})", file=sys.stderr, flush=True)
     host = HostLayer(w, max(T, Td))
     torch.cuda.init()
+    if args.eplb:
+        print(json.dumps({"workload": f"{w.desc}, T={T}",
+                          "eplb": run_eplb(host, w, T, args.eplb, args.steps, args.warmup)}))
+        return
     if args.exchange_only:
         b = Bench(w, T, host)
         b.forward()
