@@ -51,7 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "router_logits", "softmax_fp32", "select_experts", "routing_weights", "route_from_logits",
+    "router_logits", "softmax_fp32", "sigmoid_fp32", "select_experts", "routing_weights", "route_from_logits",
     "route",
     "gated_mlp", "moe_forward_given_routing", "moe_forward", "moe_forward_per_token",
     "align_permute", "weight_bytes",
@@ -87,7 +87,20 @@ def softmax_fp32(logits):
     return (e / s).astype(np.float32)
 
 
-def select_experts(p, top_k, use_grouped_topk=False, num_expert_group=1, topk_group=1):
+def sigmoid_fp32(logits):
+    """Element-wise logistic scores 1 / (1 + exp(-l)), computed in fp64 and rounded once to fp32.
+
+    ``scoring_func`` of the fused layer (``recursive_replace`` passes it through; softmax is
+    the default). The pages name the switch without its formula; sigmoid is the logistic
+    function, as DeepSeek-V3 scores its experts.
+    """
+    l = np.asarray(logits, np.float64)
+    with np.errstate(over="ignore"):
+        return (1.0 / (1.0 + np.exp(-l))).astype(np.float32)
+
+
+def select_experts(p, top_k, use_grouped_topk=False, num_expert_group=1, topk_group=1,
+                   score_bias=None):
     """Top-k expert ids per token, plain or group-limited.
 
     Plain: the k largest probabilities (``torch.topk`` in ``MixtralMoE.forward``).
@@ -97,8 +110,14 @@ def select_experts(p, top_k, use_grouped_topk=False, num_expert_group=1, topk_gr
     probability; the ``topk_group`` best groups are kept and the top-k is taken among
     their experts only (others are excluded, not zeroed).
 
-    Order and ties: slots are sorted by probability descending; equal values go to the
-    lower expert id (groups: the lower group id).
+    ``score_bias`` (``e_score_correction_bias``, named on the transformers MoE page without
+    its use): a per-expert bias added to the scores for the choice only, as DeepSeek-V3
+    does: candidates are ranked by the fp32 sum p + b, and a group's score is the fp32 sum
+    of its two largest biased scores (the larger first; one score for groups of one). The
+    weights still come from p (``routing_weights``).
+
+    Order and ties: slots are sorted by score descending; equal values go to the lower
+    expert id (groups: the lower group id).
 
     Returns ``ids`` int32 [T, k], ``gap`` fp32 [T] = k-th minus (k+1)-th candidate score
     (+inf without a (k+1)-th candidate) and ``ggap`` fp32 [T] = the same gap between the
@@ -106,11 +125,18 @@ def select_experts(p, top_k, use_grouped_topk=False, num_expert_group=1, topk_gr
     """
     p = np.asarray(p, np.float32)
     T, E = p.shape
+    if score_bias is not None:
+        p = (p + np.asarray(score_bias, np.float32)[None, :]).astype(np.float32)
     ggap = np.full(T, np.inf, np.float32)
     if use_grouped_topk:
         G = int(num_expert_group)
         per = E // G
-        gs = p.reshape(T, G, per).max(axis=2)
+        grp = p.reshape(T, G, per)
+        if score_bias is None:
+            gs = grp.max(axis=2)
+        else:
+            top = -np.sort(-grp, axis=2)
+            gs = top[:, :, 0] if per == 1 else (top[:, :, 0] + top[:, :, 1]).astype(np.float32)
         gorder = np.argsort(-gs, axis=1, kind="stable")
         if topk_group < G:
             gsorted = np.take_along_axis(gs, gorder, axis=1)
@@ -149,21 +175,30 @@ def routing_weights(p, ids, renormalize, routed_scaling_factor=1.0):
 
 
 def route_from_logits(logits, top_k, renormalize, use_grouped_topk=False, num_expert_group=1,
-                      topk_group=1, routed_scaling_factor=1.0):
-    """Softmax -> (grouped) top-k -> weights on given fp32 logits (bias already added)."""
-    p = softmax_fp32(logits)
-    ids, gap, ggap = select_experts(p, top_k, use_grouped_topk, num_expert_group, topk_group)
+                      topk_group=1, routed_scaling_factor=1.0, scoring_func="softmax",
+                      score_bias=None):
+    """Scores (softmax or sigmoid) -> (grouped) top-k -> weights on given fp32 logits (logit
+    bias already added); ``score_bias`` steers the choice only."""
+    if scoring_func == "softmax":
+        p = softmax_fp32(logits)
+    elif scoring_func == "sigmoid":
+        p = sigmoid_fp32(logits)
+    else:
+        raise ValueError(scoring_func)
+    ids, gap, ggap = select_experts(p, top_k, use_grouped_topk, num_expert_group, topk_group,
+                                    score_bias)
     w = routing_weights(p, ids, renormalize, routed_scaling_factor)
     return {"logits": np.asarray(logits, np.float32), "probs": p, "ids": ids, "weights": w,
             "gap": gap, "ggap": ggap}
 
 
 def route(x, w_gate, top_k, renormalize, use_grouped_topk=False, num_expert_group=1,
-          topk_group=1, routed_scaling_factor=1.0, logit_bias=None):
-    """Router: logits -> fp32 softmax -> (grouped) top-k -> weights. Returns a dict."""
+          topk_group=1, routed_scaling_factor=1.0, logit_bias=None, scoring_func="softmax",
+          score_bias=None):
+    """Router: logits -> fp32 scores -> (grouped) top-k -> weights. Returns a dict."""
     return route_from_logits(router_logits(x, w_gate, logit_bias), top_k, renormalize,
                              use_grouped_topk, num_expert_group, topk_group,
-                             routed_scaling_factor)
+                             routed_scaling_factor, scoring_func, score_bias)
 
 
 def gated_mlp(x, w13, w2):

@@ -530,3 +530,80 @@ def test_forward_given_slots_matches_per_expert_form():
                 a = h[:I] / (1 + np.exp(-h[:I])) * h[I:]
                 want[t] += w[t, j] * (w2[loc[s]] @ a)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- routing variants
+def test_sigmoid_special_values_and_symmetry():
+    s = oracle.sigmoid_fp32(np.array([[0.0, math.log(3.0), -math.log(3.0), 200.0, -200.0]]))
+    assert s.dtype == np.float32
+    assert s[0, 0] == 0.5 and s[0, 1] == 0.75 and s[0, 2] == 0.25
+    assert s[0, 3] == 1.0 and s[0, 4] == 0.0  # exp(200) overflows the fp32 range of 1/(1+e)
+    x = _rand((1, 257), (901, 0, 0), 4.0)
+    a, b = oracle.sigmoid_fp32(x), oracle.sigmoid_fp32(-x)
+    assert np.max(np.abs(a.astype(np.float64) + b - 1.0)) <= 2.0 ** -24
+    assert np.all(np.diff(oracle.sigmoid_fp32(np.sort(x, axis=1))) >= 0)
+
+
+def test_sigmoid_and_softmax_pick_the_same_experts():
+    """Both scores are increasing in the logit, so the plain top-k is the same set (tokens
+    whose chosen logits are clearly apart)."""
+    l = _rand((64, 32), (902, 0, 0), 2.0).astype(np.float32)
+    a = oracle.route_from_logits(l, 5, True, scoring_func="softmax")
+    b = oracle.route_from_logits(l, 5, True, scoring_func="sigmoid")
+    srt = -np.sort(-l, axis=1)
+    clear = (srt[:, 4] - srt[:, 5]) > 1e-4
+    assert np.array_equal(np.sort(a["ids"], 1)[clear], np.sort(b["ids"], 1)[clear])
+    # the sigmoid weights are the scores of the chosen experts, renormalised
+    p = 1.0 / (1.0 + np.exp(-l.astype(np.float64)))
+    pc = np.take_along_axis(p, b["ids"].astype(np.int64), axis=1)
+    assert np.allclose(b["weights"], pc / pc.sum(axis=1, keepdims=True), rtol=1e-6)
+
+
+def _v3_brute(p, b, k, G, keep):
+    """Group-limited choice with a selection bias, by plain enumeration on one token."""
+    E = len(p)
+    per = E // G
+    s = [float(np.float32(np.float32(p[e]) + np.float32(b[e]))) for e in range(E)]
+    gsc = []
+    for g in range(G):
+        top = sorted(s[g * per:(g + 1) * per], reverse=True)
+        gsc.append(float(np.float32(top[0] + top[1])) if per > 1 else top[0])
+    groups = sorted(range(G), key=lambda g: (-gsc[g], g))[:keep]
+    cand = [e for e in range(E) if e // per in groups]
+    return sorted(sorted(cand, key=lambda e: (-s[e], e))[:k])
+
+
+@pytest.mark.parametrize("E,G,keep,k", [(8, 4, 2, 3), (12, 3, 1, 2), (16, 8, 3, 4), (6, 6, 6, 2)])
+def test_grouped_choice_with_bias_brute_force(E, G, keep, k):
+    rng = np.random.default_rng(E * 10 + G)
+    for trial in range(40):
+        p = oracle.softmax_fp32(rng.normal(size=(1, E)).astype(np.float32))
+        b = rng.normal(scale=0.05, size=E).astype(np.float32)
+        ids, _, _ = oracle.select_experts(p, k, True, G, keep, score_bias=b)
+        assert sorted(ids[0].tolist()) == _v3_brute(p[0], b, k, G, keep), trial
+
+
+def test_bias_steers_choice_not_weights():
+    """A large bias forces an expert into the top-k; its weight is still its own score."""
+    l = np.array([[2.0, 1.0, 0.5, 0.0, -1.0, -3.0]], np.float32)
+    b = np.zeros(6, np.float32)
+    b[5] = 10.0
+    r = oracle.route_from_logits(l, 2, False, scoring_func="sigmoid", score_bias=b)
+    assert sorted(r["ids"][0].tolist()) == [0, 5]
+    w = dict(zip(r["ids"][0].tolist(), r["weights"][0].tolist()))
+    assert w[5] == np.float32(1.0 / (1.0 + math.exp(3.0)))
+    assert w[0] == np.float32(1.0 / (1.0 + math.exp(-2.0)))
+    # a bias equal on every expert changes nothing in the plain choice
+    l2 = _rand((40, 16), (903, 0, 0)).astype(np.float32)
+    r0 = oracle.route_from_logits(l2, 4, True, scoring_func="sigmoid")
+    r1 = oracle.route_from_logits(l2, 4, True, scoring_func="sigmoid",
+                                  score_bias=np.full(16, 0.125, np.float32))
+    assert np.array_equal(r0["ids"], r1["ids"]) and np.array_equal(r0["weights"], r1["weights"])
+
+
+def test_grouped_with_bias_and_groups_of_one_is_plain_topk():
+    l = _rand((30, 16), (904, 0, 0)).astype(np.float32)
+    b = (_rand((16,), (904, 0, 1)) * 0.1).astype(np.float32)
+    g = oracle.route_from_logits(l, 3, True, True, 16, 16, scoring_func="sigmoid", score_bias=b)
+    pl = oracle.route_from_logits(l, 3, True, scoring_func="sigmoid", score_bias=b)
+    assert np.array_equal(g["ids"], pl["ids"]) and np.array_equal(g["weights"], pl["weights"])
