@@ -108,7 +108,7 @@ class Bench:
         self.p = moe.make_params(w.num_experts, w.top_k, w.hidden_size, w.intermediate_size,
                                  w.renormalize, w.use_grouped_topk, w.num_expert_group,
                                  w.topk_group, w.routed_scaling_factor, w.num_local_experts,
-                                 w.shared_intermediate_size, w.dtype)
+                                 w.shared_intermediate_size, w.dtype, w.scoring_func)
         self.d = host.device_tensors(T)
         dt = self.d["x"].dtype
         k, H = w.top_k, w.hidden_size
@@ -133,7 +133,8 @@ class Bench:
     def forward(self):
         d = self.d
         self.moe.moe_forward(self.p, self.T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
-                             d["w2"], d["sw13"], d["sw2"], self.out, self.ids, self.tw, self.ws)
+                             d["w2"], d["sw13"], d["sw2"], self.out, self.ids, self.tw, self.ws,
+                             score_bias=d["sbias"])
 
     def split_step(self, ev=None):
         """The same kernels as moe_forward through the split entry points; events at stage ends."""
@@ -141,7 +142,7 @@ class Bench:
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         m.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], self.ids, self.tw, self.local,
-                    self.sws)
+                    self.sws, score_bias=d["sbias"])
         rec(1)
         m.moe_align_permute(p, T, self.local, self.bm, self.sp, self.be, self.pr, self.npad, self.sws)
         rec(2)
@@ -165,6 +166,7 @@ class HostLayer:
         self.x = wl.x(w, T_max)
         self.gate = wl.gate(w)
         self.bias = wl.logit_bias(w)
+        self.sbias = wl.score_bias(w)
         self.emap = wl.expert_map(w)
         self.w13, self.w2 = wl.local_expert_weights(w)
         self.sw13, self.sw2 = wl.shared_weights(w)
@@ -173,7 +175,7 @@ class HostLayer:
     def _weights_on_device(self):
         if self._dev is None:
             self._dev = {k: _dev(getattr(self, k)) for k in
-                         ("gate", "bias", "emap", "w13", "w2", "sw13", "sw2")}
+                         ("gate", "bias", "sbias", "emap", "w13", "w2", "sw13", "sw2")}
         return self._dev
 
     def device_tensors(self, T):
@@ -343,6 +345,7 @@ def run_eplb(host, w, T, extra, steps, warmup):
     x = _dev(host.x[:T])
     gate = _dev(host.gate)
     bias = _dev(host.bias)
+    sbias = _dev(host.sbias)
     dt = x.dtype
     out = torch.empty(T, H, dtype=dt, device=dev)
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
@@ -360,10 +363,11 @@ def run_eplb(host, w, T, extra, steps, warmup):
 
         def call():
             if eplb is None:
-                moe.moe_forward(p, T, x, gate, bias, emap, w13, w2, None, None, out, ids, tw, ws)
+                moe.moe_forward(p, T, x, gate, bias, emap, w13, w2, None, None, out, ids, tw, ws,
+                                score_bias=sbias)
             else:
                 moe.moe_forward_eplb(p, eplb, T, x, gate, bias, emap, w13, w2, None, None, out,
-                                     ids, tw, ws)
+                                     ids, tw, ws, score_bias=sbias)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -378,7 +382,7 @@ def run_eplb(host, w, T, extra, steps, warmup):
     def params(n_local):
         return moe.make_params(E, k, H, w.intermediate_size, w.renormalize, w.use_grouped_topk,
                                w.num_expert_group, w.topk_group, w.routed_scaling_factor, n_local,
-                               0, w.dtype)
+                               0, w.dtype, w.scoring_func)
 
     per = E // ep
     plain_ms, plain_pairs = [], []
@@ -432,7 +436,8 @@ def cpu_baseline(host, w, sample):
     x = wl.to_f32(host.x[:sample])
     t0 = time.perf_counter()
     r = oracle.route(x, wl.to_f32(host.gate), w.top_k, w.renormalize, w.use_grouped_topk,
-                     w.num_expert_group, w.topk_group, w.routed_scaling_factor, host.bias)
+                     w.num_expert_group, w.topk_group, w.routed_scaling_factor, host.bias,
+                     w.scoring_func, host.sbias)
 
     class Lazy:
         def __init__(self, a):

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libexpert_moe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -53,6 +54,7 @@ class moe_params(ctypes.Structure):
         ("num_local_experts", ctypes.c_int32),
         ("shared_intermediate_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("scoring_func", ctypes.c_int32),
     ]
 
 
@@ -78,13 +80,19 @@ def make_eplb(num_physical_experts, max_replicas, logical_to_physical, replica_c
 def make_params(num_experts, top_k, hidden_size, intermediate_size, renormalize=True,
                 use_grouped_topk=False, num_expert_group=1, topk_group=1,
                 routed_scaling_factor=1.0, num_local_experts=None, shared_intermediate_size=0,
-                dtype="bf16") -> moe_params:
+                dtype="bf16", scoring_func="softmax") -> moe_params:
+    if scoring_func in ("softmax", MOE_SCORE_SOFTMAX):
+        sf = MOE_SCORE_SOFTMAX
+    elif scoring_func in ("sigmoid", MOE_SCORE_SIGMOID):
+        sf = MOE_SCORE_SIGMOID
+    else:
+        raise ValueError(f"scoring_func {scoring_func!r}")
     return moe_params(
         int(num_experts), int(top_k), int(hidden_size), int(intermediate_size),
         int(bool(renormalize)), int(bool(use_grouped_topk)), int(num_expert_group),
         int(topk_group), float(routed_scaling_factor),
         int(num_experts if num_local_experts is None else num_local_experts),
-        int(shared_intermediate_size), MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32)
+        int(shared_intermediate_size), MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32, sf)
 
 
 _lib = None
@@ -99,7 +107,7 @@ _SIGS = {
     "moe_workspace_size": ([_P, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "moe_make_expert_map": ([_i32, _i32, _i32, _vp], ctypes.c_int),
     "moe_weight_bytes": ([_i64, _i64, _i64, _i32, _i64], _i64),
-    "moe_route": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_route": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_align_permute": ([_P, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_grouped_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                         ctypes.c_int),
@@ -107,18 +115,18 @@ _SIGS = {
     "moe_expert_down": ([_P, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "moe_shared_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_combine": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
-    "moe_forward": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
-                     _vp], ctypes.c_int),
+    "moe_forward": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                     _sz, _vp], ctypes.c_int),
     "moe_ep_send_capacity": ([_P, _i64, _i32], _i64),
     "moe_ep_workspace_size": ([_P, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "moe_ep_dispatch": ([_P, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                         ctypes.c_int),
     "moe_ep_combine": ([_P, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_eplb_tables": ([_i32, _i32, _vp, _i32, _vp, _vp], ctypes.c_int),
-    "moe_route_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_route_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                        ctypes.c_int),
     "moe_forward_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                          _vp, _sz, _vp], ctypes.c_int),
+                          _vp, _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -207,10 +215,10 @@ def moe_weight_bytes(n_experts: int, hidden: int, inter: int, dtype_bytes: int, 
 
 
 def moe_route(p, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w, topk_local,
-              ws, stream=None):
+              ws, stream=None, score_bias=None):
     wp, wn = _ws(ws)
     _check(lib().moe_route(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w_gate), _ptr(logit_bias),
-                           _ptr(expert_map), _ptr(topk_ids), _ptr(topk_w), _ptr(topk_local),
+                           _ptr(score_bias), _ptr(expert_map), _ptr(topk_ids), _ptr(topk_w), _ptr(topk_local),
                            wp, wn, _stream(stream)), "moe_route")
 
 
@@ -256,10 +264,10 @@ def moe_combine(p, num_tokens, y, pair_row, topk_w, shared_y, out, stream=None):
 
 
 def moe_forward(p, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
-                shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None):
+                shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None):
     wp, wn = _ws(ws)
     _check(lib().moe_forward(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w_gate), _ptr(logit_bias),
-                             _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(shared_w13),
+                             _ptr(score_bias), _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(shared_w13),
                              _ptr(shared_w2), _ptr(out), _ptr(topk_ids_out), _ptr(topk_w_out),
                              wp, wn, _stream(stream)), "moe_forward")
 
@@ -306,19 +314,20 @@ def moe_eplb_tables(num_logical: int, physical_to_logical, max_replicas: int | N
 
 
 def moe_route_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
-                   topk_local, ws, stream=None):
+                   topk_local, ws, stream=None, score_bias=None):
     wp, wn = _ws(ws)
     _check(lib().moe_route_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
-                                _ptr(w_gate), _ptr(logit_bias), _ptr(expert_map), _ptr(topk_ids),
+                                _ptr(w_gate), _ptr(logit_bias), _ptr(score_bias), _ptr(expert_map), _ptr(topk_ids),
                                 _ptr(topk_w), _ptr(topk_local), wp, wn, _stream(stream)),
            "moe_route_eplb")
 
 
 def moe_forward_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
-                     shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None):
+                     shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None):
     wp, wn = _ws(ws)
     _check(lib().moe_forward_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
-                                  _ptr(w_gate), _ptr(logit_bias), _ptr(expert_map), _ptr(w13),
+                                  _ptr(w_gate), _ptr(logit_bias), _ptr(score_bias),
+                                  _ptr(expert_map), _ptr(w13),
                                   _ptr(w2), _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
                                   _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
            "moe_forward_eplb")

@@ -24,6 +24,7 @@ inline bool mult64(int32_t v) { return v > 0 && v % 64 == 0; }
 int check_params(const moe_params* p) {
   if (!p) return MOE_EINVAL;
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (p->scoring_func != MOE_SCORE_SOFTMAX && p->scoring_func != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   const int E = p->num_experts;
   if (E < 1 || p->top_k < 1 || p->top_k > E) return MOE_EINVAL;
   if (!mult64(p->hidden_size) || !mult64(p->intermediate_size)) return MOE_EINVAL;
@@ -234,8 +235,9 @@ int64_t moe_weight_bytes(int64_t n_experts, int64_t hidden, int64_t inter, int32
 // moe_route with an optional replicated placement (eplb = NULL: the expert map is by expert id)
 static int route_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num_tokens,
                       const void* x, const void* w_gate, const float* logit_bias,
-                      const int32_t* expert_map, int32_t* topk_ids, float* topk_w,
-                      int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
+                      const float* score_bias, const int32_t* expert_map, int32_t* topk_ids,
+                      float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes,
+                      void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
@@ -247,15 +249,16 @@ static int route_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num
   const int T = static_cast<int>(num_tokens);
   float* logits = static_cast<float*>(ws);
   if ((rc = moe::launch_router_logits(*p, T, x, w_gate, logits, as_stream(stream)))) return rc;
-  return moe::launch_topk(*p, T, logits, logit_bias, expert_map, topk_ids, topk_w, topk_local,
-                          as_stream(stream), eplb);
+  return moe::launch_topk(*p, T, logits, logit_bias, score_bias, expert_map, topk_ids, topk_w,
+                          topk_local, as_stream(stream), eplb);
 }
 
 int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
-              const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
-              float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
-  return route_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
-                    topk_local, ws, ws_bytes, stream);
+              const float* logit_bias, const float* score_bias, const int32_t* expert_map,
+              int32_t* topk_ids, float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes,
+              void* stream) {
+  return route_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                    topk_ids, topk_w, topk_local, ws, ws_bytes, stream);
 }
 
 int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* topk_local,
@@ -361,10 +364,10 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
 // moe_forward with an optional replicated placement (eplb = NULL: the expert map is by expert id)
 static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num_tokens,
                         const void* x, const void* w_gate, const float* logit_bias,
-                        const int32_t* expert_map, const void* w13, const void* w2,
-                        const void* shared_w13, const void* shared_w2, void* out,
-                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        const float* score_bias, const int32_t* expert_map, const void* w13,
+                        const void* w2, const void* shared_w13, const void* shared_w2,
+                        void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                        size_t ws_bytes, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
@@ -416,8 +419,8 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t n
   }
 
   if ((rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s))) return rc;
-  if ((rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, expert_map, ids, tw,
-                             local, s, eplb)))
+  if ((rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, score_bias,
+                             expert_map, ids, tw, local, s, eplb)))
     return rc;
   if ((rc = moe::launch_align(*p, T, local, bm, sorted_pairs, block_expert, pair_row, num_padded,
                               at<int32_t>(ws, L.meta), at<int32_t>(ws, L.chunk), s)))
@@ -435,12 +438,13 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t n
 }
 
 int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
-                const float* logit_bias, const int32_t* expert_map, const void* w13,
-                const void* w2, const void* shared_w13, const void* shared_w2, void* out,
-                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                const float* logit_bias, const float* score_bias, const int32_t* expert_map,
+                const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
+                void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                 void* stream) {
-  return forward_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2,
-                      shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+  return forward_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, w13,
+                      w2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes,
+                      stream);
 }
 
 }  // extern "C"
@@ -486,26 +490,27 @@ int moe_eplb_tables(int32_t num_logical, int32_t num_physical, const int32_t* ph
 }
 
 int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
-                   const void* w_gate, const float* logit_bias, const int32_t* expert_map,
-                   int32_t* topk_ids, float* topk_w, int32_t* topk_local, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const void* w_gate, const float* logit_bias, const float* score_bias,
+                   const int32_t* expert_map, int32_t* topk_ids, float* topk_w,
+                   int32_t* topk_local, void* ws, size_t ws_bytes, void* stream) {
   moe::EplbMap m;
   int rc = check_eplb(p, eplb, &m);
   if (rc) return rc;
-  return route_impl(p, &m, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
-                    topk_local, ws, ws_bytes, stream);
+  return route_impl(p, &m, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, topk_ids,
+                    topk_w, topk_local, ws, ws_bytes, stream);
 }
 
 int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
-                     const void* w_gate, const float* logit_bias, const int32_t* expert_map,
-                     const void* w13, const void* w2, const void* shared_w13,
-                     const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
-                     void* ws, size_t ws_bytes, void* stream) {
+                     const void* w_gate, const float* logit_bias, const float* score_bias,
+                     const int32_t* expert_map, const void* w13, const void* w2,
+                     const void* shared_w13, const void* shared_w2, void* out,
+                     int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     void* stream) {
   moe::EplbMap m;
   int rc = check_eplb(p, eplb, &m);
   if (rc) return rc;
-  return forward_impl(p, &m, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
-                      shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+  return forward_impl(p, &m, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, w13, w2,
+                      shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

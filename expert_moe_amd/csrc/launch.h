@@ -32,12 +32,12 @@ struct EplbMap {
   int P;
 };
 
-// Sum of the logit partials (written back into partial 0), fp32 softmax, (grouped) top-k,
-// renormalise, scale, expert_map lookup (through the replica of token t, t mod cnt[e], when
-// eplb is given).
+// Sum of the logit partials (written back into partial 0), fp32 softmax or sigmoid, (grouped)
+// top-k on the scores plus score_bias (when given), renormalise, scale, expert_map lookup
+// (through the replica of token t, t mod cnt[e], when eplb is given).
 int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
-                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s,
-                const EplbMap* eplb = nullptr);
+                const float* score_bias, const int32_t* expert_map, int32_t* ids, float* w,
+                int32_t* local, hipStream_t s, const EplbMap* eplb = nullptr);
 
 // Count / scan / scatter of the (token, slot) pairs by local expert (block_expert may be NULL).
 // meta: [num_padded(1) | offsets(E_l+1) | counts(E_l)], chunk: [align_chunks(T) * E_l].

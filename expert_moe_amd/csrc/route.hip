@@ -1,13 +1,17 @@
 // Router of the fused MoE forward on gfx950: logits GEMM launch and the per-token fp32
-// softmax / top-k epilogue, one wavefront per token.
+// scores / top-k epilogue, one wavefront per token.
 //
 // Steps ("[Feature] Expert parallelism support", MixtralMoE.forward; "ep_fused_moe_patch.py",
 // _ep_forward Step 1 select_experts; "vllm.model_executor.models.transformers.moe",
 // recursive_replace routed_scaling_factor / n_group / topk_group):
-//   p = softmax(logits + bias) in fp32 over all E global experts
-//   grouped: group score = largest p of each contiguous group of E/G experts; keep the
-//            topk_group best groups; experts of other groups are excluded
-//   ids = k best candidates, probability descending, ties to the lower id
+//   p = softmax(logits + bias) in fp32 over all E global experts, or with the sigmoid scoring
+//       function 1 / (1 + exp(-(logits + bias))) per expert (scoring_func, named on the
+//       transformers MoE page; the logistic form is DeepSeek-V3's)
+//   s = p + score_bias (the selection-only e_score_correction_bias, DeepSeek-V3's use), or p
+//   grouped: group score = largest s of each contiguous group of E/G experts, or with a
+//            score bias the sum of its two largest s; keep the topk_group best groups;
+//            experts of other groups are excluded
+//   ids = k best candidates by s, descending, ties to the lower id
 //   w = p[ids], / sum_j w (slot order) if renormalize, * routed_scaling_factor
 //   local = expert_map[ids] (-1 if not on this share)
 #include <math.h>
@@ -22,7 +26,9 @@ namespace {
 struct TopkArgs {
   float* logits;  // [splits, T, E] partial sums; their total is written back to split 0
   int splits;
-  const float* bias;
+  const float* bias;   // added to the logits
+  const float* sbias;  // added to the scores for the choice only, or NULL
+  int sigmoid;         // 1: logistic scores, 0: softmax
   const int32_t* emap;
   const int32_t* l2p;  // replicated experts: [E, max_rep] physical ids, or NULL
   const int32_t* cnt;  // [E] replica counts
@@ -92,11 +98,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return wave_reduce(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
 }
 
-// Selection key of a probability p in [0, 1]: the bit pattern of a non-negative float is
-// ordered like its value, so key = bits(p) + 1 orders candidates by p and leaves 0 for an
-// expert that may not be chosen (excluded group, or past E). p(key) = float(key - 1).
-__device__ __forceinline__ uint32_t prob_key(float p) { return __float_as_uint(p) + 1u; }
-__device__ __forceinline__ float key_prob(uint32_t k) { return __uint_as_float(k - 1u); }
+// Selection key of a score of either sign: the bit pattern with the sign bit set for
+// non-negative values and all bits flipped for negative ones is ordered like the value, and
+// no finite score maps to 0, which marks an expert that may not be chosen (excluded group, or
+// past E).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // 4 tokens per workgroup (one per wave); lane l holds experts l + 64 q for q < NQ, E <= 64 NQ.
 template <int NQ>
@@ -123,36 +132,65 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     }
     pv[q] = l;
   }
-  float lmax = pv[0];
+  if (a.sigmoid) {
 #pragma unroll
-  for (int q = 1; q < NQ; ++q) lmax = fmaxf(lmax, pv[q]);
-  const float m = wave_max(lmax);
-  float part = 0.f;
+    for (int q = 0; q < NQ; ++q) pv[q] = (lane + 64 * q < E) ? 1.f / (1.f + expf(-pv[q])) : 0.f;
+  } else {
+    float lmax = pv[0];
+#pragma unroll
+    for (int q = 1; q < NQ; ++q) lmax = fmaxf(lmax, pv[q]);
+    const float m = wave_max(lmax);
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      pv[q] = (lane + 64 * q < E) ? expf(pv[q] - m) : 0.f;
+      part += pv[q];
+    }
+    const float ssum = wave_sum(part);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) pv[q] = pv[q] / ssum;
+  }
+
+  // selection scores: p, plus the selection bias when there is one
+  float sv[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    pv[q] = (lane + 64 * q < E) ? expf(pv[q] - m) : 0.f;
-    part += pv[q];
+    const int e = lane + 64 * q;
+    sv[q] = pv[q];
+    if (a.sbias && valid && e < E) sv[q] += a.sbias[e];
   }
-  const float ssum = wave_sum(part);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) pv[q] = pv[q] / ssum;
-
   uint32_t key[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) key[q] = (lane + 64 * q < E) ? prob_key(pv[q]) : 0u;
+  for (int q = 0; q < NQ; ++q) key[q] = (lane + 64 * q < E) ? order_key(sv[q]) : 0u;
 
   if (a.grouped) {
-    // group score = largest p of the group's E/G contiguous experts; the topk_group best
-    // groups (ties to the lower group) stay candidates
+    // group score over the group's E/G contiguous experts: the largest score, or with a
+    // selection bias the sum of the two largest biased scores (the larger first); the
+    // topk_group best groups (ties to the lower group) stay candidates
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      if (lane + 64 * q < E) sp[wave][lane + 64 * q] = pv[q];
+      if (lane + 64 * q < E) sp[wave][lane + 64 * q] = sv[q];
     __syncthreads();
     const int gsz = E / a.G;
-    float gs = 0.f;
-    if (lane < a.G)
-      for (int i = 0; i < gsz; ++i) gs = fmaxf(gs, sp[wave][lane * gsz + i]);
-    uint32_t gk = lane < a.G ? prob_key(gs) : 0u;
+    float gs = -INFINITY;
+    if (lane < a.G) {
+      if (a.sbias == nullptr) {
+        for (int i = 0; i < gsz; ++i) gs = fmaxf(gs, sp[wave][lane * gsz + i]);
+      } else {
+        float t1 = -INFINITY, t2 = -INFINITY;
+        for (int i = 0; i < gsz; ++i) {
+          const float v = sp[wave][lane * gsz + i];
+          if (v > t1) {
+            t2 = t1;
+            t1 = v;
+          } else if (v > t2) {
+            t2 = v;
+          }
+        }
+        gs = gsz > 1 ? t1 + t2 : t1;
+      }
+    }
+    uint32_t gk = lane < a.G ? order_key(gs) : 0u;
     uint64_t kept = 0;
     for (int r = 0; r < a.keep; ++r) {
       const uint32_t best = wave_max_u32(gk);
@@ -188,7 +226,12 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
       for (int q = 0; q < NQ; ++q)
         if ((id >> 6) == q) key[q] = 0u;
     }
-    const float bv = key_prob(best);
+    // the chosen expert's own score p (the weight never includes the selection bias)
+    float pc = pv[0];
+#pragma unroll
+    for (int q = 1; q < NQ; ++q)
+      if ((id >> 6) == q) pc = pv[q];
+    const float bv = __shfl(pc, id & 63);
     if (lane == j) { my_id = id; my_w = bv; }
     wsum = j == 0 ? bv : wsum + bv;
   }
@@ -273,12 +316,14 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
 }
 
 int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
-                const int32_t* expert_map, int32_t* ids, float* w, int32_t* local, hipStream_t s,
-                const EplbMap* eplb) {
+                const float* score_bias, const int32_t* expert_map, int32_t* ids, float* w,
+                int32_t* local, hipStream_t s, const EplbMap* eplb) {
   TopkArgs a;
   a.logits = logits;
   a.splits = router_splits(p, T);
   a.bias = bias;
+  a.sbias = score_bias;
+  a.sigmoid = p.scoring_func == MOE_SCORE_SIGMOID;
   a.emap = expert_map;
   a.l2p = eplb ? eplb->l2p : nullptr;
   a.cnt = eplb ? eplb->cnt : nullptr;

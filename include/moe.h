@@ -4,8 +4,9 @@
  *
  * What is computed (per token t of x [T, H]):
  *   logits  = x[t] . Wg^T (+ logit_bias)        replicated router gate over ALL E experts
- *   p       = softmax(logits) in fp32
- *   ids     = top-k of p (plain, or group-limited), ties to the lower expert id
+ *   p       = softmax(logits) in fp32 (or the logistic sigmoid of each logit)
+ *   ids     = top-k of p (+ score_bias, when given: it steers the choice only), plain or
+ *             group-limited, ties to the lower expert id
  *   w       = p[ids] (/ sum if renormalize) * routed_scaling_factor
  *   out[t]  = sum over slots j whose expert is local of w[j] * MLP_{ids[j]}(x[t])
  *             (+ the shared expert's MLP(x[t]), weight 1, when its weights are given)
@@ -59,6 +60,9 @@ extern "C" {
 #define MOE_F32 0
 #define MOE_BF16 1
 
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+
 /*
  * Layer parameters, named after the EP-aware FusedMoE constructor (_ep_init on the
  * ep_fused_moe_patch.py page) and the config fields of MoEMixin.recursive_replace.
@@ -78,6 +82,15 @@ extern "C" {
  *  shared_intermediate_size  I_s of the shared expert MLP (n_shared * I), 0 = none,
  *                            multiple of 64 otherwise.
  *  dtype                     MOE_F32 or MOE_BF16 (x, weights, y, out).
+ *  scoring_func              MOE_SCORE_SOFTMAX (0, the default of a zeroed struct) or
+ *                            MOE_SCORE_SIGMOID (1: p = 1 / (1 + exp(-logit)) per expert, as
+ *                            DeepSeek-V3 scores; the pages name the switch, not its formula).
+ *
+ * Selection bias (score_bias, "e_score_correction_bias" on the transformers MoE page, named
+ * there without its use): an fp32 [E] device vector added to p for the choice only, as
+ * DeepSeek-V3 does. Candidates rank by the fp32 sum p + b; with group-limited routing a
+ * group's score becomes the sum of its two largest biased scores (one score for groups of
+ * one); the weights still come from p. NULL = no bias (groups score by their largest p).
  */
 typedef struct moe_params {
   int32_t num_experts;
@@ -92,6 +105,7 @@ typedef struct moe_params {
   int32_t num_local_experts;
   int32_t shared_intermediate_size;
   int32_t dtype;
+  int32_t scoring_func;
 } moe_params;
 
 /* ------------------------------------------------------------------ host helpers */
@@ -144,18 +158,21 @@ int64_t moe_weight_bytes(int64_t n_experts, int64_t hidden, int64_t inter, int32
 /* ------------------------------------------------------------------ device entry points */
 
 /*
- * Router: logits = x . Wg^T (+ logit_bias), fp32 softmax, plain or grouped top-k,
- * renormalisation, routed scaling, expert_map lookup (MixtralMoE.forward's gate /
- * softmax / topk / renormalise; select_experts in _ep_forward Step 1).
- *  x [T, H] dtype; w_gate [E, H] dtype; logit_bias [E] fp32 or NULL; expert_map [E].
+ * Router: logits = x . Wg^T (+ logit_bias), fp32 softmax (or sigmoid), plain or grouped
+ * top-k (steered by score_bias when given), renormalisation, routed scaling, expert_map
+ * lookup (MixtralMoE.forward's gate / softmax / topk / renormalise; select_experts in
+ * _ep_forward Step 1).
+ *  x [T, H] dtype; w_gate [E, H] dtype; logit_bias [E] fp32 or NULL; score_bias [E] fp32 or
+ *  NULL; expert_map [E].
  *  Outputs [T, k]: topk_ids (global ids, probability descending, ties to the lower id),
  *  topk_w (fp32), topk_local (expert_map[topk_ids], -1 = not local).
  *  ws: device scratch of at least moe_workspace_size(p, T, 0) bytes. On completion its
  *  first T*E*4 bytes hold the fp32 router logits x . Wg^T [T, E] (without logit_bias).
  */
 int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
-              const float* logit_bias, const int32_t* expert_map, int32_t* topk_ids,
-              float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes, void* stream);
+              const float* logit_bias, const float* score_bias, const int32_t* expert_map,
+              int32_t* topk_ids, float* topk_w, int32_t* topk_local, void* ws, size_t ws_bytes,
+              void* stream);
 
 /*
  * Groups the (token, slot) pairs by local expert, stable in pair id p = t*k + j, each
@@ -238,15 +255,16 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
  * that stream. out [T, H] = this share's partial sum; summing the outputs of all disjoint
  * shares (the shared expert passed to exactly one of them) gives the full layer.
  * A share that receives no pairs writes zeros (plus the shared expert).
+ *  logit_bias, score_bias: as moe_route.
  *  shared_w13 / shared_w2: both NULL (no shared expert on this share) or both given
  *    (then p->shared_intermediate_size > 0).
  *  topk_ids_out / topk_w_out: optional [T, k] copies of the routing (NULL = not wanted).
  *  ws: device scratch of at least moe_workspace_size(p, T, 0) bytes.
  */
 int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
-                const float* logit_bias, const int32_t* expert_map, const void* w13,
-                const void* w2, const void* shared_w13, const void* shared_w2, void* out,
-                int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                const float* logit_bias, const float* score_bias, const int32_t* expert_map,
+                const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
+                void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                 void* stream);
 
 /* ------------------------------------------------------------------ replicated experts */
@@ -291,9 +309,9 @@ int moe_eplb_tables(int32_t num_logical, int32_t num_physical, const int32_t* ph
  * errors as moe_route; eplb as above (MOE_EINVAL when it breaks the rules above).
  */
 int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
-                   const void* w_gate, const float* logit_bias, const int32_t* expert_map,
-                   int32_t* topk_ids, float* topk_w, int32_t* topk_local, void* ws,
-                   size_t ws_bytes, void* stream);
+                   const void* w_gate, const float* logit_bias, const float* score_bias,
+                   const int32_t* expert_map, int32_t* topk_ids, float* topk_w,
+                   int32_t* topk_local, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_forward with a replicated placement: w13 / w2 hold the share's physical experts (slot s
@@ -301,10 +319,11 @@ int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens
  * and errors as moe_forward.
  */
 int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
-                     const void* w_gate, const float* logit_bias, const int32_t* expert_map,
-                     const void* w13, const void* w2, const void* shared_w13,
-                     const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
-                     void* ws, size_t ws_bytes, void* stream);
+                     const void* w_gate, const float* logit_bias, const float* score_bias,
+                     const int32_t* expert_map, const void* w13, const void* w2,
+                     const void* shared_w13, const void* shared_w2, void* out,
+                     int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* ------------------------------------------------------------------ expert-parallel exchange */
 /*

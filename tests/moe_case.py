@@ -42,7 +42,8 @@ def params(w: wl.Workload, **over) -> moe.moe_params:
               use_grouped_topk=w.use_grouped_topk, num_expert_group=w.num_expert_group,
               topk_group=w.topk_group, routed_scaling_factor=w.routed_scaling_factor,
               num_local_experts=w.num_local_experts,
-              shared_intermediate_size=w.shared_intermediate_size, dtype=w.dtype)
+              shared_intermediate_size=w.shared_intermediate_size, dtype=w.dtype,
+              scoring_func=w.scoring_func)
     kw.update(over)
     return moe.make_params(**kw)
 
@@ -55,12 +56,14 @@ class Layer:
         self.x = wl.x(w, T)
         self.gate = wl.gate(w)
         self.bias = wl.logit_bias(w)
+        self.sbias = wl.score_bias(w)
         self.emap = wl.expert_map(w)
         self.w13, self.w2 = wl.local_expert_weights(w)
         self.sw13, self.sw2 = wl.shared_weights(w)
         self.d = {
             "x": dev_tensor(self.x, device), "gate": dev_tensor(self.gate, device),
             "bias": None if self.bias is None else dev_tensor(self.bias, device),
+            "sbias": None if self.sbias is None else dev_tensor(self.sbias, device),
             "emap": dev_tensor(self.emap, device),
             "w13": dev_tensor(self.w13, device), "w2": dev_tensor(self.w2, device),
             "sw13": None if self.sw13 is None else dev_tensor(self.sw13, device),
@@ -81,7 +84,7 @@ class Layer:
         sw13 = d["sw13"] if with_shared else None
         sw2 = d["sw2"] if with_shared else None
         moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"], sw13, sw2,
-                        out, ids, tw, ws)
+                        out, ids, tw, ws, score_bias=d["sbias"])
         torch.cuda.synchronize()
         return out.float().cpu().numpy(), ids.cpu().numpy(), tw.cpu().numpy()
 
@@ -94,7 +97,8 @@ class Layer:
         tw = torch.empty(T, w.top_k, dtype=torch.float32, device=dev)
         local = torch.empty(T, w.top_k, dtype=torch.int32, device=dev)
         ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
-        moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws)
+        moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws,
+                      score_bias=d["sbias"])
         torch.cuda.synchronize()
         logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts)
         return ids.cpu().numpy(), tw.cpu().numpy(), logits.cpu().numpy()
@@ -110,7 +114,8 @@ class Layer:
         w = self.w
         x = wl.to_f32(self.x if rows is None else self.x[rows])
         return oracle.route(x, wl.to_f32(self.gate), w.top_k, w.renormalize, w.use_grouped_topk,
-                            w.num_expert_group, w.topk_group, w.routed_scaling_factor, self.bias)
+                            w.num_expert_group, w.topk_group, w.routed_scaling_factor, self.bias,
+                            w.scoring_func, self.sbias)
 
     def oracle_out(self, rows, ids, weights, with_shared=True):
         w = self.w
@@ -164,7 +169,7 @@ def check_routing(w: wl.Workload, ids, weights, ref, logits=None, x=None, gate=N
         assert worst <= 1.0, f"router logits off by {worst:.3g} x the fp32 summation bound"
         own = oracle.route_from_logits(l_gpu.astype(np.float32), w.top_k, w.renormalize,
                                        w.use_grouped_topk, w.num_expert_group, w.topk_group,
-                                       w.routed_scaling_factor)
+                                       w.routed_scaling_factor, w.scoring_func, wl.score_bias(w))
         near_own = (own["gap"] < TIE_GAP) | (own["ggap"] < TIE_GAP)
         same_own = np.all(np.sort(own["ids"], 1) == gs, axis=1)
         assert np.all(same_own | near_own), "ids differ from the oracle's top-k of the GPU logits"

@@ -84,6 +84,12 @@ def test_param_errors():
         if over.get("dtype") == 7:
             p.dtype = 7
         assert moe.moe_check_params(p) == want, over
+    p = _params(w)
+    p.scoring_func = 2  # neither softmax nor sigmoid
+    assert moe.moe_check_params(p) == E
+    assert moe.moe_check_params(_params(w, scoring_func="sigmoid")) == moe.MOE_OK
+    with pytest.raises(ValueError):
+        _params(w, scoring_func="tanh")
 
 
 def test_expert_map_shares():
@@ -138,29 +144,29 @@ def test_entry_point_argument_errors():
     ws = moe.moe_workspace_size(p, T)
     F = FAKE
     # missing required pointers
-    assert L.moe_forward(pp, T, None, F, None, F, F, F, None, None, F, None, None, F, ws, None) == -1
-    assert L.moe_forward(pp, T, F, F, None, None, F, F, None, None, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, None, F, None, None, F, F, F, None, None, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, F, F, None, None, None, F, F, None, None, F, None, None, F, ws, None) == -1
     # only one of the two shared-expert pointers
-    assert L.moe_forward(pp, T, F, F, None, F, F, F, F, None, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, F, F, None, None, F, F, F, F, None, F, None, None, F, ws, None) == -1
     # workspace too small
-    assert L.moe_forward(pp, T, F, F, None, F, F, F, F, F, F, None, None, F, ws - 1, None) == -3
+    assert L.moe_forward(pp, T, F, F, None, None, F, F, F, F, F, F, None, None, F, ws - 1, None) == -3
     # tensor pointers that are not 16-byte aligned
-    assert L.moe_forward(pp, T, F + 2, F, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
-    assert L.moe_forward(pp, T, F, F, None, F, F, F, F, F, F + 8, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, F + 2, F, None, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, T, F, F, None, None, F, F, F, F, F, F + 8, None, None, F, ws, None) == -1
     assert L.moe_grouped_mlp(pp, T, F, F, F, F, F, F, 16, F + 4, F, ws, None) == -1
     assert L.moe_combine(pp, T, F, F, F, F + 2, F, None) == -1
     # negative token count
-    assert L.moe_forward(pp, -1, F, F, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
+    assert L.moe_forward(pp, -1, F, F, None, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
     # bad block_m for the split entry points
     assert L.moe_align_permute(pp, T, F, 48, F, F, F, F, F, ws, None) == -1
     assert L.moe_grouped_mlp(pp, T, F, F, F, F, F, F, 0, F, F, ws, None) == -1
     assert L.moe_align_permute(pp, T, F, 16, F, F, F, F, F, 8, None) == -3
-    assert L.moe_route(pp, T, F, F, None, F, F, F, F, F, 8, None) == -3
+    assert L.moe_route(pp, T, F, F, None, None, F, F, F, F, F, 8, None) == -3
     # shared MLP on a share without a shared expert
     p2 = _params(wl.WORKLOADS["ep_share"])
     assert L.moe_shared_mlp(ctypes.byref(p2), T, F, F, F, F, F, ws, None) == -1
     # shared expert pointers given but the params say there is none
-    assert L.moe_forward(ctypes.byref(p2), T, F, F, None, F, F, F, F, F, F, None, None, F,
+    assert L.moe_forward(ctypes.byref(p2), T, F, F, None, None, F, F, F, F, F, F, None, None, F,
                          moe.moe_workspace_size(p2, T), None) == -1
 
 
@@ -231,12 +237,12 @@ def test_eplb_tables_and_argument_errors():
     for e in [moe.moe_eplb(255, 2, F, F), moe.moe_eplb(4097, 2, F, F), moe.moe_eplb(264, 0, F, F),
               moe.moe_eplb(264, 265, F, F), moe.moe_eplb(264, 2, None, F),
               moe.moe_eplb(264, 2, F, None)]:
-        assert L.moe_route_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, F, F, F, F, F,
+        assert L.moe_route_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, None, F, F, F, F, F,
                                 ws, None) == -1
-        assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, F, F, F, None,
+        assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, None, F, F, F, None,
                                   None, F, None, None, F, ws, None) == -1
-    assert L.moe_route_eplb(ctypes.byref(p), None, T, F, F, None, F, F, F, F, F, ws, None) == -1
-    assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(good), T, F, F, None, F, F, F, None,
+    assert L.moe_route_eplb(ctypes.byref(p), None, T, F, F, None, None, F, F, F, F, F, ws, None) == -1
+    assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(good), T, F, F, None, None, F, F, F, None,
                               None, F, None, None, F, ws - 1, None) == -3
     moe.moe_route_eplb(p, good, 0, None, None, None, None, None, None, None, None, stream=0)
     moe.moe_forward_eplb(p, good, 0, None, None, None, None, None, None, None, None, None, None,

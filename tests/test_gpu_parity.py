@@ -138,7 +138,7 @@ def test_concurrent_callers_match_single_thread(case):
             for _ in range(n_calls):
                 moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"],
                                 d["sw13"], d["sw2"], b["out"], b["ids"], b["tw"], b["ws"],
-                                stream=b["st"])
+                                stream=b["st"], score_bias=d["sbias"])
                 b["st"].synchronize()
                 results[i].append((b["out"].float().cpu().numpy(), b["ids"].cpu().numpy(),
                                    b["tw"].cpu().numpy()))
@@ -211,7 +211,8 @@ def test_split_entry_points(case, block_m):
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
     tw = torch.empty(T, k, dtype=torch.float32, device=dev)
     local = torch.empty(T, k, dtype=torch.int32, device=dev)
-    moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws)
+    moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws,
+                  score_bias=d["sbias"])
     # the logits sit at the start of the workspace until the next call reuses it
     logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts).clone()
     cap = moe.moe_sorted_capacity(p, T, block_m)
@@ -360,7 +361,7 @@ def test_graph_replay_matches_eager(case):
 
     def call():
         moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"], d["sw13"],
-                        d["sw2"], out, ids, tw, ws)
+                        d["sw2"], out, ids, tw, ws, score_bias=d["sbias"])
 
     call()
     torch.cuda.synchronize()

@@ -133,6 +133,8 @@ class Workload:
     ep_rank: int = 0
     shared_intermediate_size: int = 0
     zipf_bias: float = 0.0  # s of the Zipf logit bias; 0 = none
+    scoring_func: str = "softmax"  # or "sigmoid"
+    score_bias_std: float = 0.0  # std of the seeded selection bias N(0, std^2); 0 = none
     extra: dict = field(default_factory=dict)
 
     @property
@@ -168,6 +170,12 @@ WORKLOADS = {
     "skewed": Workload("skewed", 5, "skewed-load layer, bf16 (experts 0..7 of 64)", "bf16",
                        (1, 256, 16384), 4096, 64, 3072, 8, True, ep_size=8, ep_rank=0,
                        shared_intermediate_size=3072, zipf_bias=1.2),
+    # routing variants: sigmoid scores, selection-only bias, group score = top-2 sum
+    "dsv3": Workload("dsv3", 6, "DeepSeek-V3-shaped layer, bf16 (experts 0..31 of 256, sigmoid "
+                     "scores with a selection bias)", "bf16", (32, 4096), 7168, 256, 2048, 8, True,
+                     use_grouped_topk=True, num_expert_group=8, topk_group=4,
+                     routed_scaling_factor=2.5, ep_size=8, ep_rank=0,
+                     shared_intermediate_size=2048, scoring_func="sigmoid", score_bias_std=0.05),
 }
 
 
@@ -205,6 +213,13 @@ def logit_bias(w: Workload):
         return None
     e = np.arange(w.num_experts, dtype=np.float64)
     return (-w.zipf_bias * np.log(e + 1.0)).astype(np.float32)
+
+
+def score_bias(w: Workload):
+    """fp32 [E] selection-only score bias (seeded N(0, std^2)), or None."""
+    if not w.score_bias_std:
+        return None
+    return normal((w.cid, 5, 0), w.num_experts, w.score_bias_std).astype(np.float32)
 
 
 def _storage(w: Workload):
