@@ -13,6 +13,9 @@ gate/up and down GEMMs, combine); inputs are resident in HBM before timing start
 expert-parallel exchange around the path (dispatch and unpack, at the workload's EP degree)
 is timed on the step's routing and reported in the ``ep_exchange`` field.
 
+Warm-up: the requested W steps, extended until at least 0.3 s of steps have run (the GPU clock
+ramps over the first tens of milliseconds of load; ``warmup_run`` reports the count).
+
 The dominant kernel's duration comes from HIP events recorded on the launch stream
 around ``moe_expert_gate_up`` in a second timed loop that runs the same kernels through
 the split entry points. The oracle (CPU, float64 expert MLPs) is timed on a bounded
@@ -214,12 +217,30 @@ def algorithmic(w, T, ids):
             "rows_per_expert_min": int(counts.min()), "rows_per_expert_max": int(counts.max())}
 
 
+WARM_SECONDS = 0.3
+
+
+def warm_up(fn, steps):
+    """Untimed calls of fn: at least `steps`, and for at least WARM_SECONDS of GPU time. The
+    GPU's clock ramps over the first tens of milliseconds of load (and again after an idle
+    gap): a Mixtral-shaped step takes 3.4 ms at first and settles at 2.66 ms after about
+    30 steps, so a fixed handful of warm-up steps would time the ramp. Returns the count."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < steps or time.perf_counter() - t0 < WARM_SECONDS:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def run_point(host, w, T, steps, warmup):
     import torch
     b = Bench(w, T, host)
-    for _ in range(warmup):
-        b.forward()
-    torch.cuda.synchronize()
+    b.warmup_run = warm_up(b.forward, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         b.forward()
@@ -229,8 +250,7 @@ def run_point(host, w, T, steps, warmup):
     alg = algorithmic(w, T, ids)
 
     # second timed loop: same kernels, HIP events on the launch stream at stage ends
-    b.split_step()
-    torch.cuda.synchronize()
+    warm_up(b.split_step, 1)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -296,10 +316,7 @@ def run_exchange(w, T, ep, x, ids, tw, steps, warmup):
     def unpack():  # the returned rows stand in place: send_x plays recv_y
         moe.moe_ep_combine(p, T, send_pos, send_x, out)
 
-    for _ in range(warmup):
-        dispatch()
-        unpack()
-    torch.cuda.synchronize()
+    warm_up(lambda: (dispatch(), unpack()), warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -368,9 +385,7 @@ def run_eplb(host, w, T, extra, steps, warmup):
             else:
                 moe.moe_forward_eplb(p, eplb, T, x, gate, bias, emap, w13, w2, None, None, out,
                                      ids, tw, ws, score_bias=sbias)
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
+        warm_up(call, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
@@ -494,6 +509,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": b.warmup_run,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
