@@ -39,7 +39,10 @@ grouped top-k scores a group by its largest softmax probability, keeps ``topk_gr
 groups and picks top-k among their experts; ties go to the lower expert (or group) id;
 renormalisation is over all k global picks, before the expert_map mask; the routed
 scaling factor multiplies the routing weights after renormalisation and does not touch
-the shared expert; the routing weight multiplies the expert output (after W2).
+the shared expert; the routing weight multiplies the expert output (after W2). The
+activation switch ``swigluoai`` is gpt-oss's clamped SwiGLU (alpha 1.702, limit 7) and the
+expert biases (``has_bias``) are added to the gate/up pre-activations and to the expert
+output; the pages name both without their formulas.
 
 Pins: every function here is checked by the ``not gpu`` tests against closed forms,
 library routines on special cases, brute force on tiny inputs and invariants of the
@@ -47,6 +50,8 @@ method (see the tests of the oracle). The absolute outputs of the large workload
 pinned only through those checks.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -201,25 +206,50 @@ def route(x, w_gate, top_k, renormalize, use_grouped_topk=False, num_expert_grou
                              routed_scaling_factor, scoring_func, score_bias)
 
 
-def gated_mlp(x, w13, w2):
-    """fp64 gated-SiLU expert MLP on rows of x: W2 (silu(W1 x) * (W3 x)).
+SWIGLUOAI_ALPHA = 1.702
+SWIGLUOAI_LIMIT = 7.0
+
+
+def gated_mlp(x, w13, w2, activation="silu", b13=None, b2=None):
+    """fp64 gated expert MLP on rows of x: W2 act(W1 x + b1, W3 x + b3) + b2.
 
     ``w13`` is [2I, H] with the W1 (gate) rows first and the W3 (up) rows after them, the
     packed ``gate_up_proj`` (E, 2I, H) of ``recursive_replace``; ``w2`` is [H, I].
-    silu(g) = g / (1 + exp(-g)).
+    ``activation`` (``recursive_replace`` picks ``"silu"``, or ``"swigluoai"`` for gpt-oss;
+    the page names the switch, not the formula):
+      silu:      act(g, u) = g / (1 + exp(-g)) * u
+      swigluoai: g' = min(g, 7), u' = clip(u, -7, 7), act = g' / (1 + exp(-1.702 g')) * (u' + 1)
+                 (gpt-oss's clamped SwiGLU).
+    ``b13`` [2I] (gate biases, then up biases) and ``b2`` [H] are the expert biases
+    (``has_bias`` of ``recursive_replace``), or None.
     """
     x64 = np.asarray(x, np.float64)
     w13 = np.asarray(w13, np.float64)
     I = w13.shape[0] // 2
     g = x64 @ w13[:I].T
     u = x64 @ w13[I:].T
+    if b13 is not None:
+        b = np.asarray(b13, np.float64)
+        g = g + b[:I]
+        u = u + b[I:]
     with np.errstate(over="ignore"):
-        a = g / (1.0 + np.exp(-g)) * u
-    return a @ np.asarray(w2, np.float64).T
+        if activation == "silu":
+            a = g / (1.0 + np.exp(-g)) * u
+        elif activation == "swigluoai":
+            g = np.minimum(g, SWIGLUOAI_LIMIT)
+            u = np.clip(u, -SWIGLUOAI_LIMIT, SWIGLUOAI_LIMIT)
+            a = g / (1.0 + np.exp(-SWIGLUOAI_ALPHA * g)) * (u + 1.0)
+        else:
+            raise ValueError(activation)
+    y = a @ np.asarray(w2, np.float64).T
+    if b2 is not None:
+        y = y + np.asarray(b2, np.float64)
+    return y
 
 
 def moe_forward_given_routing(x, ids, weights, expert_map, w13_local, w2_local,
-                              shared_w13=None, shared_w2=None):
+                              shared_w13=None, shared_w2=None, activation="silu", b13_local=None,
+                              b2_local=None):
     """One share's output [T, H] (fp64) for given routing, as ``MixtralMoE.forward`` does it.
 
     For each local expert (slot s of ``expert_map``): the per-token weight is the sum over
@@ -229,7 +259,9 @@ def moe_forward_given_routing(x, ids, weights, expert_map, w13_local, w2_local,
     the same value for finite inputs. Experts outside the share (map value -1)
     contribute nothing. The shared expert, if given, is added with weight 1 ("Expert
     Parallel" Step 5). ``w13_local[s]`` / ``w2_local[s]`` may be any per-slot sequence
-    of arrays (converted one slot at a time).
+    of arrays (converted one slot at a time). ``activation`` applies to every expert,
+    shared included; the expert biases ``b13_local[s]`` / ``b2_local[s]`` (or None) belong to
+    the routed experts, whose weighted output includes them.
     """
     x64 = np.asarray(x, np.float64)
     T, H = x64.shape
@@ -244,9 +276,11 @@ def moe_forward_given_routing(x, ids, weights, expert_map, w13_local, w2_local,
         if rows.size == 0:
             continue
         w_tok = (wts * hit).sum(axis=1)
-        out[rows] += w_tok[rows, None] * gated_mlp(x64[rows], w13_local[s], w2_local[s])
+        out[rows] += w_tok[rows, None] * gated_mlp(
+            x64[rows], w13_local[s], w2_local[s], activation,
+            None if b13_local is None else b13_local[s], None if b2_local is None else b2_local[s])
     if shared_w13 is not None:
-        out += gated_mlp(x64, shared_w13, shared_w2)
+        out += gated_mlp(x64, shared_w13, shared_w2, activation)
     return out
 
 
@@ -262,7 +296,8 @@ def moe_forward(x, w_gate, expert_map, w13_local, w2_local, top_k, renormalize,
 
 
 def moe_forward_per_token(x, ids, weights, expert_map, w13_local, w2_local,
-                          shared_w13=None, shared_w2=None):
+                          shared_w13=None, shared_w2=None, activation="silu", b13_local=None,
+                          b2_local=None):
     """The per-token definition, with Python loops (small inputs only).
 
     out[t] = sum over slots j whose expert is local of weights[t, j] * MLP(x[t]) (+ shared
@@ -274,16 +309,23 @@ def moe_forward_per_token(x, ids, weights, expert_map, w13_local, w2_local,
     out = np.zeros((T, H), np.float64)
     emap = np.asarray(expert_map)
 
-    def mlp_row(xt, w13, w2):
+    def mlp_row(xt, w13, w2, b13=None, b2=None):
         w13 = np.asarray(w13, np.float64)
         w2 = np.asarray(w2, np.float64)
         I = w13.shape[0] // 2
         act = np.empty(I)
         for i in range(I):
-            g = float(np.dot(w13[i], xt))
-            u = float(np.dot(w13[I + i], xt))
-            act[i] = g / (1.0 + np.exp(-g)) * u if g > -700 else 0.0
-        return np.array([float(np.dot(w2[h], act)) for h in range(w2.shape[0])])
+            g = float(np.dot(w13[i], xt)) + (0.0 if b13 is None else float(b13[i]))
+            u = float(np.dot(w13[I + i], xt)) + (0.0 if b13 is None else float(b13[I + i]))
+            if activation == "swigluoai":
+                g = min(g, SWIGLUOAI_LIMIT)
+                u = max(-SWIGLUOAI_LIMIT, min(u, SWIGLUOAI_LIMIT))
+                act[i] = g / (1.0 + math.exp(-SWIGLUOAI_ALPHA * g)) * (u + 1.0) \
+                    if SWIGLUOAI_ALPHA * g > -700 else 0.0
+            else:
+                act[i] = g / (1.0 + np.exp(-g)) * u if g > -700 else 0.0
+        return np.array([float(np.dot(w2[h], act)) + (0.0 if b2 is None else float(b2[h]))
+                         for h in range(w2.shape[0])])
 
     for t in range(T):
         acc = np.zeros(H)
@@ -291,7 +333,9 @@ def moe_forward_per_token(x, ids, weights, expert_map, w13_local, w2_local,
             s = int(emap[int(ids[t, j])])
             if s < 0:
                 continue
-            acc += float(weights[t, j]) * mlp_row(x64[t], w13_local[s], w2_local[s])
+            acc += float(weights[t, j]) * mlp_row(
+                x64[t], w13_local[s], w2_local[s], None if b13_local is None else b13_local[s],
+                None if b2_local is None else b2_local[s])
         if shared_w13 is not None:
             acc += mlp_row(x64[t], shared_w13, shared_w2)
         out[t] = acc
@@ -458,7 +502,7 @@ def eplb_local_slots(topk_ids, top_k, logical_to_physical, replica_count, phys_e
 
 
 def moe_forward_given_slots(x, slots, weights, w13_local, w2_local, shared_w13=None,
-                            shared_w2=None):
+                            shared_w2=None, activation="silu", b13_local=None, b2_local=None):
     """One share's output [T, H] (fp64) given each pair's local slot (-1: not this share).
 
     The same sum as ``moe_forward_given_routing`` with the slot of each pair given directly
@@ -475,7 +519,9 @@ def moe_forward_given_slots(x, slots, weights, w13_local, w2_local, shared_w13=N
         if rows.size == 0:
             continue
         w_tok = (wts * hit).sum(axis=1)
-        out[rows] += w_tok[rows, None] * gated_mlp(x64[rows], w13_local[s], w2_local[s])
+        out[rows] += w_tok[rows, None] * gated_mlp(
+            x64[rows], w13_local[s], w2_local[s], activation,
+            None if b13_local is None else b13_local[s], None if b2_local is None else b2_local[s])
     if shared_w13 is not None:
-        out += gated_mlp(x64, shared_w13, shared_w2)
+        out += gated_mlp(x64, shared_w13, shared_w2, activation)
     return out

@@ -607,3 +607,71 @@ def test_grouped_with_bias_and_groups_of_one_is_plain_topk():
     g = oracle.route_from_logits(l, 3, True, True, 16, 16, scoring_func="sigmoid", score_bias=b)
     pl = oracle.route_from_logits(l, 3, True, scoring_func="sigmoid", score_bias=b)
     assert np.array_equal(g["ids"], pl["ids"]) and np.array_equal(g["weights"], pl["weights"])
+
+
+# ---------------------------------------------------------------- MLP variants
+def _unit_mlp(g, u, activation, b13=None, b2=None):
+    """One-row MLP whose gate and up pre-activations are the inputs themselves (H = 2, I = 1,
+    identity W1/W3 rows), read out through W2 = [1, 0]^T."""
+    w13 = np.array([[1.0, 0.0], [0.0, 1.0]])
+    w2 = np.array([[1.0], [0.0]])
+    return oracle.gated_mlp(np.array([[g, u]]), w13, w2, activation, b13, b2)[0]
+
+
+def test_swigluoai_closed_forms():
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))
+    assert _unit_mlp(1.0, 0.0, "swigluoai")[0] == pytest.approx(sig(1.702), rel=1e-15)
+    assert _unit_mlp(-2.0, 3.0, "swigluoai")[0] == pytest.approx(-2.0 * sig(-3.404) * 4.0, rel=1e-15)
+    # gate clamped above at 7, up clamped to [-7, 7]
+    assert _unit_mlp(10.0, 9.0, "swigluoai")[0] == pytest.approx(7.0 * sig(7 * 1.702) * 8.0, rel=1e-15)
+    assert _unit_mlp(2.0, -9.0, "swigluoai")[0] == pytest.approx(2.0 * sig(3.404) * -6.0, rel=1e-15)
+    assert _unit_mlp(-50.0, 1.0, "swigluoai")[0] == pytest.approx(-50.0 * sig(-85.1) * 2.0, rel=1e-12)
+    # up = -1 cancels the gate; silu at the same point for contrast
+    assert _unit_mlp(3.0, -1.0, "swigluoai")[0] == 0.0
+    assert _unit_mlp(1.0, 2.0, "silu")[0] == pytest.approx(sig(1.0) * 2.0, rel=1e-15)
+    with pytest.raises(ValueError):
+        _unit_mlp(1.0, 1.0, "gelu")
+
+
+def test_expert_biases_are_affine_shifts():
+    """A gate/up bias is a weight column on a constant input of 1; an output bias adds itself."""
+    x, _, w13, w2, _, _ = _tiny_layer(E=1, H=24, I=16, T=9, seed=7)
+    b13 = _rand((32,), (905, 0, 0))
+    b2 = _rand((24,), (905, 0, 1))
+    for act in ("silu", "swigluoai"):
+        with_b = oracle.gated_mlp(x, w13[0], w2[0], act, b13, None)
+        aug = oracle.gated_mlp(np.hstack([x, np.ones((9, 1))]), np.hstack([w13[0], b13[:, None]]),
+                               w2[0], act)
+        assert np.allclose(with_b, aug, rtol=1e-13, atol=1e-13)
+        d = oracle.gated_mlp(x, w13[0], w2[0], act, b13, b2) - with_b
+        assert np.allclose(d, np.broadcast_to(b2, d.shape), rtol=0, atol=1e-13)
+        zero = oracle.gated_mlp(x, w13[0], w2[0], act, np.zeros(32), np.zeros(24))
+        assert np.array_equal(zero, oracle.gated_mlp(x, w13[0], w2[0], act))
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_mlp_variants_share_sum_and_per_token_form(R):
+    """swigluoai with expert biases: the vectorised per-expert form equals the per-token loop,
+    and the shares (shared expert on one of them) sum to the all-local layer."""
+    E, H, I, T, k = 8, 24, 16, 10, 3
+    x, _, w13, w2, sw13, sw2 = _tiny_layer(E=E, H=H, I=I, T=T, seed=8, shared_I=8)
+    x = 3.0 * x  # reach the clamps
+    b13 = _rand((E, 2 * I), (906, 0, 0))
+    b2 = _rand((E, H), (906, 0, 1))
+    ids = _distinct_ids(T, k, E, 14)
+    w = np.random.default_rng(15).uniform(0.1, 1.0, (T, k))
+    kw = dict(activation="swigluoai", b13_local=b13, b2_local=b2)
+    full = oracle.moe_forward_given_routing(x, ids, w, np.arange(E), w13, w2, sw13, sw2, **kw)
+    per_tok = oracle.moe_forward_per_token(x, ids, w, np.arange(E), w13, w2, sw13, sw2, **kw)
+    assert np.allclose(full, per_tok, rtol=1e-12, atol=1e-12)
+    per = E // R
+    total = np.zeros((T, H))
+    for r in range(R):
+        emap = np.full(E, -1)
+        emap[r * per:(r + 1) * per] = np.arange(per)
+        sl = slice(r * per, (r + 1) * per)
+        sh = (sw13, sw2) if r == 0 else (None, None)
+        total += oracle.moe_forward_given_routing(x, ids, w, emap, w13[sl], w2[sl], *sh,
+                                                  activation="swigluoai", b13_local=b13[sl],
+                                                  b2_local=b2[sl])
+    assert np.allclose(total, full, rtol=1e-12, atol=1e-12)
