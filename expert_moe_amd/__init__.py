@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libexpert_moe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_ACT_SILU, MOE_ACT_SWIGLUOAI = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -55,6 +56,7 @@ class moe_params(ctypes.Structure):
         ("shared_intermediate_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("scoring_func", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
     ]
 
 
@@ -80,19 +82,26 @@ def make_eplb(num_physical_experts, max_replicas, logical_to_physical, replica_c
 def make_params(num_experts, top_k, hidden_size, intermediate_size, renormalize=True,
                 use_grouped_topk=False, num_expert_group=1, topk_group=1,
                 routed_scaling_factor=1.0, num_local_experts=None, shared_intermediate_size=0,
-                dtype="bf16", scoring_func="softmax") -> moe_params:
+                dtype="bf16", scoring_func="softmax", activation="silu") -> moe_params:
     if scoring_func in ("softmax", MOE_SCORE_SOFTMAX):
         sf = MOE_SCORE_SOFTMAX
     elif scoring_func in ("sigmoid", MOE_SCORE_SIGMOID):
         sf = MOE_SCORE_SIGMOID
     else:
         raise ValueError(f"scoring_func {scoring_func!r}")
+    if activation in ("silu", MOE_ACT_SILU):
+        act = MOE_ACT_SILU
+    elif activation in ("swigluoai", MOE_ACT_SWIGLUOAI):
+        act = MOE_ACT_SWIGLUOAI
+    else:
+        raise ValueError(f"activation {activation!r}")
     return moe_params(
         int(num_experts), int(top_k), int(hidden_size), int(intermediate_size),
         int(bool(renormalize)), int(bool(use_grouped_topk)), int(num_expert_group),
         int(topk_group), float(routed_scaling_factor),
         int(num_experts if num_local_experts is None else num_local_experts),
-        int(shared_intermediate_size), MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32, sf)
+        int(shared_intermediate_size), MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32, sf,
+        act)
 
 
 _lib = None
@@ -109,14 +118,14 @@ _SIGS = {
     "moe_weight_bytes": ([_i64, _i64, _i64, _i32, _i64], _i64),
     "moe_route": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_align_permute": ([_P, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
-    "moe_grouped_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
-                        ctypes.c_int),
-    "moe_expert_gate_up": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
-    "moe_expert_down": ([_P, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
+    "moe_grouped_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz,
+                         _vp], ctypes.c_int),
+    "moe_expert_gate_up": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
+    "moe_expert_down": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "moe_shared_mlp": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_combine": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_forward": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                     _sz, _vp], ctypes.c_int),
+                     _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_ep_send_capacity": ([_P, _i64, _i32], _i64),
     "moe_ep_workspace_size": ([_P, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "moe_ep_dispatch": ([_P, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -126,7 +135,7 @@ _SIGS = {
     "moe_route_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                        ctypes.c_int),
     "moe_forward_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                          _vp, _vp, _sz, _vp], ctypes.c_int),
+                          _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -231,22 +240,23 @@ def moe_align_permute(p, num_tokens, topk_local, block_m, sorted_pairs, block_ex
 
 
 def moe_grouped_mlp(p, num_tokens, x, w13, w2, sorted_pairs, block_expert, num_padded, block_m,
-                    y, ws, stream=None):
+                    y, ws, stream=None, b13=None, b2=None):
     wp, wn = _ws(ws)
     _check(lib().moe_grouped_mlp(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(w2),
-                                 _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
+                                 _ptr(b13), _ptr(b2), _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
                                  block_m, _ptr(y), wp, wn, _stream(stream)), "moe_grouped_mlp")
 
 
 def moe_expert_gate_up(p, num_tokens, x, w13, sorted_pairs, block_expert, num_padded, block_m,
-                       act, stream=None):
-    _check(lib().moe_expert_gate_up(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13),
+                       act, stream=None, b13=None):
+    _check(lib().moe_expert_gate_up(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(b13),
                                     _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
                                     block_m, _ptr(act), _stream(stream)), "moe_expert_gate_up")
 
 
-def moe_expert_down(p, num_tokens, act, w2, block_expert, num_padded, block_m, y, stream=None):
-    _check(lib().moe_expert_down(ctypes.byref(p), num_tokens, _ptr(act), _ptr(w2),
+def moe_expert_down(p, num_tokens, act, w2, block_expert, num_padded, block_m, y, stream=None,
+                    b2=None):
+    _check(lib().moe_expert_down(ctypes.byref(p), num_tokens, _ptr(act), _ptr(w2), _ptr(b2),
                                  _ptr(block_expert), _ptr(num_padded), block_m, _ptr(y),
                                  _stream(stream)), "moe_expert_down")
 
@@ -264,12 +274,14 @@ def moe_combine(p, num_tokens, y, pair_row, topk_w, shared_y, out, stream=None):
 
 
 def moe_forward(p, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
-                shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None):
+                shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None,
+                b13=None, b2=None):
     wp, wn = _ws(ws)
     _check(lib().moe_forward(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w_gate), _ptr(logit_bias),
-                             _ptr(score_bias), _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(shared_w13),
-                             _ptr(shared_w2), _ptr(out), _ptr(topk_ids_out), _ptr(topk_w_out),
-                             wp, wn, _stream(stream)), "moe_forward")
+                             _ptr(score_bias), _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(b13),
+                             _ptr(b2), _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
+                             _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
+           "moe_forward")
 
 
 def moe_ep_send_capacity(p, num_tokens: int, ep_size: int) -> int:
@@ -323,11 +335,12 @@ def moe_route_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, topk_
 
 
 def moe_forward_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
-                     shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None):
+                     shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None,
+                     b13=None, b2=None):
     wp, wn = _ws(ws)
     _check(lib().moe_forward_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
                                   _ptr(w_gate), _ptr(logit_bias), _ptr(score_bias),
-                                  _ptr(expert_map), _ptr(w13),
-                                  _ptr(w2), _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
+                                  _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(b13), _ptr(b2),
+                                  _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
                                   _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
            "moe_forward_eplb")

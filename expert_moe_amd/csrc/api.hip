@@ -25,6 +25,7 @@ int check_params(const moe_params* p) {
   if (!p) return MOE_EINVAL;
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (p->scoring_func != MOE_SCORE_SOFTMAX && p->scoring_func != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (p->activation != MOE_ACT_SILU && p->activation != MOE_ACT_SWIGLUOAI) return MOE_EINVAL;
   const int E = p->num_experts;
   if (E < 1 || p->top_k < 1 || p->top_k > E) return MOE_EINVAL;
   if (!mult64(p->hidden_size) || !mult64(p->intermediate_size)) return MOE_EINVAL;
@@ -282,7 +283,8 @@ int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* to
 }
 
 int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
-                    const void* w2, const int32_t* sorted_pairs, const int32_t* block_expert,
+                    const void* w2, const float* b13, const float* b2,
+                    const int32_t* sorted_pairs, const int32_t* block_expert,
                     const int32_t* num_padded, int32_t block_m, void* y, void* ws,
                     size_t ws_bytes, void* stream) {
   int rc = check_params(p);
@@ -292,17 +294,17 @@ int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, cons
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w13 || !w2 || !sorted_pairs || !block_expert || !num_padded || !y || !ws)
     return MOE_EINVAL;
-  if (!aligned16({x, w13, w2, y, ws})) return MOE_EINVAL;
+  if (!aligned16({x, w13, w2, b13, b2, y, ws})) return MOE_EINVAL;
   const Layout L = layout(*p, num_tokens, block_m);
   if (ws_bytes < L.mlp_need) return MOE_ENOSPC;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_mlp(*p, static_cast<int>(num_tokens), x, w13, w2, p->intermediate_size,
                          sorted_pairs, num_padded, block_expert, block_m, rows, ws, y,
-                         as_stream(stream));
+                         as_stream(stream), b13, b2);
 }
 
 int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
-                       const int32_t* sorted_pairs, const int32_t* block_expert,
+                       const float* b13, const int32_t* sorted_pairs, const int32_t* block_expert,
                        const int32_t* num_padded, int32_t block_m, void* act, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
@@ -310,26 +312,26 @@ int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, c
   if (!valid_block_m(block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w13 || !sorted_pairs || !block_expert || !num_padded || !act) return MOE_EINVAL;
-  if (!aligned16({x, w13, act})) return MOE_EINVAL;
+  if (!aligned16({x, w13, b13, act})) return MOE_EINVAL;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_gate_up(*p, static_cast<int>(num_tokens), x, w13, p->intermediate_size,
                              sorted_pairs, num_padded, block_expert, block_m, rows, act,
-                             as_stream(stream));
+                             as_stream(stream), b13);
 }
 
 int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, const void* w2,
-                    const int32_t* block_expert, const int32_t* num_padded, int32_t block_m,
-                    void* y, void* stream) {
+                    const float* b2, const int32_t* block_expert, const int32_t* num_padded,
+                    int32_t block_m, void* y, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
   if (!valid_block_m(block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!act || !w2 || !block_expert || !num_padded || !y) return MOE_EINVAL;
-  if (!aligned16({act, w2, y})) return MOE_EINVAL;
+  if (!aligned16({act, w2, b2, y})) return MOE_EINVAL;
   const int rows = static_cast<int>(capacity(*p, num_tokens, block_m));
   return moe::launch_down(*p, static_cast<int>(num_tokens), act, w2, p->intermediate_size,
-                          num_padded, block_expert, block_m, rows, y, as_stream(stream));
+                          num_padded, block_expert, block_m, rows, y, as_stream(stream), b2);
 }
 
 int moe_shared_mlp(const moe_params* p, int64_t num_tokens, const void* x,
@@ -365,9 +367,10 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
 static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num_tokens,
                         const void* x, const void* w_gate, const float* logit_bias,
                         const float* score_bias, const int32_t* expert_map, const void* w13,
-                        const void* w2, const void* shared_w13, const void* shared_w2,
-                        void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        const void* w2, const float* b13, const float* b2,
+                        const void* shared_w13, const void* shared_w2, void* out,
+                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                        void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
@@ -376,7 +379,7 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t n
   if (shared && p->shared_intermediate_size == 0) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w_gate || !expert_map || !w13 || !w2 || !out || !ws) return MOE_EINVAL;
-  if (!aligned16({x, w_gate, w13, w2, shared_w13, shared_w2, out, ws})) return MOE_EINVAL;
+  if (!aligned16({x, w_gate, w13, w2, b13, b2, shared_w13, shared_w2, out, ws})) return MOE_EINVAL;
   const int bm = pick_block_m(*p, num_tokens);
   const Layout L = layout(*p, num_tokens, bm);
   if (ws_bytes < L.total) return MOE_ENOSPC;
@@ -427,7 +430,7 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t n
     return rc;
   const int rows = static_cast<int>(capacity(*p, T, bm));
   if ((rc = moe::launch_mlp(*p, T, x, w13, w2, p->intermediate_size, sorted_pairs, num_padded,
-                            block_expert, bm, rows, scratch, y, s)))
+                            block_expert, bm, rows, scratch, y, s, b13, b2)))
     return rc;
   if (side) {
     if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return MOE_EHIP;
@@ -439,12 +442,12 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t n
 
 int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
                 const float* logit_bias, const float* score_bias, const int32_t* expert_map,
-                const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
-                void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                void* stream) {
+                const void* w13, const void* w2, const float* b13, const float* b2,
+                const void* shared_w13, const void* shared_w2, void* out, int32_t* topk_ids_out,
+                float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, w13,
-                      w2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes,
-                      stream);
+                      w2, b13, b2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws,
+                      ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -503,14 +506,15 @@ int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens
 int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
                      const void* w_gate, const float* logit_bias, const float* score_bias,
                      const int32_t* expert_map, const void* w13, const void* w2,
-                     const void* shared_w13, const void* shared_w2, void* out,
-                     int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     const float* b13, const float* b2, const void* shared_w13,
+                     const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, void* stream) {
   moe::EplbMap m;
   int rc = check_eplb(p, eplb, &m);
   if (rc) return rc;
   return forward_impl(p, &m, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, w13, w2,
-                      shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+                      b13, b2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes,
+                      stream);
 }
 
 }  // extern "C"

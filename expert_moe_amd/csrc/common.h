@@ -43,6 +43,19 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// gpt-oss's clamped SwiGLU ("swigluoai"): the gate is clamped above at 7 and the up value to
+// [-7, 7]; act = g * sigmoid(1.702 g) * (u + 1).
+__device__ __forceinline__ float swigluoai_mul(float g, float u) {
+  g = fminf(g, 7.0f);
+  u = fminf(fmaxf(u, -7.0f), 7.0f);
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
+}
+
+// The activation of the gate/up pair: act 0 = silu, 1 = swigluoai (MOE_ACT_*).
+__device__ __forceinline__ float act_mul(float g, float u, int act) {
+  return act == 1 ? swigluoai_mul(g, u) : silu_mul(g, u);
+}
+
 // 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes at
 // base + voff land at LDS byte address lds_addr + 16 l; base and lds_addr are wave-uniform.
 // Written as inline asm on purpose: the compiler has to assume that such a load may touch

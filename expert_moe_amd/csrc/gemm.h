@@ -6,9 +6,10 @@
 // (src(r) = sorted_pairs[r] / top_k, padding rows read token 0) or taken in order
 // (identity, for the shared expert and the router). B is a weight matrix stored with the
 // reduction dimension contiguous ([rows, K]), selected per block of rows by block_expert.
-// Epilogues: fused silu(gate) * up for the w13 projection (gate rows [0, N), up rows
-// [N, 2N) of B), plain bf16 store for the w2 projection, bounded fp32 store for router
-// logits.
+// Epilogues: fused act(gate + b_gate, up + b_up) for the w13 projection (gate rows [0, N), up
+// rows [N, 2N) of B; act = silu(g) * u or gpt-oss's clamped SwiGLU; the per-slot biases
+// optional), bf16 store (+ optional per-slot bias) for the w2 projection, bounded fp32 store
+// for router logits.
 #pragma once
 
 #include <type_traits>
@@ -47,6 +48,10 @@ struct GemmArgs {
                                // tail (tail_tiles); 2: the quarter tiles (half BM, half BNR) of the
                                // tail of the tiling with twice this kernel's BM and BNR
   int32_t n_cu;                // tiles per round (one workgroup per CU) for the tail rule
+  const float* bias;           // kSiluMul: [slots, 2N] gate then up biases; kStore: [slots, N];
+                               // slot s at bias + s * bias_stride; NULL = none
+  int64_t bias_stride;
+  int32_t act;                 // kSiluMul: 0 = silu, 1 = swigluoai
 };
 
 // K range [k0, k0 + klen) of this workgroup (blockIdx.y selects the split).
@@ -479,6 +484,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
     // 16..23 of the block and lane l + 32 columns 8..15 and 24..31: two 16-byte stores.
     constexpr int OUTB = MODE == kSiluMul ? TNB / 2 : TNB;  // 32-column output blocks per wave
     const int col0 = (MODE == kSiluMul ? nt * (BNR / 2) + wn * (TNR / 2) : nt * BNR + wn * TNR) + 8 * (lane >> 5);
+    // column of register 4 q + 2 h (and + 1) of block j before the lane swap:
+    // colb + 32 j + 8 q + 2 h
+    const int colb = col0 - 8 * (lane >> 5) + 4 * (lane >> 5);
+    const float* const bias = a.bias ? a.bias + slot * a.bias_stride : nullptr;
+    const int act = a.act;
 #pragma unroll
     for (int i = 0; i < TMB; ++i) {
       const int row = orow + i * 32;
@@ -492,11 +502,32 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
           for (int h = 0; h < 2; ++h) {
             float v0, v1;
             if constexpr (MODE == kSiluMul) {
-              v0 = silu_mul(acc[i][j][4 * q + 2 * h], acc[i][j + TNB / 2][4 * q + 2 * h]);
-              v1 = silu_mul(acc[i][j][4 * q + 2 * h + 1], acc[i][j + TNB / 2][4 * q + 2 * h + 1]);
+              float g0 = acc[i][j][4 * q + 2 * h], g1 = acc[i][j][4 * q + 2 * h + 1];
+              float u0 = acc[i][j + TNB / 2][4 * q + 2 * h], u1 = acc[i][j + TNB / 2][4 * q + 2 * h + 1];
+              if (bias) {
+                const int c = colb + 32 * j + 8 * q + 2 * h;
+                const float2 bg = *reinterpret_cast<const float2*>(bias + c);
+                const float2 bu = *reinterpret_cast<const float2*>(bias + a.N + c);
+                g0 += bg.x;
+                g1 += bg.y;
+                u0 += bu.x;
+                u1 += bu.y;
+              }
+              if (act == 0) {
+                v0 = silu_mul(g0, u0);
+                v1 = silu_mul(g1, u1);
+              } else {
+                v0 = swigluoai_mul(g0, u0);
+                v1 = swigluoai_mul(g1, u1);
+              }
             } else {
               v0 = acc[i][j][4 * q + 2 * h];
               v1 = acc[i][j][4 * q + 2 * h + 1];
+              if (bias) {
+                const float2 b = *reinterpret_cast<const float2*>(bias + colb + 32 * j + 8 * q + 2 * h);
+                v0 += b.x;
+                v1 += b.y;
+              }
             }
             p[q][h] = pack_bf16x2(v0, v1);
           }
@@ -630,12 +661,20 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
     const float v = red[0][i][nb][r][l] + red[1][i][nb][r][l] + red[2][i][nb][r][l] + red[3][i][nb][r][l];
     if (MODE == kSiluMul) {
       const int nu = nb + NB / 2;
-      const float u = red[0][i][nu][r][l] + red[1][i][nu][r][l] + red[2][i][nu][r][l] + red[3][i][nu][r][l];
+      float u = red[0][i][nu][r][l] + red[1][i][nu][r][l] + red[2][i][nu][r][l] + red[3][i][nu][r][l];
+      float g = v;
+      const int col = nt * (BNR / 2) + nb * 16 + (l & 15);
+      if (a.bias) {
+        g += a.bias[slot * a.bias_stride + col];
+        u += a.bias[slot * a.bias_stride + a.N + col];
+      }
       uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
-      C[nt * (BNR / 2) + nb * 16 + (l & 15)] = f32_to_bf16(silu_mul(v, u));
+      C[col] = f32_to_bf16(act_mul(g, u, a.act));
     } else if (MODE == kStore) {
+      const int col = nt * BNR + nb * 16 + (l & 15);
+      const float b = a.bias ? a.bias[slot * a.bias_stride + col] : 0.f;
       uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc;
-      C[nt * BNR + nb * 16 + (l & 15)] = f32_to_bf16(v);
+      C[col] = f32_to_bf16(a.bias ? v + b : v);
     } else {
       const int col = nt * BNR + nb * 16 + (l & 15);
       if (col < a.N_valid)
@@ -704,13 +743,19 @@ __global__ void __launch_bounds__(256) gemm_f32_tile(GemmArgs a) {
   const int row = m0 + ty;
   if (row >= a.M_rows) return;
   float* C = static_cast<float*>(a.C) + static_cast<int64_t>(row) * a.ldc;
+  const float* const bias = a.bias ? a.bias + slot * a.bias_stride : nullptr;
   if (MODE == kSiluMul) {
-    C[nt * (BNR / 2) + 2 * tx] = silu_mul(acc[0], acc[2]);
-    C[nt * (BNR / 2) + 2 * tx + 1] = silu_mul(acc[1], acc[3]);
+    for (int c = 0; c < 2; ++c) {
+      const int col = nt * (BNR / 2) + 2 * tx + c;
+      const float g = acc[c] + (bias ? bias[col] : 0.f);
+      const float u = acc[2 + c] + (bias ? bias[a.N + col] : 0.f);
+      C[col] = act_mul(g, u, a.act);
+    }
   } else {
     for (int c = 0; c < 4; ++c) {
       const int col = nt * BNR + bcol[c];
-      if (MODE == kStore || col < a.N_valid) C[col] = acc[c];
+      if (MODE == kStore) C[col] = bias ? acc[c] + bias[col] : acc[c];
+      else if (col < a.N_valid) C[col] = acc[c];
     }
   }
 }

@@ -45,21 +45,24 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
                  int32_t* sorted_pairs, int32_t* block_expert, int32_t* pair_row,
                  int32_t* num_padded, int32_t* meta, int32_t* chunk, hipStream_t s);
 
-// The two GEMMs of the expert MLP (see launch_mlp for the row modes).
+// The two GEMMs of the expert MLP (see launch_mlp for the row modes). b13: per-slot fp32
+// [slots, 2 inter] gate then up biases, b2: [slots, H], each NULL = none.
 int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, int inter,
                    const int32_t* row_map, const int32_t* num_padded,
-                   const int32_t* block_expert, int block_m, int rows, void* act, hipStream_t s);
+                   const int32_t* block_expert, int block_m, int rows, void* act, hipStream_t s,
+                   const float* b13 = nullptr);
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
                 const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
-                void* y, hipStream_t s);
+                void* y, hipStream_t s, const float* b2 = nullptr);
 
-// Expert MLP over rows: act = silu(x W1^T) * (x W3^T), y = act W2^T.
+// Expert MLP over rows: act = act_fn(x W1^T + b1, x W3^T + b3) (p.activation: silu(g) * u or
+// the clamped SwiGLU), y = act W2^T + b2 (biases optional).
 //  sorted (row_map != NULL): rows of the expert-sorted pair list, capacity rows, block_m granule;
 //  dense  (row_map == NULL): the first `rows` tokens with a single weight set.
 int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const void* w2,
                int inter, const int32_t* row_map, const int32_t* num_padded,
                const int32_t* block_expert, int block_m, int rows, void* act, void* y,
-               hipStream_t s);
+               hipStream_t s, const float* b13 = nullptr, const float* b2 = nullptr);
 
 // Compute units of the current device (cached per device); 0 if the query fails.
 int device_cu_count();

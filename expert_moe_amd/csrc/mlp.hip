@@ -279,7 +279,8 @@ GemmArgs base_args(const moe_params& p, int T, const int32_t* num_padded,
 
 int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, int inter,
                    const int32_t* row_map, const int32_t* num_padded,
-                   const int32_t* block_expert, int block_m, int rows, void* act, hipStream_t s) {
+                   const int32_t* block_expert, int block_m, int rows, void* act, hipStream_t s,
+                   const float* b13) {
   const int H = p.hidden_size;
   const int I = inter;
   // act[r, :] = silu(x[src(r)] W1^T) * (x[src(r)] W3^T), B = w13 [2I, H] per slot.
@@ -298,6 +299,9 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
   g.N_valid = I;
   g.C = act;
   g.ldc = I;
+  g.bias = b13;
+  g.bias_stride = static_cast<int64_t>(2) * I;
+  g.act = p.activation;
   const bool sorted = row_map != nullptr;
   const Plan pl = plan_rows(p, sorted, block_m, rows, 2 * I);
   const int tr = pl.rows;
@@ -319,7 +323,7 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
 
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
                 const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
-                void* y, hipStream_t s) {
+                void* y, hipStream_t s, const float* b2) {
   const int H = p.hidden_size;
   const int I = inter;
   // y[r, :] = act[r] W2^T, B = w2 [H, I] per slot; act rows are already in order.
@@ -336,6 +340,8 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   g.N_valid = H;
   g.C = y;
   g.ldc = H;
+  g.bias = b2;
+  g.bias_stride = H;
   const bool sorted = num_padded != nullptr;
   const Plan pl = plan_rows(p, sorted, block_m, rows, H);
   const int tr = pl.rows;
@@ -360,11 +366,11 @@ int device_cu_count() { return cu_count(); }
 int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const void* w2,
                int inter, const int32_t* row_map, const int32_t* num_padded,
                const int32_t* block_expert, int block_m, int rows, void* act, void* y,
-               hipStream_t s) {
+               hipStream_t s, const float* b13, const float* b2) {
   int rc = launch_gate_up(p, T, x, w13, inter, row_map, num_padded, block_expert, block_m, rows,
-                          act, s);
+                          act, s, b13);
   if (rc) return rc;
-  return launch_down(p, T, act, w2, inter, num_padded, block_expert, block_m, rows, y, s);
+  return launch_down(p, T, act, w2, inter, num_padded, block_expert, block_m, rows, y, s, b2);
 }
 
 }  // namespace moe

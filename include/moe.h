@@ -10,7 +10,7 @@
  *   w       = p[ids] (/ sum if renormalize) * routed_scaling_factor
  *   out[t]  = sum over slots j whose expert is local of w[j] * MLP_{ids[j]}(x[t])
  *             (+ the shared expert's MLP(x[t]), weight 1, when its weights are given)
- *   MLP(x)  = W2 (silu(W1 x) * (W3 x))
+ *   MLP(x)  = W2 (silu(W1 x) * (W3 x))  (+ expert biases; or the clamped SwiGLU, see activation)
  * Sources: "[Feature] Expert parallelism support" (sglang issue #1435), MixtralMoE.forward
  * (gate, fp32 softmax, top-k, renormalise, weighted per-expert sum, all-reduce of the
  * rank's partial sum); "ep_fused_moe_patch.py: EP-aware FusedMoE override for vllm
@@ -63,6 +63,9 @@ extern "C" {
 #define MOE_SCORE_SOFTMAX 0
 #define MOE_SCORE_SIGMOID 1
 
+#define MOE_ACT_SILU 0
+#define MOE_ACT_SWIGLUOAI 1
+
 /*
  * Layer parameters, named after the EP-aware FusedMoE constructor (_ep_init on the
  * ep_fused_moe_patch.py page) and the config fields of MoEMixin.recursive_replace.
@@ -85,6 +88,16 @@ extern "C" {
  *  scoring_func              MOE_SCORE_SOFTMAX (0, the default of a zeroed struct) or
  *                            MOE_SCORE_SIGMOID (1: p = 1 / (1 + exp(-logit)) per expert, as
  *                            DeepSeek-V3 scores; the pages name the switch, not its formula).
+ *  activation                MOE_ACT_SILU (0, the default): act = silu(g) * u, or
+ *                            MOE_ACT_SWIGLUOAI (1, gpt-oss): g' = min(g, 7), u' = clamp(u, -7, 7),
+ *                            act = g' * sigmoid(1.702 g') * (u' + 1). recursive_replace names
+ *                            "swigluoai" for gpt-oss; the formula is gpt-oss's. Applies to the
+ *                            routed and the shared experts.
+ *
+ * Expert biases (has_bias of recursive_replace): optional fp32 b13 [E_l, 2I] (per slot: the I
+ * gate biases, then the I up biases, the order of w13's rows) added to the gate/up
+ * pre-activations, and b2 [E_l, H] added to the expert output before the routing weight
+ * multiplies it. NULL = none; 16-byte aligned. The shared expert has none.
  *
  * Selection bias (score_bias, "e_score_correction_bias" on the transformers MoE page, named
  * there without its use): an fp32 [E] device vector added to p for the choice only, as
@@ -106,6 +119,7 @@ typedef struct moe_params {
   int32_t shared_intermediate_size;
   int32_t dtype;
   int32_t scoring_func;
+  int32_t activation;
 } moe_params;
 
 /* ------------------------------------------------------------------ host helpers */
@@ -195,32 +209,34 @@ int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* to
 /*
  * Grouped expert MLP over the sorted pairs: for each row r < *num_padded with pair
  * p = sorted_pairs[r] >= 0 and slot e = block_expert[r / block_m],
- *   y[r] = W2_e (silu(W1_e x[p / k]) * (W3_e x[p / k]))
- * (MixtralMLP of MixtralMoE; fused_experts with w13 / w2 in _ep_forward Step 3).
+ *   y[r] = W2_e act(W1_e x[p / k] + b1_e, W3_e x[p / k] + b3_e) + b2_e
+ * (MixtralMLP of MixtralMoE; fused_experts with w13 / w2 in _ep_forward Step 3); the biases
+ * b13 / b2 are optional (NULL = none), act follows p->activation.
  * Padding rows of y hold unspecified values. y [moe_sorted_capacity, H] dtype.
  * The routing weight is NOT applied here (moe_combine applies it).
  *  ws: device scratch, at least moe_workspace_size(p, T, block_m) bytes.
  */
 int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
-                    const void* w2, const int32_t* sorted_pairs, const int32_t* block_expert,
+                    const void* w2, const float* b13, const float* b2,
+                    const int32_t* sorted_pairs, const int32_t* block_expert,
                     const int32_t* num_padded, int32_t block_m, void* y, void* ws,
                     size_t ws_bytes, void* stream);
 
 /*
  * The two stages of moe_grouped_mlp, for callers that want them apart (e.g. to time or
  * overlap them). Same row rules as moe_grouped_mlp.
- *  moe_expert_gate_up: act[r] = silu(W1_e x[p / k]) * (W3_e x[p / k]), act [capacity, I] dtype
- *    (the gate/up projection and activation of the expert MLP).
- *  moe_expert_down:    y[r] = W2_e act[r], y [capacity, H] dtype (the down projection).
+ *  moe_expert_gate_up: act[r] = act(W1_e x[p / k] + b1_e, W3_e x[p / k] + b3_e),
+ *    act [capacity, I] dtype (the gate/up projection and activation of the expert MLP).
+ *  moe_expert_down:    y[r] = W2_e act[r] + b2_e, y [capacity, H] dtype (the down projection).
  * Neither needs a workspace.
  */
 int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, const void* w13,
-                       const int32_t* sorted_pairs, const int32_t* block_expert,
+                       const float* b13, const int32_t* sorted_pairs, const int32_t* block_expert,
                        const int32_t* num_padded, int32_t block_m, void* act, void* stream);
 
 int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, const void* w2,
-                    const int32_t* block_expert, const int32_t* num_padded, int32_t block_m,
-                    void* y, void* stream);
+                    const float* b2, const int32_t* block_expert, const int32_t* num_padded,
+                    int32_t block_m, void* y, void* stream);
 
 /*
  * Shared expert on every token: shared_y [T, H] = W2s (silu(W1s x) * (W3s x)) with
@@ -255,7 +271,7 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
  * that stream. out [T, H] = this share's partial sum; summing the outputs of all disjoint
  * shares (the shared expert passed to exactly one of them) gives the full layer.
  * A share that receives no pairs writes zeros (plus the shared expert).
- *  logit_bias, score_bias: as moe_route.
+ *  logit_bias, score_bias: as moe_route. b13, b2: the expert biases (NULL = none).
  *  shared_w13 / shared_w2: both NULL (no shared expert on this share) or both given
  *    (then p->shared_intermediate_size > 0).
  *  topk_ids_out / topk_w_out: optional [T, k] copies of the routing (NULL = not wanted).
@@ -263,9 +279,9 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
  */
 int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
                 const float* logit_bias, const float* score_bias, const int32_t* expert_map,
-                const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
-                void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                void* stream);
+                const void* w13, const void* w2, const float* b13, const float* b2,
+                const void* shared_w13, const void* shared_w2, void* out, int32_t* topk_ids_out,
+                float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ replicated experts */
 /*
@@ -321,9 +337,9 @@ int moe_route_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens
 int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_tokens, const void* x,
                      const void* w_gate, const float* logit_bias, const float* score_bias,
                      const int32_t* expert_map, const void* w13, const void* w2,
-                     const void* shared_w13, const void* shared_w2, void* out,
-                     int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                     void* stream);
+                     const float* b13, const float* b2, const void* shared_w13,
+                     const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ expert-parallel exchange */
 /*

@@ -43,7 +43,7 @@ def params(w: wl.Workload, **over) -> moe.moe_params:
               topk_group=w.topk_group, routed_scaling_factor=w.routed_scaling_factor,
               num_local_experts=w.num_local_experts,
               shared_intermediate_size=w.shared_intermediate_size, dtype=w.dtype,
-              scoring_func=w.scoring_func)
+              scoring_func=w.scoring_func, activation=w.activation)
     kw.update(over)
     return moe.make_params(**kw)
 
@@ -60,6 +60,7 @@ class Layer:
         self.emap = wl.expert_map(w)
         self.w13, self.w2 = wl.local_expert_weights(w)
         self.sw13, self.sw2 = wl.shared_weights(w)
+        self.b13, self.b2 = wl.expert_biases(w)
         self.d = {
             "x": dev_tensor(self.x, device), "gate": dev_tensor(self.gate, device),
             "bias": None if self.bias is None else dev_tensor(self.bias, device),
@@ -68,6 +69,8 @@ class Layer:
             "w13": dev_tensor(self.w13, device), "w2": dev_tensor(self.w2, device),
             "sw13": None if self.sw13 is None else dev_tensor(self.sw13, device),
             "sw2": None if self.sw2 is None else dev_tensor(self.sw2, device),
+            "b13": None if self.b13 is None else dev_tensor(self.b13, device),
+            "b2": None if self.b2 is None else dev_tensor(self.b2, device),
         }
         if not host_weights:
             self.w13 = self.w2 = None
@@ -84,7 +87,7 @@ class Layer:
         sw13 = d["sw13"] if with_shared else None
         sw2 = d["sw2"] if with_shared else None
         moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"], sw13, sw2,
-                        out, ids, tw, ws, score_bias=d["sbias"])
+                        out, ids, tw, ws, score_bias=d["sbias"], b13=d["b13"], b2=d["b2"])
         torch.cuda.synchronize()
         return out.float().cpu().numpy(), ids.cpu().numpy(), tw.cpu().numpy()
 
@@ -124,7 +127,8 @@ class Layer:
         sh = (wl.to_f32(self.sw13), wl.to_f32(self.sw2)) if (with_shared and self.sw13 is not None) \
             else (None, None)
         return oracle.moe_forward_given_routing(wl.to_f32(self.x[rows]), ids, weights, self.emap,
-                                                w13, w2, sh[0], sh[1])
+                                                w13, w2, sh[0], sh[1], w.activation, self.b13,
+                                                self.b2)
 
 
 class _LazyF32:

@@ -136,6 +136,19 @@ def test_entry_points_zero_tokens_are_noops():
     moe.moe_combine(p, 0, None, None, None, None, None, stream=0)
 
 
+def _forward_raw(pp, T, ws_bytes, **over):
+    """moe_forward through the raw C symbol with every pointer a fake non-NULL address unless
+    overridden (only for calls that must fail before launching anything)."""
+    F = FAKE
+    a = dict(x=F, w_gate=F, logit_bias=None, score_bias=None, expert_map=F, w13=F, w2=F, b13=None,
+             b2=None, shared_w13=F, shared_w2=F, out=F, topk_ids=None, topk_w=None, ws=F)
+    a.update(over)
+    return moe.lib().moe_forward(pp, T, a["x"], a["w_gate"], a["logit_bias"], a["score_bias"],
+                                 a["expert_map"], a["w13"], a["w2"], a["b13"], a["b2"],
+                                 a["shared_w13"], a["shared_w2"], a["out"], a["topk_ids"],
+                                 a["topk_w"], a["ws"], ws_bytes, None)
+
+
 def test_entry_point_argument_errors():
     p = _params(wl.WORKLOADS["dsv2"])
     L = moe.lib()
@@ -144,30 +157,34 @@ def test_entry_point_argument_errors():
     ws = moe.moe_workspace_size(p, T)
     F = FAKE
     # missing required pointers
-    assert L.moe_forward(pp, T, None, F, None, None, F, F, F, None, None, F, None, None, F, ws, None) == -1
-    assert L.moe_forward(pp, T, F, F, None, None, None, F, F, None, None, F, None, None, F, ws, None) == -1
+    assert _forward_raw(pp, T, ws, x=None) == -1
+    assert _forward_raw(pp, T, ws, expert_map=None) == -1
     # only one of the two shared-expert pointers
-    assert L.moe_forward(pp, T, F, F, None, None, F, F, F, F, None, F, None, None, F, ws, None) == -1
+    assert _forward_raw(pp, T, ws, shared_w2=None) == -1
     # workspace too small
-    assert L.moe_forward(pp, T, F, F, None, None, F, F, F, F, F, F, None, None, F, ws - 1, None) == -3
+    assert _forward_raw(pp, T, ws - 1) == -3
     # tensor pointers that are not 16-byte aligned
-    assert L.moe_forward(pp, T, F + 2, F, None, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
-    assert L.moe_forward(pp, T, F, F, None, None, F, F, F, F, F, F + 8, None, None, F, ws, None) == -1
-    assert L.moe_grouped_mlp(pp, T, F, F, F, F, F, F, 16, F + 4, F, ws, None) == -1
+    assert _forward_raw(pp, T, ws, x=F + 2) == -1
+    assert _forward_raw(pp, T, ws, out=F + 8) == -1
+    assert _forward_raw(pp, T, ws, b13=F + 8) == -1
+    assert _forward_raw(pp, T, ws, b2=F + 4) == -1
+    assert L.moe_grouped_mlp(pp, T, F, F, F, None, None, F, F, F, 16, F + 4, F, ws, None) == -1
+    assert L.moe_grouped_mlp(pp, T, F, F, F, F + 4, None, F, F, F, 16, F, F, ws, None) == -1
+    assert L.moe_expert_gate_up(pp, T, F, F, F + 8, F, F, F, 16, F, None) == -1
+    assert L.moe_expert_down(pp, T, F, F, F + 8, F, F, 16, F, None) == -1
     assert L.moe_combine(pp, T, F, F, F, F + 2, F, None) == -1
     # negative token count
-    assert L.moe_forward(pp, -1, F, F, None, None, F, F, F, F, F, F, None, None, F, ws, None) == -1
+    assert _forward_raw(pp, -1, ws) == -1
     # bad block_m for the split entry points
     assert L.moe_align_permute(pp, T, F, 48, F, F, F, F, F, ws, None) == -1
-    assert L.moe_grouped_mlp(pp, T, F, F, F, F, F, F, 0, F, F, ws, None) == -1
+    assert L.moe_grouped_mlp(pp, T, F, F, F, None, None, F, F, F, 0, F, F, ws, None) == -1
     assert L.moe_align_permute(pp, T, F, 16, F, F, F, F, F, 8, None) == -3
     assert L.moe_route(pp, T, F, F, None, None, F, F, F, F, F, 8, None) == -3
     # shared MLP on a share without a shared expert
     p2 = _params(wl.WORKLOADS["ep_share"])
     assert L.moe_shared_mlp(ctypes.byref(p2), T, F, F, F, F, F, ws, None) == -1
     # shared expert pointers given but the params say there is none
-    assert L.moe_forward(ctypes.byref(p2), T, F, F, None, None, F, F, F, F, F, F, None, None, F,
-                         moe.moe_workspace_size(p2, T), None) == -1
+    assert _forward_raw(ctypes.byref(p2), T, moe.moe_workspace_size(p2, T)) == -1
 
 
 def test_ep_exchange_host_logic():
@@ -239,10 +256,11 @@ def test_eplb_tables_and_argument_errors():
               moe.moe_eplb(264, 2, F, None)]:
         assert L.moe_route_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, None, F, F, F, F, F,
                                 ws, None) == -1
-        assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, None, F, F, F, None,
-                                  None, F, None, None, F, ws, None) == -1
+        assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(e), T, F, F, None, None, F, F, F,
+                                  None, None, None, None, F, None, None, F, ws, None) == -1
     assert L.moe_route_eplb(ctypes.byref(p), None, T, F, F, None, None, F, F, F, F, F, ws, None) == -1
-    assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(good), T, F, F, None, None, F, F, F, None,
+    assert L.moe_forward_eplb(ctypes.byref(p), ctypes.byref(good), T, F, F, None, None, F, F, F,
+                              None, None, None,
                               None, F, None, None, F, ws - 1, None) == -3
     moe.moe_route_eplb(p, good, 0, None, None, None, None, None, None, None, None, stream=0)
     moe.moe_forward_eplb(p, good, 0, None, None, None, None, None, None, None, None, None, None,

@@ -135,6 +135,8 @@ class Workload:
     zipf_bias: float = 0.0  # s of the Zipf logit bias; 0 = none
     scoring_func: str = "softmax"  # or "sigmoid"
     score_bias_std: float = 0.0  # std of the seeded selection bias N(0, std^2); 0 = none
+    activation: str = "silu"  # or "swigluoai"
+    expert_bias_std: float = 0.0  # std of the seeded expert biases N(0, std^2); 0 = none
     extra: dict = field(default_factory=dict)
 
     @property
@@ -176,6 +178,10 @@ WORKLOADS = {
                      use_grouped_topk=True, num_expert_group=8, topk_group=4,
                      routed_scaling_factor=2.5, ep_size=8, ep_rank=0,
                      shared_intermediate_size=2048, scoring_func="sigmoid", score_bias_std=0.05),
+    # MLP variants: gpt-oss's clamped SwiGLU and expert biases
+    "gptoss": Workload("gptoss", 7, "gpt-oss-shaped layer, bf16 (experts 0..15 of 128, clamped "
+                       "SwiGLU, expert biases)", "bf16", (32, 4096), 2880, 128, 2880, 4, True,
+                       ep_size=8, ep_rank=0, activation="swigluoai", expert_bias_std=0.1),
 }
 
 
@@ -220,6 +226,18 @@ def score_bias(w: Workload):
     if not w.score_bias_std:
         return None
     return normal((w.cid, 5, 0), w.num_experts, w.score_bias_std).astype(np.float32)
+
+
+def expert_biases(w: Workload, experts=None):
+    """fp32 (b13 [n, 2I], b2 [n, H]) of the given global experts (default: the share's local
+    experts), seeded N(0, std^2) per expert; (None, None) when the layer has none."""
+    if not w.expert_bias_std:
+        return None, None
+    experts = list(w.local_experts if experts is None else experts)
+    I, H = w.intermediate_size, w.hidden_size
+    b13 = np.stack([normal((w.cid, 6, 2 * e), 2 * I, w.expert_bias_std) for e in experts])
+    b2 = np.stack([normal((w.cid, 6, 2 * e + 1), H, w.expert_bias_std) for e in experts])
+    return b13.astype(np.float32), b2.astype(np.float32)
 
 
 def _storage(w: Workload):
