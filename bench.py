@@ -111,7 +111,8 @@ class Bench:
         self.p = moe.make_params(w.num_experts, w.top_k, w.hidden_size, w.intermediate_size,
                                  w.renormalize, w.use_grouped_topk, w.num_expert_group,
                                  w.topk_group, w.routed_scaling_factor, w.num_local_experts,
-                                 w.shared_intermediate_size, w.dtype, w.scoring_func)
+                                 w.shared_intermediate_size, w.dtype, w.scoring_func,
+                                 w.activation)
         self.d = host.device_tensors(T)
         dt = self.d["x"].dtype
         k, H = w.top_k, w.hidden_size
@@ -137,7 +138,7 @@ class Bench:
         d = self.d
         self.moe.moe_forward(self.p, self.T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
                              d["w2"], d["sw13"], d["sw2"], self.out, self.ids, self.tw, self.ws,
-                             score_bias=d["sbias"])
+                             score_bias=d["sbias"], b13=d["b13"], b2=d["b2"])
 
     def split_step(self, ev=None):
         """The same kernels as moe_forward through the split entry points; events at stage ends."""
@@ -149,9 +150,10 @@ class Bench:
         rec(1)
         m.moe_align_permute(p, T, self.local, self.bm, self.sp, self.be, self.pr, self.npad, self.sws)
         rec(2)
-        m.moe_expert_gate_up(p, T, d["x"], d["w13"], self.sp, self.be, self.npad, self.bm, self.act)
+        m.moe_expert_gate_up(p, T, d["x"], d["w13"], self.sp, self.be, self.npad, self.bm, self.act,
+                             b13=d["b13"])
         rec(3)
-        m.moe_expert_down(p, T, self.act, d["w2"], self.be, self.npad, self.bm, self.y)
+        m.moe_expert_down(p, T, self.act, d["w2"], self.be, self.npad, self.bm, self.y, b2=d["b2"])
         rec(4)
         if self.sy is not None:
             m.moe_shared_mlp(p, T, d["x"], d["sw13"], d["sw2"], self.sy, self.sws)
@@ -173,12 +175,14 @@ class HostLayer:
         self.emap = wl.expert_map(w)
         self.w13, self.w2 = wl.local_expert_weights(w)
         self.sw13, self.sw2 = wl.shared_weights(w)
+        self.b13, self.b2 = wl.expert_biases(w)
         self._dev = None
 
     def _weights_on_device(self):
         if self._dev is None:
             self._dev = {k: _dev(getattr(self, k)) for k in
-                         ("gate", "bias", "sbias", "emap", "w13", "w2", "sw13", "sw2")}
+                         ("gate", "bias", "sbias", "emap", "w13", "w2", "sw13", "sw2", "b13",
+                          "b2")}
         return self._dev
 
     def device_tensors(self, T):
@@ -369,22 +373,28 @@ def run_eplb(host, w, T, extra, steps, warmup):
     tw = torch.empty(T, k, dtype=torch.float32, device=dev)
     cache = {}
 
-    def expert(e):  # device weights of logical expert e (drawn once)
+    def expert(e):  # device weights (and biases, or None) of logical expert e, drawn once
         if e not in cache:
             a, b = wl.expert_weights(w, e)
-            cache[e] = (_dev(a), _dev(b))
+            b13, b2 = wl.expert_biases(w, [e])
+            cache[e] = (_dev(a), _dev(b), None if b13 is None else _dev(b13[0]),
+                        None if b2 is None else _dev(b2[0]))
         return cache[e]
 
-    def time_share(p, emap, w13, w2, eplb=None):
+    def stack(experts, i):
+        parts = [expert(int(e))[i] for e in experts]
+        return None if parts[0] is None else torch.stack(parts)
+
+    def time_share(p, emap, w13, w2, b13, b2, eplb=None):
         ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
 
         def call():
             if eplb is None:
                 moe.moe_forward(p, T, x, gate, bias, emap, w13, w2, None, None, out, ids, tw, ws,
-                                score_bias=sbias)
+                                score_bias=sbias, b13=b13, b2=b2)
             else:
                 moe.moe_forward_eplb(p, eplb, T, x, gate, bias, emap, w13, w2, None, None, out,
-                                     ids, tw, ws, score_bias=sbias)
+                                     ids, tw, ws, score_bias=sbias, b13=b13, b2=b2)
         warm_up(call, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -397,16 +407,15 @@ def run_eplb(host, w, T, extra, steps, warmup):
     def params(n_local):
         return moe.make_params(E, k, H, w.intermediate_size, w.renormalize, w.use_grouped_topk,
                                w.num_expert_group, w.topk_group, w.routed_scaling_factor, n_local,
-                               0, w.dtype, w.scoring_func)
+                               0, w.dtype, w.scoring_func, w.activation)
 
     per = E // ep
     plain_ms, plain_pairs = [], []
     for r in range(ep):
         emap = torch.from_numpy(moe.moe_make_expert_map(E, ep, r)).to(dev)
-        w13 = torch.stack([expert(e)[0] for e in range(r * per, (r + 1) * per)])
-        w2 = torch.stack([expert(e)[1] for e in range(r * per, (r + 1) * per)])
-        plain_ms.append(time_share(params(per), emap, w13, w2))
-        del w13, w2
+        mine = range(r * per, (r + 1) * per)
+        plain_ms.append(time_share(params(per), emap, stack(mine, 0), stack(mine, 1),
+                                   stack(mine, 2), stack(mine, 3)))
     ids_h = ids.cpu().numpy()
     loads = np.bincount(ids_h.ravel(), minlength=E)
     plain_pairs = [int(loads[r * per:(r + 1) * per].sum()) for r in range(ep)]
@@ -420,14 +429,13 @@ def run_eplb(host, w, T, extra, steps, warmup):
     for r in range(ep):
         pmap = np.full(P, -1, np.int32)
         pmap[r * pp:(r + 1) * pp] = np.arange(pp)
-        w13 = torch.stack([expert(int(e))[0] for e in p2l[r * pp:(r + 1) * pp]])
-        w2 = torch.stack([expert(int(e))[1] for e in p2l[r * pp:(r + 1) * pp]])
-        eplb_ms.append(time_share(params(pp), torch.from_numpy(pmap).to(dev), w13, w2, eplb))
+        mine = p2l[r * pp:(r + 1) * pp]
+        eplb_ms.append(time_share(params(pp), torch.from_numpy(pmap).to(dev), stack(mine, 0),
+                                  stack(mine, 1), stack(mine, 2), stack(mine, 3), eplb))
         # pairs that landed on this rank (replica t mod count of each pair's logical expert)
         t = np.arange(T)[:, None]
         phys = l2p[ids_h, t % cnt[ids_h]]
         eplb_pairs.append(int(((phys >= r * pp) & (phys < (r + 1) * pp)).sum()))
-        del w13, w2
     return {"ep_size": ep, "redundant_experts": extra, "physical_experts": P,
             "placement": p2l.tolist(),
             "rank_ms_plain": [round(v, 4) for v in plain_ms],
@@ -463,7 +471,7 @@ def cpu_baseline(host, w, sample):
 
     sh = (wl.to_f32(host.sw13), wl.to_f32(host.sw2)) if host.sw13 is not None else (None, None)
     oracle.moe_forward_given_routing(x, r["ids"], r["weights"], host.emap, Lazy(host.w13),
-                                     Lazy(host.w2), sh[0], sh[1])
+                                     Lazy(host.w2), sh[0], sh[1], w.activation, host.b13, host.b2)
     dt = time.perf_counter() - t0
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 2),

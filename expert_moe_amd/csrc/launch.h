@@ -16,7 +16,8 @@ constexpr int kAlignChunk = 256;
 inline int align_chunks(int64_t T) { return static_cast<int>((T + kAlignChunk - 1) / kAlignChunk); }
 
 // Number of K splits of the router logits GEMM for T tokens (enough workgroups to fill the
-// chip when T is small; each split's K range stays a multiple of 256).
+// chip when T is small): powers of two whose K ranges stay multiples of 256, or for hidden
+// sizes without such a split a divisor of H / (K step) with at least four K steps per range.
 int router_splits(const moe_params& p, int T);
 
 // Router logits: router_splits() partial sums [splits, T, E] fp32 of x . Wg^T.

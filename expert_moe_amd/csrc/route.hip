@@ -266,6 +266,17 @@ int router_splits(const moe_params& p, int T) {
   const int blocks = ((T + rows - 1) / rows) * ((p.num_experts + bnr - 1) / bnr);
   int sp = 1;
   while (sp < 16 && blocks * sp < 256 && p.hidden_size % (256 * 2 * sp) == 0) sp *= 2;
+  if (sp == 1 && blocks < 256) {
+    // hidden sizes with no power-of-two split (e.g. 2880 = 45 x 64): the largest split of at
+    // most 16 that divides H into whole K steps of the logits kernel, at least four each, and
+    // stays under about two workgroups per CU
+    const int units = p.hidden_size / (T <= 64 ? 32 : 64);
+    for (int d = 16; d > 1; --d)
+      if (units % d == 0 && units / d >= 4 && blocks * d < 512) {
+        sp = d;
+        break;
+      }
+  }
   return sp;
 }
 
