@@ -124,11 +124,14 @@ inline int pick_bnr(int n_rows_b, int est_blocks, bool silu) {
 inline int pick_bnr256(int n_rows_b, int est_blocks, bool silu, int n_cu) {
   if (n_cu <= 0) return pick_bnr(n_rows_b, est_blocks, silu);
   struct Cand { int bnr; double w; bool quarter; };
-  constexpr Cand cands[3] = {{256, 1.7, true}, {128, 1.0, true}, {64, 0.6, false}};
+  // 192 (three 64-row blocks) only for widths that 128 does not divide (e.g. 2880), where the
+  // only other choice is the narrow 64 (its gate/up pairs need an even block count)
+  constexpr Cand cands[4] = {{256, 1.7, true}, {192, 1.35, false}, {128, 1.0, true}, {64, 0.6, false}};
   int best = 0;
   double best_cost = 0.0;
   for (const Cand& c : cands) {
     if (n_rows_b % c.bnr != 0 || (silu && c.bnr < 128)) continue;
+    if (c.bnr == 192 && (silu || n_rows_b % 128 == 0)) continue;
     const int64_t tiles = static_cast<int64_t>(est_blocks) * (n_rows_b / c.bnr);
     const int64_t full = tiles / n_cu;
     const int64_t rem = tiles % n_cu;
@@ -148,7 +151,14 @@ template <int MODE>
 void launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
   if (bnr == 256)
     launch_tile<256, 256, 2, 4, MODE>(a, n_rows_b, est, s);
-  else if (bnr == 128)
+  else if constexpr (MODE == kStore) {
+    if (bnr == 192)
+      launch_tile<256, 192, 4, 2, MODE>(a, n_rows_b, est, s);
+    else if (bnr == 128)
+      launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, est, s);
+    else
+      launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, est, s);
+  } else if (bnr == 128)
     launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, est, s);
   else
     launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, est, s);
