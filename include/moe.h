@@ -24,7 +24,8 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers, borrowed: the caller owns them, they must
  *    stay alive until the work queued on `stream` has finished. The library never
- *    allocates or frees device memory and keeps no state between calls.
+ *    allocates or frees device memory; its only state is the side stream of moe_forward
+ *    (one per device, with its two events, created on first use).
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work
  *    on it: no host<->device synchronisation, no host reads of device data, so a call
  *    can be captured in a HIP graph.
