@@ -380,3 +380,34 @@ def test_graph_replay_matches_eager(case):
         call()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0]), r
+
+
+# Largest parameters the kernels take: 256 experts, all local (E_l = 256: the alignment's
+# one-slot-per-thread tables), top-64 (one wave's ballot in the top-k and the combine), plain
+# and grouped.
+MAXED = {
+    "e256_k64": (W("e256_k64", 41, "E 256, top-64, all local", "bf16", (300,), 128, 256, 64, 64,
+                   True), 300),
+    "e256_k64_grp": (W("e256_k64_grp", 42, "E 256, top-64, grouped", "bf16", (90,), 128, 256, 64,
+                       64, False, use_grouped_topk=True, num_expert_group=64, topk_group=32,
+                       routed_scaling_factor=2.0), 90),
+    "e256_k1": (W("e256_k1", 43, "E 256, top-1", "bf16", (1000,), 256, 256, 64, 1, True,
+                  ep_size=2, ep_rank=1), 1000),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MAXED))
+def test_forward_largest_parameters(case):
+    w, T = MAXED[case]
+    _full_check(Layer(w, T))
+
+
+@pytest.mark.parametrize("ep", [1, 4, 256])
+def test_exchange_largest_parameters(ep):
+    """The exchange at top-64 over 256 experts: dispatch bit for bit against the oracle."""
+    from test_gpu_exchange import _check_dispatch
+    w, T = MAXED["e256_k64"]
+    rng = np.random.default_rng(44)
+    ids = np.argsort(rng.random((T, 256)), axis=1)[:, :64].astype(np.int32)
+    tw = rng.random((T, 64)).astype(np.float32)
+    _check_dispatch(w, T, ep, ids, tw, dev_tensor(wl.x(w, T)))
