@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
 
 int router_splits(const moe_params& p, int T) {
   if (p.dtype == MOE_F32) return 1;
-  const int rows = T <= 64 ? 16 : 128;
+  const int rows = T <= 64 ? 16 : 64;
   const int bnr = 64;
   const int blocks = ((T + rows - 1) / rows) * ((p.num_experts + bnr - 1) / bnr);
   int sp = 1;
@@ -310,17 +310,14 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
     a.n_tiles = n_tiles;
     gemm_bf16_stream<4, kStoreF32><<<dim3(tile_grid(a.m_blocks, n_tiles), a.k_splits), 256, 0, s>>>(a);
   } else {
-    a.m_blocks = ceil_div(T, 128);
+    a.m_blocks = ceil_div(T, 64);
     a.n_tiles = n_tiles;
     const dim3 grid(tile_grid(a.m_blocks, n_tiles), a.k_splits);
-    if (bnr == 256)
-      gemm_bf16_dma<128, 256, 2, 2, kStoreF32><<<grid, 256, 0, s>>>(a);
-    else if (bnr == 128)
-      gemm_bf16_dma<128, 128, 2, 2, kStoreF32><<<grid, 256, 0, s>>>(a);
-    else
-      // three LDS stages: the loads run two K steps ahead, which this short-K, latency-bound
-      // launch needs (measured: EP share 42 -> 35 us, with splits for about one workgroup per CU)
-      gemm_bf16_dma<128, 64, 4, 1, kStoreF32, 3><<<grid, 256, 0, s>>>(a);
+    // 64x64 tiles, three LDS stages: the loads run two K steps ahead, which this short-K,
+    // latency-bound launch needs (measured: EP share 42 -> 35 us, with splits for about one
+    // workgroup per CU); 64-row tiles give twice the workgroups of 128-row ones for the same
+    // LDS per CU (route stage: DeepSeek-V2-shaped 39.2 -> 36.9 us, skewed T=16384 58 -> 54.5 us)
+    gemm_bf16_dma<64, 64, 2, 2, kStoreF32, 3><<<grid, 256, 0, s>>>(a);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
