@@ -482,7 +482,7 @@ def cpu_baseline(host, w, sample):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path: each expert-parallel share is benchmarked on its own GPU.",
               file=sys.stderr)
         sys.exit(2)

@@ -54,7 +54,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* a parameter or a required pointer is invalid */
-#define MOE_EUNSUPPORTED (-2) /* a valid request this build has no kernel for */
+#define MOE_EUNSUPPORTED (-2) /* a valid request the library has no kernel for */
 #define MOE_ENOSPC (-3)       /* the workspace is smaller than moe_workspace_size() */
 #define MOE_EHIP (-4)         /* a HIP launch failed */
 
