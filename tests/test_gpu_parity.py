@@ -411,3 +411,42 @@ def test_exchange_largest_parameters(ep):
     ids = np.argsort(rng.random((T, 256)), axis=1)[:, :64].astype(np.int32)
     tw = rng.random((T, 64)).astype(np.float32)
     _check_dispatch(w, T, ep, ids, tw, dev_tensor(wl.x(w, T)))
+
+
+@pytest.mark.parametrize("case", ["ds_s", "skew_s7", "e256_k64"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+def test_decode_forward_equals_split_path(case, T):
+    """Decode-sized moe_forward (shared expert on the side stream) equals, bit for bit, the
+    split entry points (route -> align_permute -> grouped MLP -> shared MLP -> combine) at the
+    same granule."""
+    w, _ = {**SMALL, **MAXED}[case]
+    layer = Layer(w, T)
+    out_f, ids_f, tw_f = layer.forward()
+    p = params(w)
+    d = layer.d
+    dev = d["x"].device
+    k, H = w.top_k, w.hidden_size
+    bm = moe.moe_pick_block_m(p, T)
+    ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    local = torch.empty(T, k, dtype=torch.int32, device=dev)
+    moe.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], ids, tw, local, ws,
+                  score_bias=d["sbias"])
+    cap = moe.moe_sorted_capacity(p, T, bm)
+    sp = torch.empty(cap, dtype=torch.int32, device=dev)
+    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
+    y = torch.empty(cap, H, dtype=d["x"].dtype, device=dev)
+    moe.moe_grouped_mlp(p, T, d["x"], d["w13"], d["w2"], sp, be, npad, bm, y, ws)
+    sy = None
+    if d["sw13"] is not None:
+        sy = torch.empty(T, H, dtype=d["x"].dtype, device=dev)
+        moe.moe_shared_mlp(p, T, d["x"], d["sw13"], d["sw2"], sy, ws)
+    out = torch.empty(T, H, dtype=d["x"].dtype, device=dev)
+    moe.moe_combine(p, T, y, pr, tw, sy, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_f) and np.array_equal(tw.cpu().numpy(), tw_f)
+    assert np.array_equal(out.float().cpu().numpy(), out_f)
