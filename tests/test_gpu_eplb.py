@@ -13,7 +13,7 @@ import torch
 import expert_moe_amd as moe
 import oracle
 import workloads as wl
-from moe_case import OUT_TOL, Layer, dev_tensor, params, reference_routing, rel_err, torch_dtype
+from moe_case import OUT_TOL, Layer, dev_tensor, params, rel_err, torch_dtype
 from test_gpu_parity import SMALL
 
 pytestmark = pytest.mark.gpu
@@ -158,3 +158,50 @@ def test_eplb_table_entries_out_of_range_are_not_local():
     assert bad.any()
     assert np.all(got[bad] == -1)
     assert np.array_equal(got[~bad], ids_h[~bad])
+
+
+def test_eplb_with_routing_and_mlp_variants():
+    """Replicated experts together with sigmoid scores, a selection bias, the clamped SwiGLU and
+    expert biases: every share's slots bit for bit, and the shares' sum against the oracle."""
+    w0 = wl.Workload("eplb_var", 51, "EPLB + variants", "bf16", (257,), 256, 32, 128, 4, True,
+                     use_grouped_topk=True, num_expert_group=4, topk_group=2,
+                     routed_scaling_factor=2.5, scoring_func="sigmoid", score_bias_std=0.05,
+                     activation="swigluoai", expert_bias_std=1.0)
+    T, ep, extra = 257, 4, 8
+    full = Layer(w0, T)
+    ids_h, tw_h, _ = full.gpu_route()
+    E, k = w0.num_experts, w0.top_k
+    P = E + extra
+    p2l = wl.eplb_placement(np.bincount(ids_h.ravel(), minlength=E) + 1.0, P, ep)
+    l2p, cnt = _tables(E, p2l)
+    eplb = moe.make_eplb(P, l2p.shape[1], dev_tensor(l2p), dev_tensor(cnt))
+    per = P // ep
+    dev = full.d["x"].device
+    total = np.zeros((T, w0.hidden_size))
+    for r in range(ep):
+        p = params(w0, num_local_experts=per)
+        pmap = _share_map(P, ep, r)
+        mine = p2l[r * per:(r + 1) * per]
+        w13, w2 = _physical_weights(w0, mine)
+        b13, b2 = wl.expert_biases(w0, [int(e) for e in mine])
+        out = torch.empty(T, w0.hidden_size, dtype=torch_dtype(w0), device=dev)
+        ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+        ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
+        moe.moe_forward_eplb(p, eplb, T, full.d["x"], full.d["gate"], full.d["bias"],
+                             dev_tensor(pmap), dev_tensor(w13), dev_tensor(w2), None, None, out,
+                             ids, tw, ws, score_bias=full.d["sbias"], b13=dev_tensor(b13),
+                             b2=dev_tensor(b2))
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ids_h) and np.array_equal(tw.cpu().numpy(), tw_h)
+        slots = oracle.eplb_local_slots(ids_h, k, l2p, cnt, pmap)
+        want_r = oracle.moe_forward_given_slots(wl.to_f32(full.x), slots, tw_h,
+                                                [wl.to_f32(a) for a in w13],
+                                                [wl.to_f32(a) for a in w2],
+                                                activation="swigluoai", b13_local=b13,
+                                                b2_local=b2)
+        got = out.float().cpu().numpy()
+        assert rel_err(got, want_r) <= OUT_TOL[w0.dtype]
+        total += got
+    want = full.oracle_out(np.arange(T), ids_h, tw_h)
+    assert rel_err(total, want) <= OUT_TOL[w0.dtype]

@@ -204,3 +204,45 @@ def test_ep_exchange_around_shares(case, ep):
     out_local, ids_l, tw_l = full.forward(with_shared=False)
     assert np.array_equal(ids_l, ids_h) and np.array_equal(tw_l, tw_h)
     assert rel_err(out.float().cpu().numpy(), out_local) <= OUT_TOL[w0.dtype]
+
+
+def test_exchange_graph_replay_matches_eager():
+    """Dispatch and unpack captured in a HIP graph: every replay, with eager work between the
+    replays, reproduces the eager outputs bit for bit."""
+    w, T, ep = SMALL["ep_s_r4"]
+    ids = _random_ids(61, T, w.num_experts, w.top_k)
+    tw = np.random.default_rng(62).random((T, w.top_k)).astype(np.float32)
+    p = params(w)
+    x = dev_tensor(wl.x(w, T))
+    ids_d, tw_d = dev_tensor(ids), dev_tensor(tw)
+    ref = _dispatch(w, T, ep, ids_d, tw_d, x)
+    R = moe.moe_ep_send_capacity(p, T, ep)
+    bufs = {kk: torch.empty_like(v) for kk, v in ref.items()}
+    ws = torch.empty(moe.moe_ep_workspace_size(p, T, ep), dtype=torch.uint8, device=x.device)
+    out = torch.empty(T, w.hidden_size, dtype=x.dtype, device=x.device)
+    out_ref = torch.empty_like(out)
+    moe.moe_ep_combine(p, T, ref["send_pos"], ref["send_x"], out_ref)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            moe.moe_ep_dispatch(p, T, ep, ids_d, tw_d, x, bufs["send_pos"], bufs["rank_meta"],
+                                bufs["send_token"], bufs["send_x"], bufs["send_local"],
+                                bufs["send_w"], ws, stream=s)
+            moe.moe_ep_combine(p, T, bufs["send_pos"], bufs["send_x"], out, stream=s)
+    n = int(ref["rank_meta"][0].item())
+    assert n <= R
+    for rep in range(3):
+        for v in bufs.values():
+            v.fill_(0)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["send_pos"], ref["send_pos"])
+        assert torch.equal(bufs["rank_meta"], ref["rank_meta"])
+        for kk in ("send_token", "send_x", "send_local", "send_w"):
+            assert torch.equal(bufs[kk][:n], ref[kk][:n]), (rep, kk)
+        assert torch.equal(out, out_ref)
+        _ = (x.float() * 2).sum().item()  # eager work between the replays
