@@ -31,6 +31,8 @@ struct GemmArgs {
   const int32_t* block_expert; // sorted rows: slot of each block of block_m rows (NULL = slot 0)
   const int32_t* valid_map;    // LDS tile with SKIP: the sorted pair list, whose -1 entries mark
                                // padding rows (padding ends each expert's segment)
+  const int32_t* store_map;    // LDS tile, bf16 out: rows whose entry is < 0 (padding of the
+                               // sorted pair list) are not stored; NULL = every row
   int32_t block_m;             // padding granule of the sorted rows (a multiple of the tile rows)
   const void* B;               // weights of slot s at B + s * b_stride elements, [rows, K]
   int64_t b_stride;
@@ -492,6 +494,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < TMB; ++i) {
       const int row = orow + i * 32;
+      const bool keep = row < a.M_rows && (!a.store_map || a.store_map[row] >= 0);
       uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc + col0;
 #pragma unroll
       for (int j = 0; j < OUTB; ++j) {
@@ -540,7 +543,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
           p[2][h] = s23[0];
           p[3][h] = s23[1];
         }
-        if (row < a.M_rows) {
+        if (keep) {
           *reinterpret_cast<uint4*>(C + j * 32) = uint4{p[0][0], p[0][1], p[1][0], p[1][1]};
           *reinterpret_cast<uint4*>(C + j * 32 + 16) = uint4{p[2][0], p[2][1], p[3][0], p[3][1]};
         }

@@ -54,7 +54,8 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
                    const float* b13 = nullptr);
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
                 const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
-                void* y, hipStream_t s, const float* b2 = nullptr);
+                void* y, hipStream_t s, const float* b2 = nullptr,
+                const int32_t* store_map = nullptr);
 
 // Expert MLP over rows: act = act_fn(x W1^T + b1, x W3^T + b3) (p.activation: silu(g) * u or
 // the clamped SwiGLU), y = act W2^T + b2 (biases optional).

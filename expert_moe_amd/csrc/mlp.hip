@@ -333,7 +333,7 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
 
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
                 const int32_t* num_padded, const int32_t* block_expert, int block_m, int rows,
-                void* y, hipStream_t s, const float* b2) {
+                void* y, hipStream_t s, const float* b2, const int32_t* store_map) {
   const int H = p.hidden_size;
   const int I = inter;
   // y[r, :] = act[r] W2^T, B = w2 [H, I] per slot; act rows are already in order.
@@ -343,6 +343,10 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   // no padding-row skip here: measured slower on the long-K down projection (Mixtral-shaped
   // prefill: 931 us with it, 814 us without), unlike the gate/up projection
   g.valid_map = nullptr;
+  // Padding rows of y (the combine reads real rows only) are left unwritten where more than
+  // 20% of the rows are expected to be padding; below that the per-row check costs more than
+  // the stores it saves.
+  g.store_map = store_map != nullptr && est_padding(p, T, block_m) > 0.2 ? store_map : nullptr;
   g.B = w2;
   g.b_stride = static_cast<int64_t>(H) * I;
   g.K = I;
@@ -380,7 +384,8 @@ int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const
   int rc = launch_gate_up(p, T, x, w13, inter, row_map, num_padded, block_expert, block_m, rows,
                           act, s, b13);
   if (rc) return rc;
-  return launch_down(p, T, act, w2, inter, num_padded, block_expert, block_m, rows, y, s, b2);
+  return launch_down(p, T, act, w2, inter, num_padded, block_expert, block_m, rows, y, s, b2,
+                     row_map);
 }
 
 }  // namespace moe

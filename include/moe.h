@@ -213,7 +213,8 @@ int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* to
  *   y[r] = W2_e act(W1_e x[p / k] + b1_e, W3_e x[p / k] + b3_e) + b2_e
  * (MixtralMLP of MixtralMoE; fused_experts with w13 / w2 in _ep_forward Step 3); the biases
  * b13 / b2 are optional (NULL = none), act follows p->activation.
- * Padding rows of y hold unspecified values. y [moe_sorted_capacity, H] dtype.
+ * Padding rows of y hold unspecified values (they may be left unwritten). y
+ * [moe_sorted_capacity, H] dtype.
  * The routing weight is NOT applied here (moe_combine applies it).
  *  ws: device scratch, at least moe_workspace_size(p, T, block_m) bytes.
  */
