@@ -28,6 +28,26 @@ __device__ __forceinline__ int local_slot(const int32_t* tl, int64_t i, int E_l)
   return (s >= 0 && s < E_l) ? s : -1;
 }
 
+// Exclusive prefix sum of v over the 256 threads of the workgroup (thread order), and the
+// total: a lane-shift scan inside each wave, then the earlier waves' totals. Every thread
+// must call it (it holds a barrier); wsum is 4 ints of LDS.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  return before + x - v;
+}
+
 __global__ void __launch_bounds__(256) align_count(const int32_t* __restrict__ tl, int T, int k,
                                                    int E_l, int32_t* __restrict__ chunk,
                                                    int32_t* __restrict__ sorted_pairs, int cap) {
@@ -50,11 +70,12 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
                                                   int bm, int32_t* __restrict__ meta,
                                                   int32_t* __restrict__ num_padded,
                                                   int32_t* __restrict__ block_expert) {
-  __shared__ int seg[257];
+  __shared__ int wsum[4];
   int32_t* offsets = meta + 1;
   int32_t* counts = meta + 1 + (E_l + 1);
   const int e = threadIdx.x;
   int run = 0;
+  int padded = 0;
   if (e < E_l) {
     // chunk counts in batches: the batch's loads are all issued before its stores, one
     // memory round trip per batch instead of one per chunk
@@ -71,28 +92,19 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
       }
     }
     counts[e] = run;
-    seg[e] = (run + bm - 1) / bm * bm;
+    padded = (run + bm - 1) / bm * bm;
   }
-  __syncthreads();
+  int acc;
+  const int off = wg_exclusive_scan(padded, wsum, acc);
   if (e == 0) {
-    int acc = 0;
-    for (int i = 0; i < E_l; ++i) {
-      const int v = seg[i];
-      seg[i] = acc;
-      acc += v;
-    }
-    seg[E_l] = acc;
     offsets[E_l] = acc;
     meta[0] = acc;
     *num_padded = acc;
   }
-  __syncthreads();
   if (e < E_l) {
-    const int off = seg[e];
-    const int end = seg[e + 1];
     offsets[e] = off;
     if (block_expert)  // NULL: no row-block table wanted (the exchange's rank grouping)
-      for (int b = off / bm; b < end / bm; ++b) block_expert[b] = e;
+      for (int b = off / bm; b < (off + padded) / bm; ++b) block_expert[b] = e;
   }
 }
 
@@ -148,7 +160,8 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ sorted_pairs,
                                                     int32_t* __restrict__ pair_row) {
   __shared__ int hist[256];
-  __shared__ int seg[257];
+  __shared__ int seg[256];
+  __shared__ int wsum[4];
   __shared__ unsigned long long mask[4][256];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -171,29 +184,23 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
   __syncthreads();
   int32_t* offsets = meta + 1;
   int32_t* counts = meta + 1 + (E_l + 1);
-  for (int e = tid; e < E_l; e += 256) {
-    counts[e] = hist[e];
-    seg[e] = (hist[e] + bm - 1) / bm * bm;
+  // E_l <= 256: thread e owns slot e
+  const int padded = tid < E_l ? (hist[tid] + bm - 1) / bm * bm : 0;
+  if (tid < E_l) counts[tid] = hist[tid];
+  int acc;
+  const int off = wg_exclusive_scan(padded, wsum, acc);
+  if (tid < E_l) {
+    seg[tid] = off;
+    offsets[tid] = off;
+    if (block_expert)
+      for (int b = off / bm; b < (off + padded) / bm; ++b) block_expert[b] = tid;
   }
-  __syncthreads();
   if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < E_l; ++i) {
-      const int v = seg[i];
-      seg[i] = acc;
-      acc += v;
-    }
-    seg[E_l] = acc;
     offsets[E_l] = acc;
     meta[0] = acc;
     *num_padded = acc;
   }
   __syncthreads();
-  for (int e = tid; e < E_l; e += 256) {
-    offsets[e] = seg[e];
-    if (block_expert)
-      for (int b = seg[e] / bm; b < seg[e + 1] / bm; ++b) block_expert[b] = e;
-  }
   if (!valid) return;
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int j = 0; j < k; ++j) {
