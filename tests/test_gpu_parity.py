@@ -345,6 +345,59 @@ def test_tail_tiles(case):
     assert err <= OUT_TOL["bf16"], err
 
 
+# Experts whose last row block holds 1, 17, 31, 32, 33 or 44 real rows (the gate/up tiles skip
+# the MFMAs of their padding-only 32-row groups), at gate/up widths whose tiles are 256 wide
+# (I = 128) or 128 wide (I = 192), with an even and an odd number of K steps.
+# (H, I, activation, expert-bias std)
+SPARSE = {
+    "silu_w256": (256, 128, "silu", 0.0),
+    "silu_w128": (320, 192, "silu", 0.0),
+    "oai_bias_w256": (320, 128, "swigluoai", 1.0),
+    "oai_bias_w128": (256, 192, "swigluoai", 1.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPARSE))
+def test_sparse_last_blocks(case):
+    """Nearly empty last row blocks of the sorted gate/up: every token's output vs the oracle."""
+    H, I, act, bstd = SPARSE[case]
+    counts = (257, 273, 287, 288, 289, 256, 300, 40)
+    k, bm = 2, 256
+    E = len(counts)
+    T = sum(counts) // k
+    w = W(f"sparse_{case}", 60 + sorted(SPARSE).index(case), "sparse last blocks", "bf16", (T,),
+          H, E, I, k, True, activation=act, expert_bias_std=bstd)
+    layer = Layer(w, T)
+    p = params(w)
+    d = layer.d
+    dev = d["x"].device
+    flat = np.repeat(np.arange(E, dtype=np.int32), counts)
+    ids = np.stack([flat[j * T:(j + 1) * T] for j in range(k)], axis=1)
+    assert all(len(set(r)) == k for r in ids.tolist())
+    rng = np.random.default_rng(11)
+    tw_h = rng.uniform(0.25, 1.0, size=(T, k)).astype(np.float32)
+    local = dev_tensor(ids)
+    tw = dev_tensor(tw_h)
+    assert moe.moe_pick_block_m(p, T) == bm
+    ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
+    cap = moe.moe_sorted_capacity(p, T, bm)
+    sp = torch.empty(cap, dtype=torch.int32, device=dev)
+    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
+    y = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+    moe.moe_grouped_mlp(p, T, d["x"], d["w13"], d["w2"], sp, be, npad, bm, y, ws, b13=d["b13"],
+                        b2=d["b2"])
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    moe.moe_combine(p, T, y, pr, tw, None, out)
+    torch.cuda.synchronize()
+    want = layer.oracle_out(np.arange(T), ids, tw_h, with_shared=False)
+    err = rel_err(out.float().cpu().numpy(), want)
+    print(f"[sparse {case}] T={T} rel_err={err:.3e}", flush=True)
+    assert err <= OUT_TOL["bf16"], err
+
+
 @pytest.mark.parametrize("case", ["ds_s", "skew_s1", "mix_m"])
 def test_graph_replay_matches_eager(case):
     """moe_forward captured in a HIP graph: every replay, with eager work and host syncs in
