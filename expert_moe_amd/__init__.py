@@ -155,10 +155,15 @@ def lib():
 
 
 def _ptr(t):
+    """Device address of a buffer argument: None, an int (taken as a device address as is), or
+    a contiguous tensor in device memory. A host tensor is refused here: the kernels would read
+    its address as device memory."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must be in device memory")
     if not t.is_contiguous():
         raise ValueError("tensor arguments must be contiguous")
     return t.data_ptr()

@@ -126,6 +126,19 @@ def test_workspace_grows_with_tokens():
         moe.moe_workspace_size(p, -1)
 
 
+def test_host_tensor_arguments_are_refused():
+    """A tensor in host memory never reaches a kernel as a device address: the binding raises
+    before calling the library."""
+    import torch
+    p = _params(wl.WORKLOADS["mixtral"])
+    x = torch.zeros(4, 4096, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device memory"):
+        moe.moe_combine(p, 4, x, None, None, None, None, stream=0)
+    with pytest.raises(ValueError, match="device memory"):
+        moe.moe_forward(p, 4, x, None, None, None, None, None, None, None, None, None, None,
+                        None, stream=0)
+
+
 def test_entry_points_zero_tokens_are_noops():
     p = _params(wl.WORKLOADS["mixtral"])
     moe.moe_forward(p, 0, None, None, None, None, None, None, None, None, None, None, None,
