@@ -6,12 +6,13 @@
 // local are grouped by slot, kept in increasing p inside a slot, and each slot's segment is
 // padded to a multiple of block_m rows so that a GEMM tile never straddles two experts.
 //
-// Three passes, no host synchronisation (one single-workgroup kernel when T fits one chunk):
+// Three passes, no host synchronisation (one single-workgroup kernel when T fits one chunk;
+// up to 64 chunks the scan runs inside every scatter workgroup, two kernels):
 //   count   : one workgroup per chunk of 256 tokens, LDS histogram of its pairs per slot; the
 //             workgroups also fill the whole sorted list with -1 (padding)
 //   scan    : one workgroup; per-slot exclusive scan over chunks (chunk bases, read in
-//             batches of 16), padded
-//             segment sizes, exclusive scan over slots (offsets), block -> slot table
+//             batches of 16), padded segment sizes, exclusive scan over slots (offsets),
+//             block -> slot table
 //   scatter : one workgroup per chunk; each wave marks its 64 tokens per slot in an LDS
 //             64-bit mask; a pair's rank inside its slot is the chunk base plus the number of
 //             marked tokens before it (earlier waves, then earlier lanes), which keeps the
@@ -46,6 +47,43 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum, int& total) {
   for (int w = 0; w < wave; ++w) before += wsum[w];
   total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   return before + x - v;
+}
+
+// Scatter of one chunk's pairs (chunk blockIdx.x): each wave marks its 64 tokens per slot in
+// an LDS mask, and a pair's position is base[slot] plus the marked tokens before it (earlier
+// waves, then earlier lanes). base holds this chunk's start per slot and mask is zeroed, both
+// visible to the workgroup; every thread must call it (it holds a barrier).
+__device__ __forceinline__ void chunk_scatter(const int32_t* __restrict__ tl, int T, int k,
+                                              int E_l, const int* base,
+                                              unsigned long long (*mask)[256],
+                                              int32_t* __restrict__ sorted_pairs,
+                                              int32_t* __restrict__ pair_row) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int t = blockIdx.x * kAlignChunk + tid;
+  const bool valid = t < T;
+  if (valid)
+    for (int j = 0; j < k; ++j) {
+      const int s = local_slot(tl, static_cast<int64_t>(t) * k + j, E_l);
+      if (s >= 0) atomicOr(&mask[wave][s], 1ull << lane);
+    }
+  __syncthreads();
+  if (!valid) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int64_t pid = static_cast<int64_t>(t) * k + j;
+    const int s = local_slot(tl, pid, E_l);
+    if (s < 0) {
+      pair_row[pid] = -1;
+      continue;
+    }
+    int before = __popcll(mask[wave][s] & below);
+    for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
+    const int pos = base[s] + before;
+    sorted_pairs[pos] = static_cast<int32_t>(pid);
+    pair_row[pid] = pos;
+  }
 }
 
 __global__ void __launch_bounds__(256) align_count(const int32_t* __restrict__ tl, int T, int k,
@@ -124,29 +162,63 @@ __global__ void __launch_bounds__(256) align_scatter(const int32_t* __restrict__
     mask[0][e] = mask[1][e] = mask[2][e] = mask[3][e] = 0ull;
   }
   __syncthreads();
-  const int t = blockIdx.x * kAlignChunk + tid;
-  const bool valid = t < T;
-  if (valid)
-    for (int j = 0; j < k; ++j) {
-      const int s = local_slot(tl, static_cast<int64_t>(t) * k + j, E_l);
-      if (s >= 0) atomicOr(&mask[wave][s], 1ull << lane);
+  chunk_scatter(tl, T, k, E_l, base, mask, sorted_pairs, pair_row);
+}
+
+// Scan and scatter in one pass, for a few chunks (the launch then has two kernels instead of
+// three): every workgroup reads all chunks' counts per slot (nchunks x E_l values), takes its
+// own chunk base and the padded segment offsets from them, and workgroup 0 writes the
+// metadata and the block -> slot table that align_scan writes in the three-pass form.
+__global__ void __launch_bounds__(256) align_scan_scatter(const int32_t* __restrict__ tl, int T,
+                                                          int k, int E_l, int bm,
+                                                          const int32_t* __restrict__ chunk,
+                                                          int nchunks, int32_t* __restrict__ meta,
+                                                          int32_t* __restrict__ num_padded,
+                                                          int32_t* __restrict__ block_expert,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ pair_row) {
+  __shared__ unsigned long long mask[4][256];
+  __shared__ int base[256];
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;  // slot of this thread (E_l <= 256)
+  const int c = blockIdx.x;
+  int pre = 0, tot = 0;
+  if (e < E_l) {
+    constexpr int kBatch = 16;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < nchunks ? chunk[static_cast<int64_t>(c0 + j) * E_l + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (c0 + j < c) pre += v[j];
+        tot += v[j];
+      }
     }
-  __syncthreads();
-  if (!valid) return;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const int64_t pid = static_cast<int64_t>(t) * k + j;
-    const int s = local_slot(tl, pid, E_l);
-    if (s < 0) {
-      pair_row[pid] = -1;
-      continue;
-    }
-    int before = __popcll(mask[wave][s] & below);
-    for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
-    const int pos = base[s] + before;
-    sorted_pairs[pos] = static_cast<int32_t>(pid);
-    pair_row[pid] = pos;
+    mask[0][e] = mask[1][e] = mask[2][e] = mask[3][e] = 0ull;
   }
+  const int padded = (tot + bm - 1) / bm * bm;
+  int acc;
+  const int off = wg_exclusive_scan(padded, wsum, acc);
+  if (e < E_l) base[e] = off + pre;
+  if (c == 0) {
+    int32_t* offsets = meta + 1;
+    int32_t* counts = meta + 1 + (E_l + 1);
+    if (e < E_l) {
+      counts[e] = tot;
+      offsets[e] = off;
+      if (block_expert)
+        for (int b = off / bm; b < (off + padded) / bm; ++b) block_expert[b] = e;
+    }
+    if (e == 0) {
+      offsets[E_l] = acc;
+      meta[0] = acc;
+      *num_padded = acc;
+    }
+  }
+  __syncthreads();
+  chunk_scatter(tl, T, k, E_l, base, mask, sorted_pairs, pair_row);
 }
 
 // All three passes in one workgroup, for T <= kAlignChunk (one chunk): LDS histogram and
@@ -220,6 +292,9 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
 
 }  // namespace
 
+// Up to this many chunks (T <= 16384) each scatter workgroup scans the counts itself.
+constexpr int kFusedScanChunks = 64;
+
 int launch_align(const moe_params& p, int T, const int32_t* topk_local, int block_m,
                  int32_t* sorted_pairs, int32_t* block_expert, int32_t* pair_row,
                  int32_t* num_padded, int32_t* meta, int32_t* chunk, hipStream_t s) {
@@ -235,6 +310,13 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
   }
   align_count<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, sorted_pairs, cap);
   MOE_LAUNCH_CHECK();
+  if (nchunks <= kFusedScanChunks) {
+    align_scan_scatter<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, block_m, chunk, nchunks,
+                                               meta, num_padded, block_expert, sorted_pairs,
+                                               pair_row);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   align_scan<<<1, 256, 0, s>>>(chunk, nchunks, E_l, block_m, meta, num_padded, block_expert);
   MOE_LAUNCH_CHECK();
   align_scatter<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, meta, sorted_pairs, pair_row);

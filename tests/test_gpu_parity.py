@@ -345,6 +345,36 @@ def test_tail_tiles(case):
     assert err <= OUT_TOL["bf16"], err
 
 
+@pytest.mark.parametrize("T,E_l,block_m", [(257, 64, 256), (16384, 64, 256), (16385, 64, 128),
+                                           (16385, 8, 16), (4000, 256, 16)])
+def test_align_chunk_counts(T, E_l, block_m):
+    """moe_align_permute bit for bit against the oracle on both sides of the chunk count (64
+    chunks of 256 tokens) up to which each scatter workgroup scans the counts itself; seeded
+    slot lists with non-local (-1) entries."""
+    k = 8
+    rng = np.random.default_rng(T + E_l)
+    local = np.stack([rng.permutation(E_l + 16)[:k] for _ in range(T)]).astype(np.int32)
+    local[local >= E_l] = -1
+    w = W("align_chunks", 70, "align sizes", "bf16", (T,), 128, E_l, 128, k, True)
+    p = params(w)
+    dev = torch.device("cuda:0")
+    ws = torch.empty(moe.moe_workspace_size(p, T, block_m), dtype=torch.uint8, device=dev)
+    cap = moe.moe_sorted_capacity(p, T, block_m)
+    sp = torch.full((cap,), 7, dtype=torch.int32, device=dev)
+    be = torch.full((cap // block_m + 1,), -5, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_align_permute(p, T, dev_tensor(local), block_m, sp, be, pr, npad, ws)
+    torch.cuda.synchronize()
+    a = oracle.align_permute(local, E_l, block_m)
+    n = int(npad.item())
+    assert n == a["num_padded"]
+    assert np.array_equal(sp.cpu().numpy()[:n], a["sorted_pairs"])
+    assert np.all(sp.cpu().numpy()[n:] == -1)
+    assert np.array_equal(be.cpu().numpy()[:n // block_m], a["block_expert"])
+    assert np.array_equal(pr.cpu().numpy(), a["pair_row"])
+
+
 # Experts whose last row block holds 1, 17, 31, 32, 33 or 44 real rows (the gate/up tiles skip
 # the MFMAs of their padding-only 32-row groups), at gate/up widths whose tiles are 256 wide
 # (I = 128) or 128 wide (I = 192), with an even and an odd number of K steps.
