@@ -133,12 +133,22 @@ class Bench:
         self.sy = torch.empty(T, H, dtype=dt, device=dev) if w.shared_intermediate_size else None
         self.sws = torch.empty(moe.moe_workspace_size(self.p, T, self.bm), dtype=torch.uint8,
                                device=dev)
+        # a shared expert runs beside the routed path on a side stream of ours (default
+        # priority), forked and joined by two events
+        self.side = None
+        if w.shared_intermediate_size:
+            st = torch.cuda.Stream(device=dev)
+            fork, join = torch.cuda.Event(), torch.cuda.Event()
+            fork.record(st)
+            join.record(st)
+            self.side = moe.make_side_stream(st, fork, join)
 
     def forward(self):
         d = self.d
-        self.moe.moe_forward(self.p, self.T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
-                             d["w2"], d["sw13"], d["sw2"], self.out, self.ids, self.tw, self.ws,
-                             score_bias=d["sbias"], b13=d["b13"], b2=d["b2"])
+        self.moe.moe_forward_overlap(self.p, self.side, self.T, d["x"], d["gate"], d["bias"],
+                                     d["emap"], d["w13"], d["w2"], d["sw13"], d["sw2"], self.out,
+                                     self.ids, self.tw, self.ws, score_bias=d["sbias"],
+                                     b13=d["b13"], b2=d["b2"])
 
     def split_step(self, ev=None):
         """The same kernels as moe_forward through the split entry points; events at stage ends."""

@@ -8,7 +8,9 @@ importing a function fails loudly when the library has not been built.
 
 Tensor arguments are ``torch`` tensors already on the GPU (bf16 data is passed as
 ``torch.bfloat16``; fp32 as ``torch.float32``; ids as ``torch.int32``); ``None`` passes
-NULL. PyTorch is used for device memory and streams only.
+NULL. Before the library is called, each tensor's dtype and element count are checked against
+the shapes ``include/moe.h`` states for the call (a raw integer address is passed unchecked).
+PyTorch is used for device memory and streams only.
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ EXPORTS = (
     "moe_align_permute", "moe_grouped_mlp", "moe_expert_gate_up", "moe_expert_down",
     "moe_shared_mlp", "moe_combine", "moe_forward",
     "moe_ep_send_capacity", "moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_combine",
-    "moe_eplb_tables", "moe_route_eplb", "moe_forward_eplb",
+    "moe_eplb_tables", "moe_route_eplb", "moe_forward_eplb", "moe_forward_overlap",
 )
 
 
@@ -70,6 +72,33 @@ class moe_eplb(ctypes.Structure):
     ]
 
 
+class moe_side_stream(ctypes.Structure):
+    """Mirror of ``struct moe_side_stream`` in include/moe.h (stream and event handles)."""
+    _fields_ = [
+        ("stream", ctypes.c_void_p),
+        ("fork_event", ctypes.c_void_p),
+        ("join_event", ctypes.c_void_p),
+    ]
+
+
+def _event(e):
+    if e is None or isinstance(e, int):
+        return e
+    h = e.cuda_event
+    if not h:
+        raise ValueError("the event has no handle yet (torch creates it on its first record); "
+                         "record it once before passing it")
+    return h
+
+
+def make_side_stream(stream, fork_event, join_event) -> moe_side_stream:
+    """A ``moe_side_stream`` from a torch stream (or raw handle) and two torch events (or raw
+    handles). The struct holds references to its arguments, so they live as long as it does."""
+    s = moe_side_stream(_stream(stream), _event(fork_event), _event(join_event))
+    s._keep = (stream, fork_event, join_event)
+    return s
+
+
 def make_eplb(num_physical_experts, max_replicas, logical_to_physical, replica_count):
     """A ``moe_eplb`` over device tables (tensors or raw addresses). The returned struct holds
     references to tensor arguments, so they live as long as it does."""
@@ -100,8 +129,27 @@ def make_params(num_experts, top_k, hidden_size, intermediate_size, renormalize=
         int(bool(renormalize)), int(bool(use_grouped_topk)), int(num_expert_group),
         int(topk_group), float(routed_scaling_factor),
         int(num_experts if num_local_experts is None else num_local_experts),
-        int(shared_intermediate_size), MOE_BF16 if dtype in ("bf16", MOE_BF16) else MOE_F32, sf,
-        act)
+        int(shared_intermediate_size), _dtype_code(dtype), sf, act)
+
+
+def _dtype_code(dtype) -> int:
+    """MOE_BF16 or MOE_F32 from a name, a code or a torch dtype; ValueError otherwise."""
+    if isinstance(dtype, str):
+        names = {"bf16": MOE_BF16, "bfloat16": MOE_BF16, "f32": MOE_F32, "fp32": MOE_F32,
+                 "float32": MOE_F32}
+        if dtype in names:
+            return names[dtype]
+    elif isinstance(dtype, int) and not isinstance(dtype, bool):
+        if dtype in (MOE_BF16, MOE_F32):
+            return dtype
+    else:
+        import torch
+        if dtype == torch.bfloat16:
+            return MOE_BF16
+        if dtype == torch.float32:
+            return MOE_F32
+    raise ValueError(f"dtype {dtype!r}: expected bf16 or f32 (a name, MOE_BF16 / MOE_F32 or a "
+                     "torch dtype)")
 
 
 _lib = None
@@ -136,6 +184,8 @@ _SIGS = {
                        ctypes.c_int),
     "moe_forward_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_forward_overlap": ([_P, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -167,6 +217,21 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensor arguments must be contiguous")
     return t.data_ptr()
+
+
+def _check_tensors(p, checks):
+    """Host-side argument checks before a call: each (name, tensor, kind, min_elements) with
+    kind "data" (p's dtype), "f32" or "i32"; None and raw addresses pass. Raises ValueError."""
+    import torch
+    data = torch.bfloat16 if p.dtype == MOE_BF16 else torch.float32
+    want = {"data": data, "f32": torch.float32, "i32": torch.int32}
+    for name, t, kind, n in checks:
+        if t is None or isinstance(t, int):
+            continue
+        if t.dtype != want[kind]:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {want[kind]}")
+        if t.numel() < n:
+            raise ValueError(f"{name}: {t.numel()} elements, at least {n} expected")
 
 
 def _stream(stream):
@@ -228,16 +293,46 @@ def moe_weight_bytes(n_experts: int, hidden: int, inter: int, dtype_bytes: int, 
     return lib().moe_weight_bytes(n_experts, hidden, inter, dtype_bytes, layers)
 
 
+def _route_checks(p, T, x, w_gate, logit_bias, score_bias, expert_map, n_map):
+    E, H = p.num_experts, p.hidden_size
+    return [("x", x, "data", T * H), ("w_gate", w_gate, "data", E * H),
+            ("logit_bias", logit_bias, "f32", E), ("score_bias", score_bias, "f32", E),
+            ("expert_map", expert_map, "i32", n_map)]
+
+
+def _expert_checks(p, w13, w2, b13, b2):
+    El, H, I = p.num_local_experts, p.hidden_size, p.intermediate_size
+    return [("w13", w13, "data", El * 2 * I * H), ("w2", w2, "data", El * H * I),
+            ("b13", b13, "f32", El * 2 * I), ("b2", b2, "f32", El * H)]
+
+
 def moe_route(p, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w, topk_local,
               ws, stream=None, score_bias=None):
+    Tk = num_tokens * p.top_k
+    _check_tensors(p, _route_checks(p, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                                    p.num_experts)
+                   + [("topk_ids", topk_ids, "i32", Tk), ("topk_w", topk_w, "f32", Tk),
+                      ("topk_local", topk_local, "i32", Tk)])
     wp, wn = _ws(ws)
     _check(lib().moe_route(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w_gate), _ptr(logit_bias),
                            _ptr(score_bias), _ptr(expert_map), _ptr(topk_ids), _ptr(topk_w), _ptr(topk_local),
                            wp, wn, _stream(stream)), "moe_route")
 
 
+def _sorted_rows(p, num_tokens, block_m):
+    try:
+        return moe_sorted_capacity(p, num_tokens, block_m)
+    except MoeError:
+        return 0  # the library reports the invalid argument itself
+
+
 def moe_align_permute(p, num_tokens, topk_local, block_m, sorted_pairs, block_expert, pair_row,
                       num_padded, ws, stream=None):
+    cap = _sorted_rows(p, num_tokens, block_m)
+    Tk = num_tokens * p.top_k
+    _check_tensors(p, [("topk_local", topk_local, "i32", Tk), ("sorted_pairs", sorted_pairs, "i32", cap),
+                       ("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                       ("pair_row", pair_row, "i32", Tk), ("num_padded", num_padded, "i32", 1)])
     wp, wn = _ws(ws)
     _check(lib().moe_align_permute(ctypes.byref(p), num_tokens, _ptr(topk_local), block_m,
                                    _ptr(sorted_pairs), _ptr(block_expert), _ptr(pair_row),
@@ -246,6 +341,11 @@ def moe_align_permute(p, num_tokens, topk_local, block_m, sorted_pairs, block_ex
 
 def moe_grouped_mlp(p, num_tokens, x, w13, w2, sorted_pairs, block_expert, num_padded, block_m,
                     y, ws, stream=None, b13=None, b2=None):
+    cap = _sorted_rows(p, num_tokens, block_m)
+    _check_tensors(p, [("x", x, "data", num_tokens * p.hidden_size)] + _expert_checks(p, w13, w2, b13, b2)
+                   + [("sorted_pairs", sorted_pairs, "i32", cap),
+                      ("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                      ("num_padded", num_padded, "i32", 1), ("y", y, "data", cap * p.hidden_size)])
     wp, wn = _ws(ws)
     _check(lib().moe_grouped_mlp(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(w2),
                                  _ptr(b13), _ptr(b2), _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
@@ -254,6 +354,13 @@ def moe_grouped_mlp(p, num_tokens, x, w13, w2, sorted_pairs, block_expert, num_p
 
 def moe_expert_gate_up(p, num_tokens, x, w13, sorted_pairs, block_expert, num_padded, block_m,
                        act, stream=None, b13=None):
+    cap = _sorted_rows(p, num_tokens, block_m)
+    _check_tensors(p, [("x", x, "data", num_tokens * p.hidden_size)]
+                   + _expert_checks(p, w13, None, b13, None)
+                   + [("sorted_pairs", sorted_pairs, "i32", cap),
+                      ("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                      ("num_padded", num_padded, "i32", 1),
+                      ("act", act, "data", cap * p.intermediate_size)])
     _check(lib().moe_expert_gate_up(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(b13),
                                     _ptr(sorted_pairs), _ptr(block_expert), _ptr(num_padded),
                                     block_m, _ptr(act), _stream(stream)), "moe_expert_gate_up")
@@ -261,12 +368,21 @@ def moe_expert_gate_up(p, num_tokens, x, w13, sorted_pairs, block_expert, num_pa
 
 def moe_expert_down(p, num_tokens, act, w2, block_expert, num_padded, block_m, y, stream=None,
                     b2=None):
+    cap = _sorted_rows(p, num_tokens, block_m)
+    _check_tensors(p, [("act", act, "data", cap * p.intermediate_size)]
+                   + _expert_checks(p, None, w2, None, b2)
+                   + [("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                      ("num_padded", num_padded, "i32", 1), ("y", y, "data", cap * p.hidden_size)])
     _check(lib().moe_expert_down(ctypes.byref(p), num_tokens, _ptr(act), _ptr(w2), _ptr(b2),
                                  _ptr(block_expert), _ptr(num_padded), block_m, _ptr(y),
                                  _stream(stream)), "moe_expert_down")
 
 
 def moe_shared_mlp(p, num_tokens, x, shared_w13, shared_w2, shared_y, ws, stream=None):
+    H, Is = p.hidden_size, p.shared_intermediate_size
+    _check_tensors(p, [("x", x, "data", num_tokens * H), ("shared_w13", shared_w13, "data", 2 * Is * H),
+                       ("shared_w2", shared_w2, "data", H * Is),
+                       ("shared_y", shared_y, "data", num_tokens * H)])
     wp, wn = _ws(ws)
     _check(lib().moe_shared_mlp(ctypes.byref(p), num_tokens, _ptr(x), _ptr(shared_w13),
                                 _ptr(shared_w2), _ptr(shared_y), wp, wn, _stream(stream)),
@@ -274,13 +390,30 @@ def moe_shared_mlp(p, num_tokens, x, shared_w13, shared_w2, shared_y, ws, stream
 
 
 def moe_combine(p, num_tokens, y, pair_row, topk_w, shared_y, out, stream=None):
+    Tk, TH = num_tokens * p.top_k, num_tokens * p.hidden_size
+    _check_tensors(p, [("y", y, "data", 0), ("pair_row", pair_row, "i32", Tk),
+                       ("topk_w", topk_w, "f32", Tk), ("shared_y", shared_y, "data", TH),
+                       ("out", out, "data", TH)])
     _check(lib().moe_combine(ctypes.byref(p), num_tokens, _ptr(y), _ptr(pair_row), _ptr(topk_w),
                              _ptr(shared_y), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def _forward_checks(p, T, x, w_gate, logit_bias, score_bias, expert_map, n_map, w13, w2, b13, b2,
+                    shared_w13, shared_w2, out, topk_ids_out, topk_w_out):
+    H, Is, Tk = p.hidden_size, p.shared_intermediate_size, T * p.top_k
+    return (_route_checks(p, T, x, w_gate, logit_bias, score_bias, expert_map, n_map)
+            + _expert_checks(p, w13, w2, b13, b2)
+            + [("shared_w13", shared_w13, "data", 2 * Is * H), ("shared_w2", shared_w2, "data", H * Is),
+               ("out", out, "data", T * H), ("topk_ids_out", topk_ids_out, "i32", Tk),
+               ("topk_w_out", topk_w_out, "f32", Tk)])
 
 
 def moe_forward(p, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
                 shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None,
                 b13=None, b2=None):
+    _check_tensors(p, _forward_checks(p, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                                      p.num_experts, w13, w2, b13, b2, shared_w13, shared_w2, out,
+                                      topk_ids_out, topk_w_out))
     wp, wn = _ws(ws)
     _check(lib().moe_forward(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w_gate), _ptr(logit_bias),
                              _ptr(score_bias), _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(b13),
@@ -305,6 +438,16 @@ def moe_ep_workspace_size(p, num_tokens: int, ep_size: int) -> int:
 
 def moe_ep_dispatch(p, num_tokens, ep_size, topk_ids, topk_w, x, send_pos, rank_meta, send_token,
                     send_x, send_local, send_w, ws, stream=None):
+    try:
+        R = moe_ep_send_capacity(p, num_tokens, ep_size)
+    except MoeError:
+        R = 0  # the library reports the invalid argument itself
+    Tk, k, H = num_tokens * p.top_k, p.top_k, p.hidden_size
+    _check_tensors(p, [("topk_ids", topk_ids, "i32", Tk), ("topk_w", topk_w, "f32", Tk),
+                       ("x", x, "data", num_tokens * H), ("send_pos", send_pos, "i32", Tk),
+                       ("rank_meta", rank_meta, "i32", 2 * ep_size + 2),
+                       ("send_token", send_token, "i32", R), ("send_x", send_x, "data", R * H),
+                       ("send_local", send_local, "i32", R * k), ("send_w", send_w, "f32", R * k)])
     wp, wn = _ws(ws)
     _check(lib().moe_ep_dispatch(ctypes.byref(p), num_tokens, ep_size, _ptr(topk_ids), _ptr(topk_w),
                                  _ptr(x), _ptr(send_pos), _ptr(rank_meta), _ptr(send_token),
@@ -313,6 +456,9 @@ def moe_ep_dispatch(p, num_tokens, ep_size, topk_ids, topk_w, x, send_pos, rank_
 
 
 def moe_ep_combine(p, num_tokens, send_pos, recv_y, out, stream=None):
+    _check_tensors(p, [("send_pos", send_pos, "i32", num_tokens * p.top_k),
+                       ("recv_y", recv_y, "data", 0),
+                       ("out", out, "data", num_tokens * p.hidden_size)])
     _check(lib().moe_ep_combine(ctypes.byref(p), num_tokens, _ptr(send_pos), _ptr(recv_y), _ptr(out),
                                 _stream(stream)), "moe_ep_combine")
 
@@ -332,6 +478,11 @@ def moe_eplb_tables(num_logical: int, physical_to_logical, max_replicas: int | N
 
 def moe_route_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w,
                    topk_local, ws, stream=None, score_bias=None):
+    Tk = num_tokens * p.top_k
+    _check_tensors(p, _route_checks(p, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                                    eplb.num_physical_experts)
+                   + [("topk_ids", topk_ids, "i32", Tk), ("topk_w", topk_w, "f32", Tk),
+                      ("topk_local", topk_local, "i32", Tk)])
     wp, wn = _ws(ws)
     _check(lib().moe_route_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
                                 _ptr(w_gate), _ptr(logit_bias), _ptr(score_bias), _ptr(expert_map), _ptr(topk_ids),
@@ -342,6 +493,9 @@ def moe_route_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, topk_
 def moe_forward_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
                      shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None, score_bias=None,
                      b13=None, b2=None):
+    _check_tensors(p, _forward_checks(p, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                                      eplb.num_physical_experts, w13, w2, b13, b2, shared_w13,
+                                      shared_w2, out, topk_ids_out, topk_w_out))
     wp, wn = _ws(ws)
     _check(lib().moe_forward_eplb(ctypes.byref(p), ctypes.byref(eplb), num_tokens, _ptr(x),
                                   _ptr(w_gate), _ptr(logit_bias), _ptr(score_bias),
@@ -349,3 +503,22 @@ def moe_forward_eplb(p, eplb, num_tokens, x, w_gate, logit_bias, expert_map, w13
                                   _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
                                   _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
            "moe_forward_eplb")
+
+
+def moe_forward_overlap(p, side, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2,
+                        shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None,
+                        score_bias=None, b13=None, b2=None, eplb=None):
+    """moe_forward (or moe_forward_eplb with ``eplb``) with the shared expert on the caller's
+    side stream; ``side`` is a ``moe_side_stream`` (see ``make_side_stream``) or None."""
+    n_map = eplb.num_physical_experts if eplb is not None else p.num_experts
+    _check_tensors(p, _forward_checks(p, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                                      n_map, w13, w2, b13, b2, shared_w13, shared_w2, out,
+                                      topk_ids_out, topk_w_out))
+    wp, wn = _ws(ws)
+    _check(lib().moe_forward_overlap(ctypes.byref(p), ctypes.byref(eplb) if eplb is not None else None,
+                                     ctypes.byref(side) if side is not None else None, num_tokens,
+                                     _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(score_bias),
+                                     _ptr(expert_map), _ptr(w13), _ptr(w2), _ptr(b13), _ptr(b2),
+                                     _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
+                                     _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
+           "moe_forward_overlap")

@@ -303,25 +303,20 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
   const int nchunks = align_chunks(T);
   const int cap = T * k + E_l * (block_m - 1);
   if (nchunks == 1) {
-    align_single<<<1, 256, 0, s>>>(topk_local, T, k, E_l, block_m, cap, meta, num_padded, block_expert,
-                                   sorted_pairs, pair_row);
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
+    return launch(align_single, 1, 256, 0, s, topk_local, T, k, E_l, block_m, cap, meta,
+                  num_padded, block_expert, sorted_pairs, pair_row);
   }
-  align_count<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, sorted_pairs, cap);
-  MOE_LAUNCH_CHECK();
-  if (nchunks <= kFusedScanChunks) {
-    align_scan_scatter<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, block_m, chunk, nchunks,
-                                               meta, num_padded, block_expert, sorted_pairs,
-                                               pair_row);
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-  }
-  align_scan<<<1, 256, 0, s>>>(chunk, nchunks, E_l, block_m, meta, num_padded, block_expert);
-  MOE_LAUNCH_CHECK();
-  align_scatter<<<nchunks, 256, 0, s>>>(topk_local, T, k, E_l, chunk, meta, sorted_pairs, pair_row);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  if (int rc = launch(align_count, nchunks, 256, 0, s, topk_local, T, k, E_l, chunk, sorted_pairs,
+                      cap))
+    return rc;
+  if (nchunks <= kFusedScanChunks)
+    return launch(align_scan_scatter, nchunks, 256, 0, s, topk_local, T, k, E_l, block_m, chunk,
+                  nchunks, meta, num_padded, block_expert, sorted_pairs, pair_row);
+  if (int rc = launch(align_scan, 1, 256, 0, s, chunk, nchunks, E_l, block_m, meta, num_padded,
+                      block_expert))
+    return rc;
+  return launch(align_scatter, nchunks, 256, 0, s, topk_local, T, k, E_l, chunk, meta,
+                sorted_pairs, pair_row);
 }
 
 }  // namespace moe

@@ -2,7 +2,6 @@
 // Declarations and the contract of every entry point are in include/moe.h.
 #include <initializer_list>
 #include <math.h>
-#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -131,36 +130,6 @@ Layout layout(const moe_params& p, int64_t T, int bm) {
   // each of them because it is at least the scratch region plus the align tables.
   if (L.align_need > L.total) L.total = L.align_need;
   return L;
-}
-
-// Side stream of a device for the shared expert. Its MLP reads only x and its own weights, so
-// it can run beside router, alignment and routed MLP, where its tiles fill the CUs that their
-// launches leave idle (last rounds, few-tile launches). One stream and a fork / join event pair
-// per device, created on first use (default priority, non-blocking); the mutex keeps each
-// caller's record / wait pairs together. Unavailable (creation failed): the caller's stream
-// runs the shared MLP in order.
-struct SideStream {
-  std::mutex mu;
-  bool tried = false;
-  bool ok = false;
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr;
-  hipEvent_t join = nullptr;
-};
-
-SideStream* side_stream() {
-  static SideStream side[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream& ss = side[dev];
-  std::lock_guard<std::mutex> lk(ss.mu);
-  if (!ss.tried) {
-    ss.tried = true;
-    ss.ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return ss.ok ? &ss : nullptr;
 }
 
 template <typename T_>
@@ -364,19 +333,21 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
 }
 
 // moe_forward with an optional replicated placement (eplb = NULL: the expert map is by expert id)
-static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num_tokens,
-                        const void* x, const void* w_gate, const float* logit_bias,
-                        const float* score_bias, const int32_t* expert_map, const void* w13,
-                        const void* w2, const float* b13, const float* b2,
-                        const void* shared_w13, const void* shared_w2, void* out,
-                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                        void* stream) {
+// and an optional caller-owned side stream for the shared expert (side = NULL: one stream).
+static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, const moe_side_stream* side,
+                        int64_t num_tokens, const void* x, const void* w_gate,
+                        const float* logit_bias, const float* score_bias,
+                        const int32_t* expert_map, const void* w13, const void* w2,
+                        const float* b13, const float* b2, const void* shared_w13,
+                        const void* shared_w2, void* out, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
   if ((shared_w13 == nullptr) != (shared_w2 == nullptr)) return MOE_EINVAL;
   const bool shared = shared_w13 != nullptr;
   if (shared && p->shared_intermediate_size == 0) return MOE_EINVAL;
+  if (side && (!side->fork_event || !side->join_event || side->stream == stream)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w_gate || !expert_map || !w13 || !w2 || !out || !ws) return MOE_EINVAL;
   if (!aligned16({x, w_gate, w13, w2, b13, b2, shared_w13, shared_w2, out, ws})) return MOE_EINVAL;
@@ -402,41 +373,48 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t n
                            nullptr, nullptr, 0, T, shared_act, shared_y, st);
   };
 
-  // Shared expert: forked onto the side stream (after everything the caller queued before) when
-  // its gate/up projection is at most four rounds of 256x256 tiles. Measured on MI355X: beside
-  // the routed path it saves 2-8% where that path leaves CUs idle (DeepSeek-V2-shaped T=4096,
-  // skewed T=1 and T=256); two long GEMMs side by side (skewed T=16384, six rounds) lose 1.6%
-  // to cache contention, so those run in order.
+  // Shared expert beside the routed path, on the caller's side stream, when its gate/up
+  // projection is at most four rounds of 256x256 tiles. Measured on MI355X: it then fills the
+  // CUs that the routed path's launches leave idle (2-8% on the DeepSeek-V2-shaped layer at
+  // T=4096 and the skewed layer at T=1 and T=256); two long GEMMs side by side (skewed T=16384,
+  // six rounds) lose 1.6% to cache contention, so those run in order on `stream`.
   const int n_cu = moe::device_cu_count();
   const int64_t shared_tiles = (static_cast<int64_t>(T) + 255) / 256 *
                                ((2 * static_cast<int64_t>(p->shared_intermediate_size) + 255) / 256);
-  SideStream* side = shared && n_cu > 0 && shared_tiles <= 4 * static_cast<int64_t>(n_cu) ? side_stream() : nullptr;
-  std::unique_lock<std::mutex> lk;
-  if (side) {
-    lk = std::unique_lock<std::mutex>(side->mu);
-    if (hipEventRecord(side->fork, s) != hipSuccess ||
-        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+  const bool fork = side && shared && n_cu > 0 && shared_tiles <= 4 * static_cast<int64_t>(n_cu);
+  hipStream_t ss = nullptr;
+  hipEvent_t join = nullptr;
+  if (fork) {
+    ss = as_stream(side->stream);
+    const hipEvent_t fork_ev = static_cast<hipEvent_t>(side->fork_event);
+    join = static_cast<hipEvent_t>(side->join_event);
+    if (hipEventRecord(fork_ev, s) != hipSuccess || hipStreamWaitEvent(ss, fork_ev, 0) != hipSuccess)
       return MOE_EHIP;
-    if ((rc = shared_mlp(side->stream))) return rc;
-    if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_EHIP;
+    rc = shared_mlp(ss);
+    // the join is recorded whatever the launches returned, and `stream` always waits for it
+    // below: no work on the side stream is left unjoined (a HIP graph capture needs every
+    // forked stream joined back)
+    if (hipEventRecord(join, ss) != hipSuccess) return rc ? rc : MOE_EHIP;
   }
-
-  if ((rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s))) return rc;
-  if ((rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, score_bias,
-                             expert_map, ids, tw, local, s, eplb)))
-    return rc;
-  if ((rc = moe::launch_align(*p, T, local, bm, sorted_pairs, block_expert, pair_row, num_padded,
-                              at<int32_t>(ws, L.meta), at<int32_t>(ws, L.chunk), s)))
-    return rc;
-  const int rows = static_cast<int>(capacity(*p, T, bm));
-  if ((rc = moe::launch_mlp(*p, T, x, w13, w2, p->intermediate_size, sorted_pairs, num_padded,
-                            block_expert, bm, rows, scratch, y, s, b13, b2)))
-    return rc;
-  if (side) {
-    if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return MOE_EHIP;
-  } else if (shared && (rc = shared_mlp(s))) {
-    return rc;
+  if (rc == MOE_OK)
+    rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s);
+  if (rc == MOE_OK)
+    rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, score_bias, expert_map,
+                          ids, tw, local, s, eplb);
+  if (rc == MOE_OK)
+    rc = moe::launch_align(*p, T, local, bm, sorted_pairs, block_expert, pair_row, num_padded,
+                           at<int32_t>(ws, L.meta), at<int32_t>(ws, L.chunk), s);
+  if (rc == MOE_OK) {
+    const int rows = static_cast<int>(capacity(*p, T, bm));
+    rc = moe::launch_mlp(*p, T, x, w13, w2, p->intermediate_size, sorted_pairs, num_padded,
+                         block_expert, bm, rows, scratch, y, s, b13, b2);
   }
+  if (fork) {
+    if (hipStreamWaitEvent(s, join, 0) != hipSuccess && rc == MOE_OK) rc = MOE_EHIP;
+  } else if (rc == MOE_OK && shared) {
+    rc = shared_mlp(s);
+  }
+  if (rc) return rc;
   return moe::launch_combine(*p, T, y, pair_row, tw, shared_y, out, s);
 }
 
@@ -445,9 +423,9 @@ int moe_forward(const moe_params* p, int64_t num_tokens, const void* x, const vo
                 const void* w13, const void* w2, const float* b13, const float* b2,
                 const void* shared_w13, const void* shared_w2, void* out, int32_t* topk_ids_out,
                 float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(p, nullptr, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, w13,
-                      w2, b13, b2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws,
-                      ws_bytes, stream);
+  return forward_impl(p, nullptr, nullptr, num_tokens, x, w_gate, logit_bias, score_bias,
+                      expert_map, w13, w2, b13, b2, shared_w13, shared_w2, out, topk_ids_out,
+                      topk_w_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -512,9 +490,26 @@ int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_toke
   moe::EplbMap m;
   int rc = check_eplb(p, eplb, &m);
   if (rc) return rc;
-  return forward_impl(p, &m, num_tokens, x, w_gate, logit_bias, score_bias, expert_map, w13, w2,
-                      b13, b2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws, ws_bytes,
-                      stream);
+  return forward_impl(p, &m, nullptr, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                      w13, w2, b13, b2, shared_w13, shared_w2, out, topk_ids_out, topk_w_out, ws,
+                      ws_bytes, stream);
+}
+
+int moe_forward_overlap(const moe_params* p, const moe_eplb* eplb, const moe_side_stream* side,
+                        int64_t num_tokens, const void* x, const void* w_gate,
+                        const float* logit_bias, const float* score_bias,
+                        const int32_t* expert_map, const void* w13, const void* w2,
+                        const float* b13, const float* b2, const void* shared_w13,
+                        const void* shared_w2, void* out, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  moe::EplbMap m;
+  if (eplb) {
+    int rc = check_eplb(p, eplb, &m);
+    if (rc) return rc;
+  }
+  return forward_impl(p, eplb ? &m : nullptr, side, num_tokens, x, w_gate, logit_bias,
+                      score_bias, expert_map, w13, w2, b13, b2, shared_w13, shared_w2, out,
+                      topk_ids_out, topk_w_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

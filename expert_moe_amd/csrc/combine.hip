@@ -120,15 +120,12 @@ __global__ void __launch_bounds__(256) combine_f32(const float* __restrict__ y,
 int launch_combine(const moe_params& p, int T, const void* y, const int32_t* pair_row,
                    const float* topk_w, const void* shared_y, void* out, hipStream_t s) {
   if (p.dtype == MOE_F32)
-    combine_f32<<<T, 256, 0, s>>>(static_cast<const float*>(y), pair_row, topk_w,
-                                  static_cast<const float*>(shared_y), static_cast<float*>(out),
-                                  p.top_k, p.hidden_size);
-  else
-    combine_bf16<<<T, 256, 0, s>>>(static_cast<const uint16_t*>(y), pair_row, topk_w,
-                                   static_cast<const uint16_t*>(shared_y),
-                                   static_cast<uint16_t*>(out), p.top_k, p.hidden_size);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+    return launch(combine_f32, T, 256, 0, s, static_cast<const float*>(y), pair_row, topk_w,
+                  static_cast<const float*>(shared_y), static_cast<float*>(out), p.top_k,
+                  p.hidden_size);
+  return launch(combine_bf16, T, 256, 0, s, static_cast<const uint16_t*>(y), pair_row, topk_w,
+                static_cast<const uint16_t*>(shared_y), static_cast<uint16_t*>(out), p.top_k,
+                p.hidden_size);
 }
 
 }  // namespace moe

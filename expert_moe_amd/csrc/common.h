@@ -102,8 +102,24 @@ inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) 
 
 }  // namespace moe
 
-// Launch helpers (host side).
-#define MOE_LAUNCH_CHECK()                                  \
-  do {                                                      \
-    if (hipGetLastError() != hipSuccess) return MOE_EHIP;   \
-  } while (0)
+namespace moe {
+
+template <class T>
+struct as_is {
+  using type = T;
+};
+
+// Kernel launch that reports its own status: hipLaunchKernel returns the launch's error code
+// directly, so an error left pending by earlier, unrelated work is neither taken for this
+// launch's nor cleared. The arguments convert to the kernel's parameter types.
+template <typename... P>
+inline int launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                  typename as_is<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, s) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_EHIP;
+}
+
+}  // namespace moe

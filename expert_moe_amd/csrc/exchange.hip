@@ -93,9 +93,9 @@ int launch_ep_dispatch(const moe_params& p, int T, int ep_size, const int32_t* i
   const int E = p.num_experts;
   const int per = E / ep_size;
   const int64_t n_pairs = static_cast<int64_t>(T) * k;
-  ep_owner_rank<<<static_cast<int>((n_pairs + 255) / 256), 256, 0, s>>>(ids, n_pairs, k, E, per,
-                                                                       ws.rank_of);
-  MOE_LAUNCH_CHECK();
+  if (int rc = launch(ep_owner_rank, static_cast<int>((n_pairs + 255) / 256), 256, 0, s, ids,
+                      n_pairs, k, E, per, ws.rank_of))
+    return rc;
   // rows grouped by rank, increasing pair (= token) index inside a rank, no padding
   moe_params pr = p;
   pr.num_local_experts = ep_size;
@@ -103,11 +103,9 @@ int launch_ep_dispatch(const moe_params& p, int T, int ep_size, const int32_t* i
                         rank_meta, ws.chunk, s);
   if (rc) return rc;
   const int elt = p.dtype == MOE_F32 ? 4 : 2;
-  ep_pack<<<T, 256, 0, s>>>(send_pos, k, E, per, static_cast<const uint4*>(x),
-                            p.hidden_size * elt / 16, ids, w, send_token,
-                            static_cast<uint4*>(send_x), send_local, send_w);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  return launch(ep_pack, T, 256, 0, s, send_pos, k, E, per, static_cast<const uint4*>(x),
+                p.hidden_size * elt / 16, ids, w, send_token, static_cast<uint4*>(send_x),
+                send_local, send_w);
 }
 
 }  // namespace moe

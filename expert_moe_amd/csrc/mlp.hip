@@ -5,6 +5,7 @@
 // fused_experts in "ep_fused_moe_patch.py" _ep_forward Step 3). Kernel choice follows the
 // number of rows per tile: the 16-row streaming kernel when few tokens reach each expert
 // (weight-bandwidth bound), the 64/128-row LDS-tiled MFMA kernel otherwise.
+#include <atomic>
 #include <cmath>
 
 #include "gemm.h"
@@ -14,21 +15,22 @@ namespace moe {
 
 namespace {
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers on several host threads may
+// fill an entry at once, with the same value).
 int cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <int BM, int BNR, int WM, int WN, int MODE>
-void launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, hipStream_t s) {
+int launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, hipStream_t s) {
   a.n_tiles = n_rows_b / BNR;
   a.tail_mode = tail_mode;
   a.n_cu = cu_count();
@@ -43,10 +45,8 @@ void launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, h
     constexpr size_t kStatic = NS * kStage;
     const size_t dyn = kStatic <= kLdsCu / 2 ? kLdsCu / 2 + 1024 - kStatic : 0;
     const int grid = (a.n_cu + kXcds - 1) / kXcds * kXcds;
-    if (a.valid_map)
-      gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, true><<<grid, kThreads, dyn, s>>>(a);
-    else
-      gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, false><<<grid, kThreads, dyn, s>>>(a);
+    if (a.valid_map) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, true>, grid, kThreads, dyn, s, a);
+    return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, false>, grid, kThreads, dyn, s, a);
   } else {
     // Three stages (one workgroup per CU) where two already take more than half of the CU's
     // LDS, or where the expected tiles fill at most two rounds of the CUs, so that latency and
@@ -59,16 +59,11 @@ void launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, h
     const bool deep = kFits3 && (kBig || few);
     // sorted rows skip padding row groups; dense launches keep the branch-free loop
     if (a.valid_map) {
-      if (deep)
-        gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, true><<<grid, kThreads, 0, s>>>(a);
-      else
-        gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, true><<<grid, kThreads, 0, s>>>(a);
-    } else {
-      if (deep)
-        gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, false><<<grid, kThreads, 0, s>>>(a);
-      else
-        gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, false><<<grid, kThreads, 0, s>>>(a);
+      if (deep) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, true>, grid, kThreads, 0, s, a);
+      return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, true>, grid, kThreads, 0, s, a);
     }
+    if (deep) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, false>, grid, kThreads, 0, s, a);
+    return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, false>, grid, kThreads, 0, s, a);
   }
 }
 
@@ -82,28 +77,23 @@ template <> struct Quarter<128, 128, kStore> { static constexpr int BM2 = 64, WM
 // A tile launch; when the shape has a quarter tile, the full-size launch leaves the tail of
 // its last round (decided on the device from the row count) to a quarter-tile launch.
 template <int BM, int BNR, int WM, int WN, int MODE>
-void launch_tile(GemmArgs a, int n_rows_b, int est_blocks, hipStream_t s) {
+int launch_tile(GemmArgs a, int n_rows_b, int est_blocks, hipStream_t s) {
   using Q = Quarter<BM, BNR, MODE>;
   if constexpr (Q::BM2 == 0) {
-    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
+    return launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
   } else {
     const int n_cu = cu_count();
-    if (n_cu <= 0) {
-      launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
-      return;
-    }
+    if (n_cu <= 0) return launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
     if (a.num_padded == nullptr) {
       // dense rows: the tile count is known here, so is whether there is a tail to split
       const int total = ceil_div(a.M_rows, BM) * (n_rows_b / BNR);
       const int rem = total % n_cu;
-      if (rem == 0 || 4 * rem > n_cu) {
-        launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
-        return;
-      }
+      if (rem == 0 || 4 * rem > n_cu)
+        return launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 0, s);
     }
-    launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 1, s);
+    if (int rc = launch_tile_only<BM, BNR, WM, WN, MODE>(a, n_rows_b, est_blocks, 1, s)) return rc;
     a.m_blocks = 0;  // unused in tail mode 2
-    launch_tile_only<Q::BM2, BNR / 2, Q::WM, Q::WN, MODE>(a, n_rows_b, 4 * est_blocks, 2, s);
+    return launch_tile_only<Q::BM2, BNR / 2, Q::WM, Q::WN, MODE>(a, n_rows_b, 4 * est_blocks, 2, s);
   }
 }
 
@@ -148,40 +138,29 @@ inline int pick_bnr256(int n_rows_b, int est_blocks, bool silu, int n_cu) {
 // Wave grids: 8 waves (two per SIMD) wherever the tile splits into 8 blocks of whole MFMA
 // tiles with gate/up pairs; measured faster than 4 on the 256-row tiles.
 template <int MODE>
-void launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
-  if (bnr == 256)
-    launch_tile<256, 256, 2, 4, MODE>(a, n_rows_b, est, s);
-  else if constexpr (MODE == kStore) {
-    if (bnr == 192)
-      launch_tile<256, 192, 4, 2, MODE>(a, n_rows_b, est, s);
-    else if (bnr == 128)
-      launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, est, s);
-    else
-      launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, est, s);
-  } else if (bnr == 128)
-    launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, est, s);
-  else
-    launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, est, s);
+int launch_tile256(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
+  if (bnr == 256) return launch_tile<256, 256, 2, 4, MODE>(a, n_rows_b, est, s);
+  if constexpr (MODE == kStore) {
+    if (bnr == 192) return launch_tile<256, 192, 4, 2, MODE>(a, n_rows_b, est, s);
+  }
+  if (bnr == 128) return launch_tile<256, 128, 4, 2, MODE>(a, n_rows_b, est, s);
+  return launch_tile<256, 64, 8, 1, MODE>(a, n_rows_b, est, s);
 }
 
 template <int MODE>
-void launch_tile128(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
-  if (bnr == 256)
-    launch_tile<128, 256, 2, 4, MODE>(a, n_rows_b, est, s);
-  else if (bnr == 128)
-    launch_tile<128, 128, 4, 2, MODE>(a, n_rows_b, est, s);
-  else
-    launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, est, s);
+int launch_tile128(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
+  if (bnr == 256) return launch_tile<128, 256, 2, 4, MODE>(a, n_rows_b, est, s);
+  if (bnr == 128) return launch_tile<128, 128, 4, 2, MODE>(a, n_rows_b, est, s);
+  return launch_tile<128, 64, 4, 1, MODE>(a, n_rows_b, est, s);
 }
 
 template <int MODE>
-void launch_tile64(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
-  if (bnr == 256)
-    launch_tile<64, 256, 1, 4, MODE>(a, n_rows_b, est, s);
-  else if (bnr == 128)
-    launch_tile<64, 128, 2, 2, MODE>(a, n_rows_b, est, s);
-  else if constexpr (MODE != kSiluMul)  // 2I is always a multiple of 128
-    launch_tile<64, 64, 2, 2, MODE>(a, n_rows_b, est, s);
+int launch_tile64(const GemmArgs& a, int n_rows_b, int bnr, int est, hipStream_t s) {
+  if (bnr == 256) return launch_tile<64, 256, 1, 4, MODE>(a, n_rows_b, est, s);
+  if (bnr == 128) return launch_tile<64, 128, 2, 2, MODE>(a, n_rows_b, est, s);
+  if constexpr (MODE != kSiluMul)  // 2I is always a multiple of 128
+    return launch_tile<64, 64, 2, 2, MODE>(a, n_rows_b, est, s);
+  return MOE_EINVAL;
 }
 
 }  // namespace
@@ -255,22 +234,19 @@ int est_row_blocks(const moe_params& p, int T, bool sorted, int tr, int rows) {
 // Streaming kernel with MB 16-row blocks per workgroup; 32 weight rows per workgroup when 64
 // would leave CUs idle. m_blocks counts row blocks of 16*MB rows.
 template <int MODE, int MB>
-void launch_stream_mb(GemmArgs g, int n_rows_b, int est_blocks, hipStream_t s) {
+int launch_stream_mb(GemmArgs g, int n_rows_b, int est_blocks, hipStream_t s) {
   if (est_blocks * (n_rows_b / 64) >= 512 || n_rows_b % 32 != 0) {
     g.n_tiles = n_rows_b / 64;
-    gemm_bf16_stream<4, MODE, MB><<<tile_grid(g.m_blocks, g.n_tiles), 256, 0, s>>>(g);
-  } else {
-    g.n_tiles = n_rows_b / 32;
-    gemm_bf16_stream<2, MODE, MB><<<tile_grid(g.m_blocks, g.n_tiles), 256, 0, s>>>(g);
+    return launch(gemm_bf16_stream<4, MODE, MB>, tile_grid(g.m_blocks, g.n_tiles), 256, 0, s, g);
   }
+  g.n_tiles = n_rows_b / 32;
+  return launch(gemm_bf16_stream<2, MODE, MB>, tile_grid(g.m_blocks, g.n_tiles), 256, 0, s, g);
 }
 
 template <int MODE>
-void launch_stream(GemmArgs g, int n_rows_b, int rows_per_block, int est_blocks, hipStream_t s) {
-  if (rows_per_block == 16)
-    launch_stream_mb<MODE, 1>(g, n_rows_b, est_blocks, s);
-  else
-    launch_stream_mb<MODE, 2>(g, n_rows_b, est_blocks, s);
+int launch_stream(GemmArgs g, int n_rows_b, int rows_per_block, int est_blocks, hipStream_t s) {
+  if (rows_per_block == 16) return launch_stream_mb<MODE, 1>(g, n_rows_b, est_blocks, s);
+  return launch_stream_mb<MODE, 2>(g, n_rows_b, est_blocks, s);
 }
 
 GemmArgs base_args(const moe_params& p, int T, const int32_t* num_padded,
@@ -317,18 +293,11 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
   const int tr = pl.rows;
   g.m_blocks = ceil_div(rows, tr);
   const int est = est_row_blocks(p, T, sorted, tr, rows);
-  if (p.dtype == MOE_F32)
-    gemm_f32_tile<kSiluMul><<<g.m_blocks * (I / 32), 256, 0, s>>>(g);
-  else if (pl.stream)
-    launch_stream<kSiluMul>(g, 2 * I, tr, est, s);
-  else if (tr == 64)
-    launch_tile64<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
-  else if (tr == 128)
-    launch_tile128<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
-  else
-    launch_tile256<kSiluMul>(g, 2 * I, pick_bnr256(2 * I, est, true, cu_count()), est, s);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  if (p.dtype == MOE_F32) return launch(gemm_f32_tile<kSiluMul>, g.m_blocks * (I / 32), 256, 0, s, g);
+  if (pl.stream) return launch_stream<kSiluMul>(g, 2 * I, tr, est, s);
+  if (tr == 64) return launch_tile64<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
+  if (tr == 128) return launch_tile128<kSiluMul>(g, 2 * I, pick_bnr(2 * I, est, true), est, s);
+  return launch_tile256<kSiluMul>(g, 2 * I, pick_bnr256(2 * I, est, true, cu_count()), est, s);
 }
 
 int launch_down(const moe_params& p, int T, const void* act, const void* w2, int inter,
@@ -361,18 +330,11 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
   const int tr = pl.rows;
   g.m_blocks = ceil_div(rows, tr);
   const int est = est_row_blocks(p, T, sorted, tr, rows);
-  if (p.dtype == MOE_F32)
-    gemm_f32_tile<kStore><<<g.m_blocks * (H / 64), 256, 0, s>>>(g);
-  else if (pl.stream)
-    launch_stream<kStore>(g, H, tr, est, s);
-  else if (tr == 64)
-    launch_tile64<kStore>(g, H, pick_bnr(H, est, false), est, s);
-  else if (tr == 128)
-    launch_tile128<kStore>(g, H, pick_bnr(H, est, false), est, s);
-  else
-    launch_tile256<kStore>(g, H, pick_bnr256(H, est, false, cu_count()), est, s);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  if (p.dtype == MOE_F32) return launch(gemm_f32_tile<kStore>, g.m_blocks * (H / 64), 256, 0, s, g);
+  if (pl.stream) return launch_stream<kStore>(g, H, tr, est, s);
+  if (tr == 64) return launch_tile64<kStore>(g, H, pick_bnr(H, est, false), est, s);
+  if (tr == 128) return launch_tile128<kStore>(g, H, pick_bnr(H, est, false), est, s);
+  return launch_tile256<kStore>(g, H, pick_bnr256(H, est, false, cu_count()), est, s);
 }
 
 int device_cu_count() { return cu_count(); }

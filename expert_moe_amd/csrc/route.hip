@@ -304,11 +304,12 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
   a.c_split_stride = static_cast<int64_t>(T) * p.num_experts;
   if (p.dtype == MOE_F32) {
     a.m_blocks = ceil_div(T, 16);
-    gemm_f32_tile<kStoreF32><<<a.m_blocks * n_tiles, 256, 0, s>>>(a);
+    return launch(gemm_f32_tile<kStoreF32>, a.m_blocks * n_tiles, 256, 0, s, a);
   } else if (T <= 64) {
     a.m_blocks = ceil_div(T, 16);
     a.n_tiles = n_tiles;
-    gemm_bf16_stream<4, kStoreF32><<<dim3(tile_grid(a.m_blocks, n_tiles), a.k_splits), 256, 0, s>>>(a);
+    return launch(gemm_bf16_stream<4, kStoreF32>, dim3(tile_grid(a.m_blocks, n_tiles), a.k_splits),
+                  256, 0, s, a);
   } else {
     a.m_blocks = ceil_div(T, 64);
     a.n_tiles = n_tiles;
@@ -317,10 +318,8 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
     // latency-bound launch needs (measured: EP share 42 -> 35 us, with splits for about one
     // workgroup per CU); 64-row tiles give twice the workgroups of 128-row ones for the same
     // LDS per CU (route stage: DeepSeek-V2-shaped 39.2 -> 36.9 us, skewed T=16384 58 -> 54.5 us)
-    gemm_bf16_dma<64, 64, 2, 2, kStoreF32, 3><<<grid, 256, 0, s>>>(a);
+    return launch(gemm_bf16_dma<64, 64, 2, 2, kStoreF32, 3>, grid, 256, 0, s, a);
   }
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
 }
 
 int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
@@ -350,14 +349,9 @@ int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
   a.E_l = p.num_local_experts;
   a.rsf = p.routed_scaling_factor;
   const int blocks = ceil_div(T, 4);
-  if (a.E <= 64)
-    topk_kernel<1><<<blocks, 256, 0, s>>>(a);
-  else if (a.E <= 128)
-    topk_kernel<2><<<blocks, 256, 0, s>>>(a);
-  else
-    topk_kernel<4><<<blocks, 256, 0, s>>>(a);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  if (a.E <= 64) return launch(topk_kernel<1>, blocks, 256, 0, s, a);
+  if (a.E <= 128) return launch(topk_kernel<2>, blocks, 256, 0, s, a);
+  return launch(topk_kernel<4>, blocks, 256, 0, s, a);
 }
 
 }  // namespace moe

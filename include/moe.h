@@ -24,8 +24,9 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers, borrowed: the caller owns them, they must
  *    stay alive until the work queued on `stream` has finished. The library never
- *    allocates or frees device memory; its only state is the side stream of moe_forward
- *    (one per device, with its two events, created on first use).
+ *    allocates or frees device memory and keeps no state of its own besides its loaded code
+ *    objects (and a per-device cache of the compute-unit count): no streams, no events, no
+ *    locks. Calls from several host threads are independent.
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work
  *    on it: no host<->device synchronisation, no host reads of device data, so a call
  *    can be captured in a HIP graph.
@@ -41,6 +42,11 @@
  *    [0, E_l) or -1 when the expert lives on another rank. Its device contents are not
  *    validated (that would need a sync); slots outside [0, E_l) are treated as -1.
  *  - T = 0 is a valid no-op.
+ *  - Size limits (MOE_EUNSUPPORTED beyond them): the GEMM kernels address each operand with
+ *    32-bit byte offsets, so (T*k + E_l*256) * max(H, I, I_s) * dtype_bytes must stay below
+ *    4 GiB (for bf16 at H = 4096 and k = 2, below about 262 000 tokens; at I = 14336, about
+ *    74 000), and so must 2*I*H*dtype_bytes and 2*I_s*H*dtype_bytes (one expert's w13);
+ *    T*k + E_l*256 must stay below 2^31.
  */
 #ifndef EXPERT_MOE_AMD_MOE_H
 #define EXPERT_MOE_AMD_MOE_H
@@ -262,16 +268,11 @@ int moe_combine(const moe_params* p, int64_t num_tokens, const void* y, const in
 
 /*
  * The whole layer on this share: moe_route -> moe_align_permute -> moe_grouped_mlp
- * (-> moe_shared_mlp) -> moe_combine, with the granule of moe_pick_block_m. Ordered on
- * `stream`: it starts after the work queued there before it, and the work queued after it
- * sees its outputs. When a short shared expert is given (its gate/up projection at most four
- * rounds of 256x256 tiles), its MLP runs on a library-owned stream of the device (one per
- * device, created on the first such call, never destroyed), forked from `stream` at the call
- * and joined back before the combine, so that it overlaps the routed path; the fork and join
- * are events, so the pattern can also be captured into a HIP graph. Calls from several host
- * threads on one device are serialised while they enqueue, and their shared-expert MLPs share
- * that stream. out [T, H] = this share's partial sum; summing the outputs of all disjoint
- * shares (the shared expert passed to exactly one of them) gives the full layer.
+ * (-> moe_shared_mlp) -> moe_combine, with the granule of moe_pick_block_m, all on `stream`,
+ * in order: it starts after the work queued there before it, and the work queued after it
+ * sees its outputs (moe_forward_overlap runs the shared expert beside the routed path on a
+ * caller-owned stream). out [T, H] = this share's partial sum; summing the outputs of all
+ * disjoint shares (the shared expert passed to exactly one of them) gives the full layer.
  * A share that receives no pairs writes zeros (plus the shared expert).
  *  logit_bias, score_bias: as moe_route. b13, b2: the expert biases (NULL = none).
  *  shared_w13 / shared_w2: both NULL (no shared expert on this share) or both given
@@ -342,6 +343,41 @@ int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_toke
                      const float* b13, const float* b2, const void* shared_w13,
                      const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ overlapped shared expert */
+/*
+ * A caller-owned side stream and two caller-owned events (hipStream_t / hipEvent_t, passed as
+ * void*) for moe_forward_overlap. The stream must differ from the call's `stream`; the events
+ * need no timing. Calls that run at the same time need their own event pair each (a record /
+ * wait pair must not interleave with another call's).
+ */
+typedef struct moe_side_stream {
+  void* stream;
+  void* fork_event;
+  void* join_event;
+} moe_side_stream;
+
+/*
+ * moe_forward (eplb = NULL) or moe_forward_eplb (eplb given), with the shared expert's MLP
+ * beside the routed path: it reads only x and its own weights, so it can fill the compute units
+ * that the router, the alignment and the last rounds of the routed GEMMs leave idle
+ * ("Expert Parallel" Step 5: the shared MLP is computed on every rank beside the routed
+ * experts). When a shared expert is given and its gate/up projection is at most four rounds of
+ * 256x256 tiles, fork_event is recorded on `stream`, side->stream waits for it and runs the
+ * shared MLP, join_event is recorded there, and `stream` waits for join_event before the
+ * combine. The join is enqueued on every path that enqueued the fork, error returns included,
+ * so the pattern can be captured into a HIP graph. Otherwise (no shared expert, or a long one
+ * that fills the GPU by itself) the call is exactly moe_forward and side is not touched.
+ * side = NULL is also moe_forward. MOE_EINVAL if side->fork_event or side->join_event is NULL
+ * or side->stream equals `stream`. Arguments, workspace and errors otherwise as moe_forward.
+ */
+int moe_forward_overlap(const moe_params* p, const moe_eplb* eplb, const moe_side_stream* side,
+                        int64_t num_tokens, const void* x, const void* w_gate,
+                        const float* logit_bias, const float* score_bias,
+                        const int32_t* expert_map, const void* w13, const void* w2,
+                        const float* b13, const float* b2, const void* shared_w13,
+                        const void* shared_w2, void* out, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ expert-parallel exchange */
 /*

@@ -77,13 +77,13 @@ def test_param_errors():
         (dict(shared_intermediate_size=100), E),
         (dict(routed_scaling_factor=float("inf")), E),
         (dict(num_experts=320, num_expert_group=8), moe.MOE_EUNSUPPORTED),
-        (dict(dtype=7), moe.MOE_EUNSUPPORTED),
     ]
     for over, want in cases:
         p = _params(w, **over)
-        if over.get("dtype") == 7:
-            p.dtype = 7
         assert moe.moe_check_params(p) == want, over
+    p = _params(w)
+    p.dtype = 7  # the library's own check (the binding refuses such a dtype before it)
+    assert moe.moe_check_params(p) == moe.MOE_EUNSUPPORTED
     p = _params(w)
     p.scoring_func = 2  # neither softmax nor sigmoid
     assert moe.moe_check_params(p) == E
@@ -282,3 +282,61 @@ def test_eplb_tables_and_argument_errors():
     p2 = _params(wl.WORKLOADS["tiny"], num_local_experts=12)
     assert moe.moe_check_params(p2) == moe.MOE_OK
     assert moe.moe_workspace_size(p2, 64) > 0
+
+
+def test_make_params_dtype_names():
+    import torch
+    for d in ("bf16", "bfloat16", torch.bfloat16, moe.MOE_BF16):
+        assert moe.make_params(8, 2, 128, 256, dtype=d).dtype == moe.MOE_BF16
+    for d in ("f32", "fp32", "float32", torch.float32, moe.MOE_F32):
+        assert moe.make_params(8, 2, 128, 256, dtype=d).dtype == moe.MOE_F32
+    for d in ("fp16", torch.float16, 2, None):
+        with pytest.raises(ValueError, match="dtype"):
+            moe.make_params(8, 2, 128, 256, dtype=d)
+
+
+def test_binding_checks_tensor_dtypes_and_sizes():
+    """The binding refuses a tensor of the wrong dtype or with fewer elements than the header's
+    shape for the call, before anything reaches the library (host tensors suffice: the checks
+    come first)."""
+    import torch
+    p = _params(wl.WORKLOADS["tiny"])  # fp32, H 128, E 8, I 256, k 2
+    T, H = 4, 128
+    x32 = torch.zeros(T, H)
+    with pytest.raises(ValueError, match="x: dtype"):
+        moe.moe_forward(p, T, x32.bfloat16(), None, None, None, None, None, None, None, None,
+                        None, None, None, stream=0)
+    with pytest.raises(ValueError, match="x: .* elements"):
+        moe.moe_forward(p, T, x32[:2], None, None, None, None, None, None, None, None, None, None,
+                        None, stream=0)
+    with pytest.raises(ValueError, match="expert_map: dtype"):
+        moe.moe_route(p, T, x32, None, None, torch.zeros(8, dtype=torch.int64), None, None, None,
+                      None, stream=0)
+    with pytest.raises(ValueError, match="w13: .* elements"):
+        moe.moe_grouped_mlp(p, T, x32, torch.zeros(8, 2 * 256, H - 1), None, None, None, None, 16,
+                            None, None, stream=0)
+    with pytest.raises(ValueError, match="topk_w: dtype"):
+        moe.moe_combine(p, T, x32, None, torch.zeros(T, 2, dtype=torch.float64), None, None,
+                        stream=0)
+    with pytest.raises(ValueError, match="out: .* elements"):
+        moe.moe_combine(p, T, x32, None, None, None, torch.zeros(T, H - 1), stream=0)
+
+
+def test_forward_overlap_argument_errors():
+    """The side stream's events are required, and the side stream must differ from the call's
+    stream; those are refused before anything is enqueued (also at T = 0). Without a side
+    stream the call is moe_forward (T = 0: a no-op)."""
+    p = _params(wl.WORKLOADS["dsv2"])
+    L = moe.lib()
+    pp = ctypes.byref(p)
+    F = FAKE
+
+    def call(side, T=0, stream=None):
+        return L.moe_forward_overlap(pp, None, side, T, F, F, None, None, F, F, F, None, None, F, F,
+                                     F, None, None, F, 1 << 30, stream)
+
+    assert call(None) == 0
+    assert call(ctypes.byref(moe.moe_side_stream(F, None, F))) == -1
+    assert call(ctypes.byref(moe.moe_side_stream(F, F, None))) == -1
+    assert call(ctypes.byref(moe.moe_side_stream(F, F, F)), stream=F) == -1
+    assert call(ctypes.byref(moe.moe_side_stream(F, F, F)), stream=None) == 0

@@ -42,7 +42,7 @@ def _check(layer, rows=None):
     ref = layer.oracle_route()
     mism, near = layer.check_routing(ids, tw, ref)
     rows = np.arange(layer.T) if rows is None else rows
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows])
     err = rel_err(out[rows], want)
     print(f"[{w.key} T={layer.T}] rel_err={err:.3e} near_ties={near} exempt={mism.size}",
@@ -118,7 +118,7 @@ def test_gptoss_full_size(T):
     ref = layer.oracle_route()
     mism, near = layer.check_routing(ids, tw, ref)
     rows = np.arange(T) if T <= 256 else sample_rows(ids, layer.emap, T)
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows])
     err = rel_err(out[rows], want)
     print(f"[gptoss T={T}] rel_err={err:.3e} near_ties={near} exempt={mism.size}", flush=True)

@@ -55,7 +55,7 @@ def _full_check(layer: Layer, rows=None, with_shared=True):
     mism, near = layer.check_routing(ids, tw, ref)
     if rows is None:
         rows = np.arange(layer.T)
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows], with_shared)
     err = rel_err(out[rows], want)
     print(f"[{w.key} T={layer.T}] rel_err={err:.3e} near_ties={near} exempt_mismatch={mism.size} "
@@ -90,7 +90,7 @@ def test_forward_full_size(key, T):
     ref = layer.oracle_route()
     mism, near = layer.check_routing(ids, tw, ref)
     rows = np.arange(T) if T <= 256 else sample_rows(ids, layer.emap, T)
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows])
     err = rel_err(out[rows], want)
     print(f"[{key} T={T}] rel_err={err:.3e} near_ties={near} exempt_mismatch={mism.size} "
@@ -107,11 +107,22 @@ def test_repeated_calls_bit_identical():
         assert np.array_equal(u, v)
 
 
+def _side(dev):
+    """A side stream and a fork / join event pair, the events created (recorded once)."""
+    st = torch.cuda.Stream(device=dev)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    fork.record(st)
+    join.record(st)
+    return st, fork, join
+
+
+@pytest.mark.parametrize("overlap", [False, True], ids=["serial", "overlap"])
 @pytest.mark.parametrize("case", ["ds_s", "skew_s600"])
-def test_concurrent_callers_match_single_thread(case):
-    """Two host threads calling moe_forward at once, each on its own stream with its own
-    buffers, so that their shared-expert MLPs meet on the library's side stream: every call
-    reproduces the single-thread output and routing bit for bit."""
+def test_concurrent_callers_match_single_thread(case, overlap):
+    """Two host threads calling the layer at once, each on its own stream with its own buffers
+    (and, with moe_forward_overlap, its own side stream and event pair; the library keeps no
+    state that they could share): every call reproduces the single-thread output and routing
+    bit for bit."""
     import threading
     w, T = SMALL[case]
     layer = Layer(w, T)
@@ -127,7 +138,8 @@ def test_concurrent_callers_match_single_thread(case):
             out=torch.empty(T, w.hidden_size, dtype=d["x"].dtype, device=dev),
             ids=torch.empty(T, w.top_k, dtype=torch.int32, device=dev),
             tw=torch.empty(T, w.top_k, dtype=torch.float32, device=dev),
-            ws=torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)))
+            ws=torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev),
+            side=moe.make_side_stream(*_side(dev)) if overlap else None))
     torch.cuda.synchronize()
     results = [[] for _ in range(n_threads)]
     errors = []
@@ -136,9 +148,15 @@ def test_concurrent_callers_match_single_thread(case):
         b = bufs[i]
         try:
             for _ in range(n_calls):
-                moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"],
-                                d["sw13"], d["sw2"], b["out"], b["ids"], b["tw"], b["ws"],
-                                stream=b["st"], score_bias=d["sbias"])
+                if overlap:
+                    moe.moe_forward_overlap(p, b["side"], T, d["x"], d["gate"], d["bias"],
+                                            d["emap"], d["w13"], d["w2"], d["sw13"], d["sw2"],
+                                            b["out"], b["ids"], b["tw"], b["ws"], stream=b["st"],
+                                            score_bias=d["sbias"])
+                else:
+                    moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
+                                    d["w2"], d["sw13"], d["sw2"], b["out"], b["ids"], b["tw"],
+                                    b["ws"], stream=b["st"], score_bias=d["sbias"])
                 b["st"].synchronize()
                 results[i].append((b["out"].float().cpu().numpy(), b["ids"].cpu().numpy(),
                                    b["tw"].cpu().numpy()))
@@ -172,7 +190,7 @@ def test_share_sum_equals_all_local(case, ep):
     ref = full.oracle_route()
     out_full, ids, tw = full.forward()
     mism, _ = full.check_routing(ids, tw, ref)
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(full_w, ids, ref, mism)
     want = full.oracle_out(np.arange(T), ids_ref, w_ref)
     assert rel_err(total, want) <= OUT_TOL[w0.dtype]
     assert rel_err(total, out_full) <= OUT_TOL[w0.dtype]
@@ -241,8 +259,8 @@ def test_split_entry_points(case, block_m):
     ids_h, tw_h = ids.cpu().numpy(), tw.cpu().numpy()
     ref = layer.oracle_route()
     mism, _ = check_routing(w, ids_h, tw_h, ref, logits.cpu().numpy(), layer.x, layer.gate,
-                            layer.bias)
-    ids_ref, w_ref = reference_routing(ids_h, tw_h, ref, mism)
+                            layer.bias, label=f"split {case} block_m={block_m}")
+    ids_ref, w_ref = reference_routing(w, ids_h, ref, mism)
     want = layer.oracle_out(np.arange(T), ids_ref, w_ref)
     assert rel_err(out.float().cpu().numpy(), want) <= OUT_TOL[w.dtype]
     # y rows of a few pairs against the oracle's expert MLP
@@ -428,10 +446,12 @@ def test_sparse_last_blocks(case):
     assert err <= OUT_TOL["bf16"], err
 
 
+@pytest.mark.parametrize("overlap", [False, True], ids=["serial", "overlap"])
 @pytest.mark.parametrize("case", ["ds_s", "skew_s1", "mix_m"])
-def test_graph_replay_matches_eager(case):
-    """moe_forward captured in a HIP graph: every replay, with eager work and host syncs in
-    between, reproduces the eager output and routing bit for bit."""
+def test_graph_replay_matches_eager(case, overlap):
+    """moe_forward (or moe_forward_overlap, whose side stream forks and joins inside the capture)
+    captured in a HIP graph: every replay, with eager work and host syncs in between,
+    reproduces the eager output and routing bit for bit."""
     w, T = SMALL[case]
     layer = Layer(w, T)
     p = params(w)
@@ -442,13 +462,23 @@ def test_graph_replay_matches_eager(case):
     tw = torch.empty(T, w.top_k, dtype=torch.float32, device=dev)
     ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
 
+    side = moe.make_side_stream(*_side(dev)) if overlap else None
+
     def call():
-        moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"], d["sw13"],
-                        d["sw2"], out, ids, tw, ws, score_bias=d["sbias"])
+        if overlap:
+            moe.moe_forward_overlap(p, side, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
+                                    d["w2"], d["sw13"], d["sw2"], out, ids, tw, ws,
+                                    score_bias=d["sbias"])
+        else:
+            moe.moe_forward(p, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"], d["w2"],
+                            d["sw13"], d["sw2"], out, ids, tw, ws, score_bias=d["sbias"])
 
     call()
     torch.cuda.synchronize()
     ref = (out.clone(), ids.clone(), tw.clone())
+    if overlap:  # the overlapped layer equals the serial one
+        serial = layer.forward()
+        assert np.array_equal(out.float().cpu().numpy(), serial[0])
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         call()

@@ -51,7 +51,7 @@ def _check(layer, rows=None, with_shared=True):
     ref = layer.oracle_route()
     mism, near = layer.check_routing(ids, tw, ref)
     rows = np.arange(layer.T) if rows is None else rows
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows], with_shared)
     err = rel_err(out[rows], want)
     print(f"[{w.key} T={layer.T}] rel_err={err:.3e} near_ties={near} exempt={mism.size}",
@@ -104,7 +104,7 @@ def test_dsv3_full_size(T):
     ref = layer.oracle_route()
     mism, near = layer.check_routing(ids, tw, ref)
     rows = np.arange(T) if T <= 256 else sample_rows(ids, layer.emap, T)
-    ids_ref, w_ref = reference_routing(ids, tw, ref, mism)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
     want = layer.oracle_out(rows, ids_ref[rows], w_ref[rows])
     err = rel_err(out[rows], want)
     print(f"[dsv3 T={T}] rel_err={err:.3e} near_ties={near} exempt={mism.size} rows={len(rows)}",
