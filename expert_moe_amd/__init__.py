@@ -33,7 +33,11 @@ EXPORTS = (
     "moe_shared_mlp", "moe_combine", "moe_forward",
     "moe_ep_send_capacity", "moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_combine",
     "moe_eplb_tables", "moe_route_eplb", "moe_forward_eplb", "moe_forward_overlap",
+    "moe_forward_noalloc",
 )
+
+# bytes of the library's own workspace array behind moe_forward_noalloc
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -184,6 +188,8 @@ _SIGS = {
                        ctypes.c_int),
     "moe_forward_eplb": ([_P, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_forward_noalloc": ([_P, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp], ctypes.c_int),
     "moe_forward_overlap": ([_P, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
 }
@@ -522,3 +528,19 @@ def moe_forward_overlap(p, side, num_tokens, x, w_gate, logit_bias, expert_map, 
                                      _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
                                      _ptr(topk_ids_out), _ptr(topk_w_out), wp, wn, _stream(stream)),
            "moe_forward_overlap")
+
+
+def moe_forward_noalloc(p, num_tokens, x, w_gate, logit_bias, expert_map, w13, w2, shared_w13,
+                        shared_w2, out, topk_ids_out, topk_w_out, stream=None, score_bias=None,
+                        b13=None, b2=None):
+    """moe_forward on the library's own workspace array (no workspace argument, nothing
+    allocated); MoeError(MOE_ENOSPC) when the call needs more than MOE_NOALLOC_SCRATCH_BYTES."""
+    _check_tensors(p, _forward_checks(p, num_tokens, x, w_gate, logit_bias, score_bias, expert_map,
+                                      p.num_experts, w13, w2, b13, b2, shared_w13, shared_w2, out,
+                                      topk_ids_out, topk_w_out))
+    _check(lib().moe_forward_noalloc(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w_gate),
+                                     _ptr(logit_bias), _ptr(score_bias), _ptr(expert_map),
+                                     _ptr(w13), _ptr(w2), _ptr(b13), _ptr(b2), _ptr(shared_w13),
+                                     _ptr(shared_w2), _ptr(out), _ptr(topk_ids_out),
+                                     _ptr(topk_w_out), _stream(stream)),
+           "moe_forward_noalloc")

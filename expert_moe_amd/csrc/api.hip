@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/moe.h.
 #include <initializer_list>
 #include <math.h>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -601,3 +602,54 @@ int moe_ep_combine(const moe_params* p, int64_t num_tokens, const int32_t* send_
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation forward
+
+namespace {
+
+// moe_forward_noalloc's workspace: a file-scope device array, one copy per GPU, held until the
+// process ends. Host code never passes its name (a host-side stand-in) to a kernel: it uses the
+// device address that hipGetSymbolAddress returns, looked up once per device.
+__device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+};
+
+// The device address of this device's copy of `scratch`, or NULL when the lookup failed.
+void* scratch_address() {
+  static ScratchAddr addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchAddr& a = addr[dev];
+  std::call_once(a.once, [&a] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) a.ptr = p;
+  });
+  return a.ptr;
+}
+
+}  // namespace
+
+extern "C" int moe_forward_noalloc(const moe_params* p, int64_t num_tokens, const void* x,
+                                   const void* w_gate, const float* logit_bias,
+                                   const float* score_bias, const int32_t* expert_map,
+                                   const void* w13, const void* w2, const float* b13,
+                                   const float* b2, const void* shared_w13, const void* shared_w2,
+                                   void* out, int32_t* topk_ids_out, float* topk_w_out,
+                                   void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_tokens(*p, num_tokens))) return rc;
+  if (num_tokens == 0) return MOE_OK;
+  const size_t need = layout(*p, num_tokens, pick_block_m(*p, num_tokens)).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ENOSPC;
+  void* ws = scratch_address();
+  if (ws == nullptr) return MOE_EHIP;
+  return forward_impl(p, nullptr, nullptr, num_tokens, x, w_gate, logit_bias, score_bias,
+                      expert_map, w13, w2, b13, b2, shared_w13, shared_w2, out, topk_ids_out,
+                      topk_w_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -344,6 +344,31 @@ int moe_forward_eplb(const moe_params* p, const moe_eplb* eplb, int64_t num_toke
                      const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ no-allocation forward */
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_forward without a workspace argument. The
+ * workspace is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU the library runs on, held until the process ends; its device address is looked up
+ * once per device, on the first call there. The call allocates nothing (no hipMalloc, no
+ * allocating library routine).
+ *  Arguments, results and errors as moe_forward, except: MOE_ENOSPC when
+ *  moe_workspace_size(p, T, 0) exceeds MOE_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. every
+ *  decode-sized call, T <= 32, of the Mixtral-, DeepSeek-V2-, DeepSeek-V3- and skewed-shaped
+ *  layers, and T <= 256 on most of them); MOE_EHIP when the array's address cannot be found.
+ *  Every call on one GPU shares that GPU's array and leaves its contents behind (nothing in it
+ *  needs to start at zero): calls that overlap on one GPU (two streams, two threads, two
+ *  graphs replayed at once) race and must be ordered by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int moe_forward_noalloc(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
+                        const float* logit_bias, const float* score_bias,
+                        const int32_t* expert_map, const void* w13, const void* w2,
+                        const float* b13, const float* b2, const void* shared_w13,
+                        const void* shared_w2, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                        void* stream);
+
 /* ------------------------------------------------------------------ overlapped shared expert */
 /*
  * A caller-owned side stream and two caller-owned events (hipStream_t / hipEvent_t, passed as
