@@ -96,6 +96,12 @@ def _parse():
                          "and with R redundant replicated experts")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the sweep over every configuration point")
+    ap.add_argument("--config-steps", type=int, default=50,
+                    help="flushed hipEvent steps per configuration point (median, p10, p90)")
+    ap.add_argument("--no-slices", action="store_true",
+                    help="skip the per-share times of the expert-parallel layers")
     return ap.parse_args()
 
 
@@ -149,6 +155,16 @@ class Bench:
                                      d["emap"], d["w13"], d["w2"], d["sw13"], d["sw2"], self.out,
                                      self.ids, self.tw, self.ws, score_bias=d["sbias"],
                                      b13=d["b13"], b2=d["b2"])
+
+    def route_logits(self):
+        """moe_route alone on the step's tokens; its fp32 router logits [T, E] (host numpy), which
+        it leaves at the start of its workspace."""
+        m, d, p, T = self.moe, self.d, self.p, self.T
+        m.moe_route(p, T, d["x"], d["gate"], d["bias"], d["emap"], self.ids, self.tw, self.local,
+                    self.sws, score_bias=d["sbias"])
+        self.torch.cuda.synchronize()
+        E = self.w.num_experts
+        return self.sws[: T * E * 4].view(self.torch.float32).view(T, E).cpu().numpy()
 
     def split_step(self, ev=None):
         """The same kernels as moe_forward through the split entry points; events at stage ends."""
@@ -456,6 +472,212 @@ def run_eplb(host, w, T, extra, steps, warmup):
                     "tokens in turn on one GPU; group time = slowest rank"}
 
 
+# Every configuration point of the layer, with the roof it is graded on: prefill-shaped (large
+# token count) points on bf16 MFMA (>= 50% of peak), decode-shaped (weight-streaming) points on
+# HBM (>= 60%); the tiny fp32 layer is checked for parity only.
+CONFIG_POINTS = (
+    ("tiny", 64, None), ("mixtral", 32, "hbm"), ("mixtral", 4096, "mfma"),
+    ("ep_share", 8192, "mfma"), ("dsv2", 4096, "mfma"),
+    ("skewed", 1, "hbm"), ("skewed", 256, "hbm"), ("skewed", 16384, "mfma"),
+)
+TARGET_FRAC = {"mfma": 0.50, "hbm": 0.60}
+TIE_GAP = 1e-6
+FLUSH_BYTES = 512 << 20  # more than the 256 MB MALL
+
+
+class Flusher:
+    """Writes a 512 MB buffer, so the next step finds its weights in HBM, not in the MALL."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i)
+
+
+def event_protocol(fn, steps, flush, warm=10):
+    """hipEvent times of `steps` single steps (ms), each after a cache flush outside the timed
+    region, following `warm` untimed steps: median, p10, p90."""
+    import numpy as np
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": round(float(np.median(t)), 4), "p10_ms": round(float(np.percentile(t, 10)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4), "steps": steps, "flush_bytes": FLUSH_BYTES}
+
+
+def near_ties(w, logits, bias):
+    """Tokens whose k-th/(k+1)-th selection-score gap (or, grouped, last kept / first dropped
+    group gap) is below TIE_GAP, from the GPU's fp32 router logits (scores recomputed on the host
+    for this report only)."""
+    import numpy as np
+    import workloads as wl
+    l = logits.astype(np.float32)
+    if bias is not None:
+        l = (l + bias[None, :]).astype(np.float32)
+    if w.scoring_func == "sigmoid":
+        p = (1.0 / (1.0 + np.exp(-l.astype(np.float64)))).astype(np.float32)
+    else:
+        e = np.exp((l - l.max(axis=1, keepdims=True)).astype(np.float64))
+        p = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    sb = wl.score_bias(w)
+    s = p if sb is None else (p + sb[None, :]).astype(np.float32)
+    T, E, k = s.shape[0], s.shape[1], w.top_k
+    near = np.zeros(T, bool)
+    if w.use_grouped_topk:
+        G, keep = w.num_expert_group, w.topk_group
+        grp = s.reshape(T, G, E // G)
+        gs = grp.max(axis=2) if sb is None else np.sort(grp, axis=2)[:, :, -2:].sum(axis=2)
+        order = np.argsort(-gs, axis=1, kind="stable")
+        if keep < G:
+            srt = np.take_along_axis(gs, order, axis=1)
+            near |= (srt[:, keep - 1] - srt[:, keep]) < TIE_GAP
+        mask = np.zeros((T, G), bool)
+        np.put_along_axis(mask, order[:, :keep], True, axis=1)
+        s = np.where(np.repeat(mask, E // G, axis=1), s, -np.inf)
+        ncand = keep * (E // G)
+    else:
+        ncand = E
+    if k < ncand:
+        srt = -np.sort(-s, axis=1)
+        near |= (srt[:, k - 1] - srt[:, k]) < TIE_GAP
+    return int(near.sum())
+
+
+def target(alg, bound):
+    """Time a point may take at the graded fraction of its roof (ms), and its roof's peak."""
+    if bound == "mfma":
+        return alg["flops"] / (TARGET_FRAC["mfma"] * PEAK_BF16_TFLOPS * 1e12) * 1e3
+    return alg["bytes"] / (TARGET_FRAC["hbm"] * PEAK_HBM_GBS * 1e9) * 1e3
+
+
+def share_slices(host, w, T, base, steps, flush):
+    """Every expert-parallel share of the layer in turn on one GPU (the routing is replicated,
+    so every share sees the same tokens): each share's layer time, their sum and the slowest.
+    The named share runs on its seeded weights; the other shares' experts are drawn on the GPU
+    from the same distributions (their values do not change the time)."""
+    import math
+    import numpy as np
+    import torch
+
+    import expert_moe_amd as moe
+    ep = w.ep_size
+    E, El, H, I = w.num_experts, w.num_local_experts, w.hidden_size, w.intermediate_size
+    ms = []
+    d = base.d
+    for r in range(ep):
+        emap = torch.from_numpy(moe.moe_make_expert_map(E, ep, r)).cuda()
+        if r == w.ep_rank:
+            w13, w2 = d["w13"], d["w2"]
+        else:
+            g = torch.Generator(device="cuda").manual_seed(1000 + r)
+            w13 = (torch.randn(El, 2 * I, H, device="cuda", generator=g) / math.sqrt(H)).bfloat16()
+            w2 = (torch.randn(El, H, I, device="cuda", generator=g) / math.sqrt(I)).bfloat16()
+        # the shared expert lives on rank 0's share
+        sh = r == 0 and w.shared_intermediate_size > 0
+        p = moe.make_params(E, w.top_k, H, I, w.renormalize, w.use_grouped_topk,
+                            w.num_expert_group, w.topk_group, w.routed_scaling_factor, El,
+                            w.shared_intermediate_size if sh else 0, w.dtype, w.scoring_func,
+                            w.activation)
+        ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device="cuda")
+        side = base.side if sh else None
+
+        def call():
+            moe.moe_forward_overlap(p, side, T, d["x"], d["gate"], d["bias"], emap, w13, w2,
+                                    d["sw13"] if sh else None, d["sw2"] if sh else None, base.out,
+                                    base.ids, base.tw, ws, score_bias=d["sbias"])
+        ms.append(event_protocol(call, steps, flush, warm=5)["median_ms"])
+        del ws, w13, w2
+    return {"ep_size": ep, "share_ms": ms, "sum_ms": round(float(np.sum(ms)), 4),
+            "max_ms": round(float(np.max(ms)), 4), "graded_share": w.ep_rank,
+            "note": "each share in turn on one GPU, median of flushed hipEvent steps; the group's "
+                    "step would take the slowest share (plus the exchange between ranks)"}
+
+
+def run_configs(steps, flush, slices=True):
+    """Every configuration point: layer time (flushed hipEvent median / p10 / p90), tokens/s,
+    algorithmic FLOPs and bytes of the actual routing, the fraction of the graded roof, the
+    target time and whether it is met, near-tie tokens, per-share times of the shared layers."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    out = []
+    hosts = {}
+    for key, T, bound in CONFIG_POINTS:
+        w = wl.WORKLOADS[key]
+        print(f"[bench] config {key} T={T}", file=sys.stderr, flush=True)
+        if key not in hosts:
+            hosts.clear()
+            torch.cuda.empty_cache()
+            hosts[key] = HostLayer(w, max(w.tokens))
+        b = Bench(w, T, hosts[key])
+        warm_up(b.forward, 5)
+        prot = event_protocol(b.forward, steps, flush)
+        # back to back (no flush; weights may stay in the MALL where they fit)
+        warm_up(b.forward, 5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            b.forward()
+        e1.record()
+        torch.cuda.synchronize()
+        b2b = e0.elapsed_time(e1) / steps
+        ids = b.ids.cpu().numpy()
+        alg = algorithmic(w, T, ids)
+        nt = near_ties(w, b.route_logits(), hosts[key].bias)
+        ms = prot["median_ms"]
+        rec = {"workload": f"{w.desc}, T={T}", "key": key, "tokens": T, **prot,
+               "back_to_back_ms": round(b2b, 4),
+               "tokens_per_s": round(T / (ms * 1e-3), 1),
+               "tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
+               "gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
+               "assignments": alg["assignments"], "touched_experts": alg["touched_experts"],
+               "rows_per_expert": [alg["rows_per_expert_min"], alg["rows_per_expert_max"]],
+               "flops": alg["flops"], "bytes": alg["bytes"], "near_ties": nt}
+        if bound is None:
+            rec.update(bound=None, target_ms=None, met=None, note="parity only (fp32)")
+        else:
+            tgt = target(alg, bound)
+            frac = (alg["flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if bound == "mfma"
+                    else alg["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+            rec.update(bound=bound, frac=round(frac, 4), target_frac=TARGET_FRAC[bound],
+                       target_ms=round(tgt, 4), met=bool(ms <= tgt),
+                       met_back_to_back=bool(b2b <= tgt))
+        if slices and w.ep_size > 1:
+            rec["shares"] = share_slices(hosts[key], w, T, b, max(10, steps // 3), flush)
+        out.append(rec)
+        del b
+    hosts.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(host, w, sample):
     """The oracle, as it stands, on `sample` tokens of the workload (CPU, float64 MLPs)."""
     import numpy as np
@@ -483,10 +705,30 @@ def cpu_baseline(host, w, sample):
     oracle.moe_forward_given_routing(x, r["ids"], r["weights"], host.emap, Lazy(host.w13),
                                      Lazy(host.w2), sh[0], sh[1], w.activation, host.b13, host.b2)
     dt = time.perf_counter() - t0
-    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {sample} tokens of the same layer (routing + every local expert MLP "
-                      f"in float64), whole-step time"}
+    res = {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle", "seconds": round(dt, 2),
+           "sample": f"first {sample} tokens of the same layer (routing + every local expert MLP "
+                     f"in float64), whole-step time",
+           "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
+    # the same oracle on one core (BLAS limited to one thread), on a smaller sample
+    try:
+        from threadpoolctl import threadpool_limits
+        n1 = max(1, min(sample, 256))
+        x1 = wl.to_f32(host.x[:n1])
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            r1 = oracle.route(x1, wl.to_f32(host.gate), w.top_k, w.renormalize, w.use_grouped_topk,
+                              w.num_expert_group, w.topk_group, w.routed_scaling_factor, host.bias,
+                              w.scoring_func, host.sbias)
+            oracle.moe_forward_given_routing(x1, r1["ids"], r1["weights"], host.emap,
+                                             Lazy(host.w13), Lazy(host.w2), sh[0], sh[1],
+                                             w.activation, host.b13, host.b2)
+            d1 = time.perf_counter() - t0
+        res["single_core"] = {"value": round(n1 / d1, 3), "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {n1} tokens", "seconds": round(d1, 2)}
+    except ImportError:  # pragma: no cover
+        pass
+    return res
 
 
 def main():
@@ -520,6 +762,9 @@ def main():
     print("[bench] timing", file=sys.stderr, flush=True)
     b, ms, split_ms, stage, alg = run_point(host, w, T, args.steps, args.warmup)
     bound = "mfma" if alg["gate_up_flops"] / max(alg["gate_up_bytes"], 1) > 312 else "hbm"
+    flush = Flusher()
+    timing = event_protocol(b.forward, max(50, args.config_steps), flush)
+    n_near = near_ties(w, b.route_logits(), host.bias)
     res = {
         "metric": "MoE-layer tokens/s on 1 MI355X",
         "value": round(T / (ms * 1e-3), 1),
@@ -543,6 +788,9 @@ def main():
         "roofline": dict(roofline(alg, stage, bound), traffic=measured_traffic(w.key, T)),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "split_path_ms_per_step": round(split_ms, 4),
+        "timing": dict(timing, note="single steps timed with hipEvents after a 512 MB cache "
+                                    "flush each; ms_per_step is the back-to-back wall-clock mean"),
+        "near_ties": n_near,
         "work": alg,
     }
     if not args.no_exchange:
@@ -570,6 +818,11 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(host, w, min(args.cpu_sample, T))
+    if not args.no_configs:
+        del host
+        res["configs"] = run_configs(args.config_steps, flush, slices=not args.no_slices)
+        met = [c for c in res["configs"] if c.get("met") is not None]
+        res["configs_met"] = f"{sum(c['met'] for c in met)} of {len(met)}"
     print(json.dumps(res))
 
 
