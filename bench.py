@@ -131,7 +131,8 @@ class Bench:
         cap = moe.moe_sorted_capacity(self.p, T, self.bm)
         self.local = torch.empty(T, k, dtype=torch.int32, device=dev)
         self.sp = torch.empty(cap, dtype=torch.int32, device=dev)
-        self.be = torch.empty(cap // self.bm + 1, dtype=torch.int32, device=dev)
+        self.be = torch.empty(moe.block_expert_len(self.p, T, self.bm), dtype=torch.int32,
+                              device=dev)
         self.pr = torch.empty(T * k, dtype=torch.int32, device=dev)
         self.npad = torch.empty(1, dtype=torch.int32, device=dev)
         self.act = torch.empty(cap, w.intermediate_size, dtype=dt, device=dev)

@@ -325,6 +325,22 @@ def moe_route(p, num_tokens, x, w_gate, logit_bias, expert_map, topk_ids, topk_w
                            wp, wn, _stream(stream)), "moe_route")
 
 
+def block_expert_len(p, num_tokens: int, block_m: int) -> int:
+    """int32 entries that block_expert needs (include/moe.h): one per block_m rows of the
+    sorted capacity, or for variable row blocks (block_m = 0) the block table."""
+    cap = moe_sorted_capacity(p, num_tokens, block_m)
+    if block_m > 0:
+        return cap // block_m + 1
+    return 2 * (cap // 256 + 1 + p.num_local_experts) + 4
+
+
+def _be_len(p, num_tokens, block_m):
+    try:
+        return block_expert_len(p, num_tokens, block_m) - 1
+    except MoeError:
+        return 0  # the library reports the invalid argument itself
+
+
 def _sorted_rows(p, num_tokens, block_m):
     try:
         return moe_sorted_capacity(p, num_tokens, block_m)
@@ -337,7 +353,7 @@ def moe_align_permute(p, num_tokens, topk_local, block_m, sorted_pairs, block_ex
     cap = _sorted_rows(p, num_tokens, block_m)
     Tk = num_tokens * p.top_k
     _check_tensors(p, [("topk_local", topk_local, "i32", Tk), ("sorted_pairs", sorted_pairs, "i32", cap),
-                       ("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                       ("block_expert", block_expert, "i32", _be_len(p, num_tokens, block_m)),
                        ("pair_row", pair_row, "i32", Tk), ("num_padded", num_padded, "i32", 1)])
     wp, wn = _ws(ws)
     _check(lib().moe_align_permute(ctypes.byref(p), num_tokens, _ptr(topk_local), block_m,
@@ -350,7 +366,7 @@ def moe_grouped_mlp(p, num_tokens, x, w13, w2, sorted_pairs, block_expert, num_p
     cap = _sorted_rows(p, num_tokens, block_m)
     _check_tensors(p, [("x", x, "data", num_tokens * p.hidden_size)] + _expert_checks(p, w13, w2, b13, b2)
                    + [("sorted_pairs", sorted_pairs, "i32", cap),
-                      ("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                      ("block_expert", block_expert, "i32", _be_len(p, num_tokens, block_m)),
                       ("num_padded", num_padded, "i32", 1), ("y", y, "data", cap * p.hidden_size)])
     wp, wn = _ws(ws)
     _check(lib().moe_grouped_mlp(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(w2),
@@ -364,7 +380,7 @@ def moe_expert_gate_up(p, num_tokens, x, w13, sorted_pairs, block_expert, num_pa
     _check_tensors(p, [("x", x, "data", num_tokens * p.hidden_size)]
                    + _expert_checks(p, w13, None, b13, None)
                    + [("sorted_pairs", sorted_pairs, "i32", cap),
-                      ("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                      ("block_expert", block_expert, "i32", _be_len(p, num_tokens, block_m)),
                       ("num_padded", num_padded, "i32", 1),
                       ("act", act, "data", cap * p.intermediate_size)])
     _check(lib().moe_expert_gate_up(ctypes.byref(p), num_tokens, _ptr(x), _ptr(w13), _ptr(b13),
@@ -377,7 +393,7 @@ def moe_expert_down(p, num_tokens, act, w2, block_expert, num_padded, block_m, y
     cap = _sorted_rows(p, num_tokens, block_m)
     _check_tensors(p, [("act", act, "data", cap * p.intermediate_size)]
                    + _expert_checks(p, None, w2, None, b2)
-                   + [("block_expert", block_expert, "i32", cap // max(block_m, 1)),
+                   + [("block_expert", block_expert, "i32", _be_len(p, num_tokens, block_m)),
                       ("num_padded", num_padded, "i32", 1), ("y", y, "data", cap * p.hidden_size)])
     _check(lib().moe_expert_down(ctypes.byref(p), num_tokens, _ptr(act), _ptr(w2), _ptr(b2),
                                  _ptr(block_expert), _ptr(num_padded), block_m, _ptr(y),

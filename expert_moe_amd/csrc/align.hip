@@ -49,6 +49,49 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum, int& total) {
   return before + x - v;
 }
 
+// Padded rows and row blocks of one slot's segment of `count` pairs. bm > 0: padded to a
+// multiple of bm, one block per bm rows. bm == 0 (variable blocks): padded to a multiple of 32
+// and cut into blocks of 256 rows, where a last piece of at most 64 rows joins the block before
+// it (blocks of 32 .. 320 rows, every one a multiple of 32).
+__device__ __forceinline__ void segment(int count, int bm, int& padded, int& nblocks) {
+  if (bm > 0) {
+    padded = (count + bm - 1) / bm * bm;
+    nblocks = padded / bm;
+    return;
+  }
+  padded = (count + 31) / 32 * 32;
+  const int q = padded / 256;
+  const int r = padded - 256 * q;
+  nblocks = (q >= 1 && r <= 64) ? q : q + (r > 0 ? 1 : 0);
+}
+
+// The row-block table of the segments. bm > 0: block_expert[b] = slot of rows [b bm, (b+1) bm).
+// bm == 0: bt[0] = number of blocks nb; block b is rows [bt[2 + 2b], bt[2 + 2(b+1)]) of slot
+// bt[1 + 2b], with bt[1 + 2 nb] = -1 and bt[2 + 2 nb] = the padded total. Thread e (< E_l) holds
+// slot e's segment (offset off, padded rows, row blocks); every thread of the workgroup must
+// call it (the variable form holds a scan with barriers; wsum is 4 ints of LDS).
+__device__ void write_blocks(int32_t* __restrict__ bt, int e, int E_l, int bm, int off,
+                             int padded, int nblocks, int total, int* wsum) {
+  if (bm > 0) {
+    if (e < E_l)
+      for (int b = off / bm; b < (off + padded) / bm; ++b) bt[b] = e;
+    return;
+  }
+  __syncthreads();  // wsum may still be read by the offsets scan
+  int nb;
+  const int first = wg_exclusive_scan(e < E_l ? nblocks : 0, wsum, nb);
+  if (e < E_l)
+    for (int j = 0; j < nblocks; ++j) {
+      bt[1 + 2 * (first + j)] = e;
+      bt[2 + 2 * (first + j)] = off + 256 * j;
+    }
+  if (e == 0) {
+    bt[0] = nb;
+    bt[1 + 2 * nb] = -1;
+    bt[2 + 2 * nb] = total;
+  }
+}
+
 // Scatter of one chunk's pairs (chunk blockIdx.x): each wave marks its 64 tokens per slot in
 // an LDS mask, and a pair's position is base[slot] plus the marked tokens before it (earlier
 // waves, then earlier lanes). base holds this chunk's start per slot and mask is zeroed, both
@@ -130,8 +173,10 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
       }
     }
     counts[e] = run;
-    padded = (run + bm - 1) / bm * bm;
   }
+  int nblocks = 0;
+  segment(run, bm, padded, nblocks);
+  if (e >= E_l) padded = nblocks = 0;
   int acc;
   const int off = wg_exclusive_scan(padded, wsum, acc);
   if (e == 0) {
@@ -139,11 +184,9 @@ __global__ void __launch_bounds__(256) align_scan(int32_t* __restrict__ chunk, i
     meta[0] = acc;
     *num_padded = acc;
   }
-  if (e < E_l) {
-    offsets[e] = off;
-    if (block_expert)  // NULL: no row-block table wanted (the exchange's rank grouping)
-      for (int b = off / bm; b < (off + padded) / bm; ++b) block_expert[b] = e;
-  }
+  if (e < E_l) offsets[e] = off;
+  // NULL: no row-block table wanted (the exchange's rank grouping)
+  if (block_expert) write_blocks(block_expert, e, E_l, bm, off, padded, nblocks, acc, wsum);
 }
 
 __global__ void __launch_bounds__(256) align_scatter(const int32_t* __restrict__ tl, int T, int k,
@@ -198,7 +241,9 @@ __global__ void __launch_bounds__(256) align_scan_scatter(const int32_t* __restr
     }
     mask[0][e] = mask[1][e] = mask[2][e] = mask[3][e] = 0ull;
   }
-  const int padded = (tot + bm - 1) / bm * bm;
+  int padded = 0, nblocks = 0;
+  segment(tot, bm, padded, nblocks);
+  if (e >= E_l) padded = nblocks = 0;
   int acc;
   const int off = wg_exclusive_scan(padded, wsum, acc);
   if (e < E_l) base[e] = off + pre;
@@ -208,14 +253,13 @@ __global__ void __launch_bounds__(256) align_scan_scatter(const int32_t* __restr
     if (e < E_l) {
       counts[e] = tot;
       offsets[e] = off;
-      if (block_expert)
-        for (int b = off / bm; b < (off + padded) / bm; ++b) block_expert[b] = e;
     }
     if (e == 0) {
       offsets[E_l] = acc;
       meta[0] = acc;
       *num_padded = acc;
     }
+    if (block_expert) write_blocks(block_expert, e, E_l, bm, off, padded, nblocks, acc, wsum);
   }
   __syncthreads();
   chunk_scatter(tl, T, k, E_l, base, mask, sorted_pairs, pair_row);
@@ -257,21 +301,23 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
   int32_t* offsets = meta + 1;
   int32_t* counts = meta + 1 + (E_l + 1);
   // E_l <= 256: thread e owns slot e
-  const int padded = tid < E_l ? (hist[tid] + bm - 1) / bm * bm : 0;
-  if (tid < E_l) counts[tid] = hist[tid];
+  int padded = 0, nblocks = 0;
+  if (tid < E_l) {
+    segment(hist[tid], bm, padded, nblocks);
+    counts[tid] = hist[tid];
+  }
   int acc;
   const int off = wg_exclusive_scan(padded, wsum, acc);
   if (tid < E_l) {
     seg[tid] = off;
     offsets[tid] = off;
-    if (block_expert)
-      for (int b = off / bm; b < (off + padded) / bm; ++b) block_expert[b] = tid;
   }
   if (tid == 0) {
     offsets[E_l] = acc;
     meta[0] = acc;
     *num_padded = acc;
   }
+  if (block_expert) write_blocks(block_expert, tid, E_l, bm, off, padded, nblocks, acc, wsum);
   __syncthreads();
   if (!valid) return;
   const unsigned long long below = (1ull << lane) - 1ull;
@@ -301,7 +347,7 @@ int launch_align(const moe_params& p, int T, const int32_t* topk_local, int bloc
   const int E_l = p.num_local_experts;
   const int k = p.top_k;
   const int nchunks = align_chunks(T);
-  const int cap = T * k + E_l * (block_m - 1);
+  const int cap = T * k + E_l * ((block_m > 0 ? block_m : 32) - 1);
   if (nchunks == 1) {
     return launch(align_single, 1, 256, 0, s, topk_local, T, k, E_l, block_m, cap, meta,
                   num_padded, block_expert, sorted_pairs, pair_row);

@@ -65,7 +65,14 @@ int check_tokens(const moe_params& p, int64_t T) {
   return MOE_OK;
 }
 
-bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+// Variable row blocks (block_m = 0) have a 320 x 256 bf16 tile: H and 2I multiples of 256.
+bool var_blocks_ok(const moe_params& p) {
+  return p.dtype == MOE_BF16 && p.hidden_size % 256 == 0 && p.intermediate_size % 128 == 0;
+}
+
+bool valid_block_m(const moe_params& p, int32_t bm) {
+  return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256 || (bm == 0 && var_blocks_ok(p));
+}
 
 int pick_block_m(const moe_params& p, int64_t T) {
   // Expected rows per local expert under uniform routing: T*k/E.
@@ -74,13 +81,25 @@ int pick_block_m(const moe_params& p, int64_t T) {
   // measured on MI355X (granule sweep on every workload): past a handful of rows per expert
   // the 256-row LDS tile wins, because each expert's weights are streamed once per row block
   // (EP share 290 -> 276 us, DeepSeek-V2-shaped 747 -> 720 us, skewed T=256 329 -> 312 us
-  // against granule 128)
+  // against granule 128); variable row blocks keep that tile height without the nearly empty
+  // block of an expert whose rows run a little past a multiple of 256
   if (rows <= 12.0) return 16;
-  return 256;
+  return var_blocks_ok(p) && moe::prefer_var_blocks(p, T) ? 0 : 256;
 }
 
+// padding granule of the sorted rows
+inline int granule(int bm) { return bm > 0 ? bm : 32; }
+
 int64_t capacity(const moe_params& p, int64_t T, int bm) {
-  return T * p.top_k + static_cast<int64_t>(p.num_local_experts) * (bm - 1);
+  return T * p.top_k + static_cast<int64_t>(p.num_local_experts) * (granule(bm) - 1);
+}
+
+// int32 entries of block_expert: one per block_m rows, or the variable block table (the
+// count, (slot, first row) of at most capacity / 256 + 1 + E_l blocks, the end marker)
+int64_t block_table_len(const moe_params& p, int64_t T, int bm) {
+  const int64_t cap = capacity(p, T, bm);
+  if (bm > 0) return cap / bm + 1;
+  return 2 * (cap / 256 + 1 + p.num_local_experts) + 4;
 }
 
 // Workspace layout of moe_forward. Each split entry point uses only `scratch`-style
@@ -109,7 +128,7 @@ Layout layout(const moe_params& p, int64_t T, int bm) {
   L.topk_w = take(tk * 4);
   L.topk_local = take(tk * 4);
   L.sorted_pairs = take(cap * 4);
-  L.block_expert = take((cap / bm + 1) * 4);
+  L.block_expert = take(static_cast<size_t>(block_table_len(p, T, bm)) * 4);
   L.pair_row = take(tk * 4);
   L.num_padded = take(4);
   L.meta = take((2 * E_l + 2) * 4);
@@ -173,7 +192,7 @@ int moe_pick_block_m(const moe_params* p, int64_t num_tokens, int32_t* block_m) 
 }
 
 int64_t moe_sorted_capacity(const moe_params* p, int64_t num_tokens, int32_t block_m) {
-  if (check_params(p) || num_tokens < 0 || !valid_block_m(block_m)) return -1;
+  if (check_params(p) || num_tokens < 0 || !valid_block_m(*p, block_m)) return -1;
   return capacity(*p, num_tokens, block_m);
 }
 
@@ -182,9 +201,15 @@ int moe_workspace_size(const moe_params* p, int64_t num_tokens, int32_t block_m,
   if (rc) return rc;
   if (!bytes) return MOE_EINVAL;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
-  const int bm = block_m == 0 ? pick_block_m(*p, num_tokens) : block_m;
-  if (!valid_block_m(bm)) return MOE_EINVAL;
-  *bytes = layout(*p, num_tokens, bm).total;
+  if (!valid_block_m(*p, block_m) && block_m != 0) return MOE_EINVAL;
+  // 0: enough for moe_forward (its own granule) and for the split entry points with variable
+  // row blocks where the shapes allow them
+  size_t need = layout(*p, num_tokens, block_m == 0 ? pick_block_m(*p, num_tokens) : block_m).total;
+  if (block_m == 0 && var_blocks_ok(*p)) {
+    const size_t v = layout(*p, num_tokens, 0).total;
+    if (v > need) need = v;
+  }
+  *bytes = need;
   return MOE_OK;
 }
 
@@ -239,7 +264,7 @@ int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* to
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
-  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (!valid_block_m(*p, block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!topk_local || !sorted_pairs || !block_expert || !pair_row || !num_padded || !ws)
     return MOE_EINVAL;
@@ -260,7 +285,7 @@ int moe_grouped_mlp(const moe_params* p, int64_t num_tokens, const void* x, cons
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
-  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (!valid_block_m(*p, block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w13 || !w2 || !sorted_pairs || !block_expert || !num_padded || !y || !ws)
     return MOE_EINVAL;
@@ -279,7 +304,7 @@ int moe_expert_gate_up(const moe_params* p, int64_t num_tokens, const void* x, c
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
-  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (!valid_block_m(*p, block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!x || !w13 || !sorted_pairs || !block_expert || !num_padded || !act) return MOE_EINVAL;
   if (!aligned16({x, w13, b13, act})) return MOE_EINVAL;
@@ -295,7 +320,7 @@ int moe_expert_down(const moe_params* p, int64_t num_tokens, const void* act, co
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_tokens(*p, num_tokens))) return rc;
-  if (!valid_block_m(block_m)) return MOE_EINVAL;
+  if (!valid_block_m(*p, block_m)) return MOE_EINVAL;
   if (num_tokens == 0) return MOE_OK;
   if (!act || !w2 || !block_expert || !num_padded || !y) return MOE_EINVAL;
   if (!aligned16({act, w2, b2, y})) return MOE_EINVAL;

@@ -28,7 +28,9 @@ struct GemmArgs {
   int32_t M_rows;              // rows of the output buffer (stores past it are dropped);
                                // identity rows past it read the last row
   const int32_t* num_padded;   // device count of rows in use, or NULL (= M_rows)
-  const int32_t* block_expert; // sorted rows: slot of each block of block_m rows (NULL = slot 0)
+  const int32_t* block_expert; // sorted rows: slot of each block of block_m rows (NULL = slot 0);
+                               // variable row blocks: the block table (count, then slot and
+                               // first row of each block, then -1 and the padded total)
   const int32_t* valid_map;    // LDS tile with SKIP: the sorted pair list, whose -1 entries mark
                                // padding rows (padding ends each expert's segment)
   const int32_t* store_map;    // LDS tile, bf16 out: rows whose entry is < 0 (padding of the
@@ -547,6 +549,296 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
           *reinterpret_cast<uint4*>(C + j * 32) = uint4{p[0][0], p[0][1], p[1][0], p[1][1]};
           *reinterpret_cast<uint4*>(C + j * 32 + 16) = uint4{p[2][0], p[2][1], p[3][0], p[3][1]};
         }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Variable row blocks: one block of the block table per tile row range (32 .. 320 rows, a
+// multiple of 32, inside one expert's segment: 256-row blocks, where an expert's last piece of
+// at most 64 rows joins the block before it instead of taking a nearly empty tile of its own).
+// 320 x 256 tile, 8 waves (2 x 4, 160 x 64 each, two per SIMD), K step 64, two LDS stages fed
+// by global->LDS loads, as gemm_bf16_dma. Each wave runs the K loop compiled for the number of
+// its five 32-row MFMA blocks that hold rows of the block (no MFMA or fragment read for the
+// others); the A loads of rows past the block are not issued (the waits are all vmcnt(0)).
+// Register budget (two waves per SIMD): the A fragments are single-buffered, each read for the
+// next K slice right after its row block's last MFMA of this slice; the B fragments alternate
+// between two sets.
+// ----------------------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
+  constexpr int BM = 320, BNR = 256, WM = 2, WN = 4, NW = 8;
+  constexpr int BK = 64, ROWB = 128;
+  constexpr int TM = BM / WM, TMB = TM / 32;        // 160 rows, 5 MFMA row blocks per wave
+  constexpr int TNR = BNR / WN, TNB = TNR / 32;     // 64 weight rows, 2 MFMA column blocks
+  constexpr int NA = BM / (8 * NW), NB = BNR / (8 * NW), ND = NA + NB;
+  static_assert(MODE != kStoreF32, "bf16 outputs");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[2][BNR * ROWB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* bt = a.block_expert;
+  const int nblk = bt[0];
+  int L, mb, nt;
+  if (!xcd_tile(static_cast<int>(blockIdx.x), nblk * a.n_tiles, L)) return;
+  tile_coords(L, nblk, a.n_tiles, mb, nt);
+  const int slot = bt[1 + 2 * mb];
+  const int m0 = bt[2 + 2 * mb];
+  const int vrows = min(BM, bt[4 + 2 * mb] - m0);
+  const char* const Abase = static_cast<const char*>(a.A);
+  const char* const Bbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.B) + slot * a.b_stride);
+  const int K = a.K;
+
+  // load sources, as gemm_bf16_dma (rows past the block read its last row)
+  const int lrow = lane >> 3;
+  uint32_t goff[ND];
+  {
+    int rows[NA], src[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) rows[j] = m0 + min(8 * (wave + NW * j) + lrow, vrows - 1);
+    gemm_src_rows(a, rows, src);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int blk = wave + NW * j;
+      const int c = (lane & 7) ^ lrow ^ (blk & 1);
+      goff[j] = static_cast<uint32_t>(src[j]) * static_cast<uint32_t>(K * 2) + c * 16;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int blk = wave + NW * j;
+    const int r = 8 * blk + lrow;
+    const int c = (lane & 7) ^ lrow ^ (blk & 1);
+    const int brow = MODE == kSiluMul ? (r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2))
+                                      : nt * BNR + r;
+    goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16;
+  }
+  uint32_t lA[2], lB[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    lA[st] = lds_addr(sA[st]);
+    lB[st] = lds_addr(sB[st]);
+  }
+  // A load instructions of this wave that fill rows of the block (bit d), wave-uniform
+  uint32_t amask = 0;
+#pragma unroll
+  for (int d = 0; d < NA; ++d)
+    if (8 * (wave + NW * d) < vrows) amask |= 1u << d;
+  amask = __builtin_amdgcn_readfirstlane(amask);
+  // load instruction d of K step kt into stage st; A rows past the block are not loaded
+  auto dma = [&](int d, int kt, int st) {
+    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
+    if (d < NA) {
+      if (amask & (1u << d))
+        dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
+    } else {
+      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024));
+    }
+  };
+
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int fr = lane & 31;
+  const int sw = (fr & 7) ^ ((fr >> 3) & 1);
+  int coff[BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) coff[ks] = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+  const int arow = (wm * TM + fr) * ROWB;  // + i * 32 * ROWB for row block i
+  int brow0[TNB];
+#pragma unroll
+  for (int j = 0; j < TNB; ++j) {
+    const int r0 = MODE == kSiluMul
+                       ? (j < TNB / 2 ? wn * (TNR / 2) + j * 32 : BNR / 2 + wn * (TNR / 2) + (j - TNB / 2) * 32)
+                       : wn * TNR + j * 32;
+    brow0[j] = (r0 + fr) * ROWB;
+  }
+
+  f32x16 acc[TMB][TNB];
+#pragma unroll
+  for (int i = 0; i < TMB; ++i)
+#pragma unroll
+    for (int j = 0; j < TNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / BK;
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+
+  auto kloop = [&](auto nact_c) {
+    constexpr int NACT = decltype(nact_c)::value;
+    constexpr int NM = NACT * TNB;
+    bf16x8 fa[TMB], fb[2][TNB];
+    auto readA = [&](const uint8_t* pA, int ks, int i) {
+      fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(pA + arow + i * 32 * ROWB + coff[ks]));
+    };
+    auto readB = [&](const uint8_t* pB, int ks, int set) {
+#pragma unroll
+      for (int j = 0; j < TNB; ++j)
+        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(pB + brow0[j] + coff[ks]));
+    };
+    // MFMAs of one K slice on B set `set`. NEXT: after row block i's MFMAs, A fragment i of the
+    // next slice (pA, ks) is read. DMA: the loads of K step kt_dma into stage dst, spread over
+    // the MFMAs.
+    auto slice = [&](int set, auto next_c, const uint8_t* pA, int ks, auto dma_c, int kt_dma, int dst) {
+      constexpr bool NEXT = decltype(next_c)::value != 0;
+      constexpr bool DMA = decltype(dma_c)::value != 0;
+      if constexpr (DMA && NM == 0) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dma(d, kt_dma, dst);
+      }
+#pragma unroll
+      for (int i = 0; i < NACT; ++i) {
+#pragma unroll
+        for (int j = 0; j < TNB; ++j) {
+          const int m = i * TNB + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[i], acc[i][j], 0, 0, 0);
+          if constexpr (DMA) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = m * ND / (NM > 0 ? NM : 1); d < (m + 1) * ND / (NM > 0 ? NM : 1); ++d) dma(d, kt_dma, dst);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if constexpr (NEXT) readA(pA, ks, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // K step kt on stage ST. KIND 0: step kt+2 is loaded during slice 3; 1: step kt+1 is the
+    // last; 2: kt is the last step.
+    auto step = [&](auto st_c, auto kind_c, int kt) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr int KIND = decltype(kind_c)::value;
+      constexpr int NX = ST ^ 1;
+      using On = std::integral_constant<int, 1>;
+      using Off = std::integral_constant<int, 0>;
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        if (NACT > 0) readB(sB[ST], s + 1, (s + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        slice(s & 1, On{}, sA[ST], s + 1, Off{}, 0, 0);
+      }
+      if constexpr (KIND < 2) {
+        // every load of step kt+1 has landed and no wave still reads stage ST
+        __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+        __syncthreads();
+        if (NACT > 0) readB(sB[NX], 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KIND == 0)
+          slice(1, On{}, sA[NX], 0, On{}, kt + 2, ST);
+        else
+          slice(1, On{}, sA[NX], 0, Off{}, 0, 0);
+      } else {
+        slice(1, Off{}, sA[ST], 0, Off{}, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: steps 0 and 1 in flight, all landed (some A loads may be skipped), slice 0 read
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma(d, 0, 0);
+    if (nk > 1) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) dma(d, 1, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (NACT > 0) readB(sB[0], 0, 0);
+#pragma unroll
+    for (int i = 0; i < NACT; ++i) readA(sA[0], 0, i);
+    if (nk == 1) {
+      step(C0{}, C2{}, 0);
+    } else if ((nk & 1) == 0) {
+      for (int kt = 0; kt < nk - 2; kt += 2) {
+        step(C0{}, C0{}, kt);
+        step(C1{}, C0{}, kt + 1);
+      }
+      step(C0{}, C1{}, nk - 2);
+      step(C1{}, C2{}, nk - 1);
+    } else {
+      for (int kt = 0; kt < nk - 3; kt += 2) {
+        step(C0{}, C0{}, kt);
+        step(C1{}, C0{}, kt + 1);
+      }
+      step(C0{}, C0{}, nk - 3);
+      step(C1{}, C1{}, nk - 2);
+      step(C0{}, C2{}, nk - 1);
+    }
+  };
+  // this wave's MFMA row blocks that hold rows of the block
+  const int na = __builtin_amdgcn_readfirstlane(min(TMB, max(0, (vrows - wm * TM + 31) / 32)));
+  switch (na) {
+    case 0: kloop(std::integral_constant<int, 0>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    default: kloop(std::integral_constant<int, 5>{}); break;
+  }
+
+  // epilogue, as gemm_bf16_dma; rows past the block are not stored
+  const int orow = m0 + wm * TM + fr;
+  constexpr int OUTB = MODE == kSiluMul ? TNB / 2 : TNB;
+  const int col0 = (MODE == kSiluMul ? nt * (BNR / 2) + wn * (TNR / 2) : nt * BNR + wn * TNR) + 8 * (lane >> 5);
+  const int colb = col0 - 8 * (lane >> 5) + 4 * (lane >> 5);
+  const float* const bias = a.bias ? a.bias + slot * a.bias_stride : nullptr;
+  const int act = a.act;
+  const int rend = min(m0 + vrows, a.M_rows);
+#pragma unroll
+  for (int i = 0; i < TMB; ++i) {
+    const int row = orow + i * 32;
+    const bool keep = row < rend && (!a.store_map || a.store_map[row] >= 0);
+    uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc + col0;
+#pragma unroll
+    for (int j = 0; j < OUTB; ++j) {
+      uint32_t p[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float v0, v1;
+          if constexpr (MODE == kSiluMul) {
+            float g0 = acc[i][j][4 * q + 2 * h], g1 = acc[i][j][4 * q + 2 * h + 1];
+            float u0 = acc[i][j + TNB / 2][4 * q + 2 * h], u1 = acc[i][j + TNB / 2][4 * q + 2 * h + 1];
+            if (bias) {
+              const int c = colb + 32 * j + 8 * q + 2 * h;
+              const float2 bg = *reinterpret_cast<const float2*>(bias + c);
+              const float2 bu = *reinterpret_cast<const float2*>(bias + a.N + c);
+              g0 += bg.x;
+              g1 += bg.y;
+              u0 += bu.x;
+              u1 += bu.y;
+            }
+            v0 = act_mul(g0, u0, act);
+            v1 = act_mul(g1, u1, act);
+          } else {
+            v0 = acc[i][j][4 * q + 2 * h];
+            v1 = acc[i][j][4 * q + 2 * h + 1];
+            if (bias) {
+              const float2 b = *reinterpret_cast<const float2*>(bias + colb + 32 * j + 8 * q + 2 * h);
+              v0 += b.x;
+              v1 += b.y;
+            }
+          }
+          p[q][h] = pack_bf16x2(v0, v1);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto s01 = __builtin_amdgcn_permlane32_swap(p[0][h], p[1][h], false, false);
+        const auto s23 = __builtin_amdgcn_permlane32_swap(p[2][h], p[3][h], false, false);
+        p[0][h] = s01[0];
+        p[1][h] = s01[1];
+        p[2][h] = s23[0];
+        p[3][h] = s23[1];
+      }
+      if (keep) {
+        *reinterpret_cast<uint4*>(C + j * 32) = uint4{p[0][0], p[0][1], p[1][0], p[1][1]};
+        *reinterpret_cast<uint4*>(C + j * 32 + 16) = uint4{p[2][0], p[2][1], p[3][0], p[3][1]};
       }
     }
   }

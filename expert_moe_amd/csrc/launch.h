@@ -69,6 +69,10 @@ int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const
 // Compute units of the current device (cached per device); 0 if the query fails.
 int device_cu_count();
 
+// Whether variable row blocks are expected to beat the 256-row granule for T tokens (fewer
+// row blocks, and at least a round of gate/up tiles).
+bool prefer_var_blocks(const moe_params& p, int64_t T);
+
 // Scratch of the exchange dispatch: the owning rank of every pair [T*k], the rank-sorted pair
 // list [T*k], the alignment's chunk counts.
 struct EpScratch {

@@ -141,20 +141,32 @@ int moe_check_params(const moe_params* p);
 
 /*
  * The per-expert padding granule moe_forward uses for T tokens: the M-tile of the grouped
- * GEMM that fits the expected rows per local expert. Writes *block_m (16, 32, 64, 128 or 256).
+ * GEMM that fits the expected rows per local expert. Writes *block_m: 16, 32, 64, 128, 256, or
+ * 0 for variable row blocks.
+ *
+ * Variable row blocks (block_m = 0; bf16 layers with H and 2I multiples of 256, else
+ * MOE_EINVAL where a granule is passed): each local expert's segment of sorted rows is padded
+ * to a multiple of 32 and cut into blocks of 256 rows, except that a last piece of at most 64
+ * rows stays in the block before it, so a block has 32 to 320 rows (an expert with 1033 rows
+ * takes four blocks, not four and a nearly empty fifth). block_expert then holds the block
+ * table: [nb, slot_0, row_0, slot_1, row_1, ..., slot_{nb-1}, row_{nb-1}, -1, num_padded],
+ * block b covering sorted rows [row_b, row_{b+1}) of slot slot_b; it needs
+ * 2 * (moe_sorted_capacity / 256 + 1 + E_l) + 4 int32.
  */
 int moe_pick_block_m(const moe_params* p, int64_t num_tokens, int32_t* block_m);
 
 /*
  * Rows of the expert-sorted buffers (sorted_pairs, y) for T tokens and granule block_m:
- * T*k + E_l*(block_m-1), the worst case over all routings (every pair local). -1 on error.
+ * T*k + E_l*(block_m-1) (T*k + E_l*31 for variable row blocks), the worst case over all
+ * routings (every pair local). -1 on error.
  */
 int64_t moe_sorted_capacity(const moe_params* p, int64_t num_tokens, int32_t block_m);
 
 /*
  * Workspace bytes that moe_forward needs for T tokens (block_m = 0: the granule
- * moe_forward picks), which is also enough for any single split entry point called with
- * the same T and block_m. Depends only on host values, so no readback is ever needed.
+ * moe_forward picks, and enough for the split entry points with variable row blocks), which is
+ * also enough for any single split entry point called with the same T and block_m. Depends
+ * only on host values, so no readback is ever needed.
  */
 int moe_workspace_size(const moe_params* p, int64_t num_tokens, int32_t block_m, size_t* bytes);
 
@@ -201,11 +213,11 @@ int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void
  * expert loop in MixtralMoE.forward / the sort before fused_experts in _ep_forward).
  *  topk_local [T, k]: slot of each pair or -1 (may come from the caller's own routing;
  *    the slots of one token must be distinct, as top-k gives them).
- *  block_m: 16, 32, 64, 128 or 256.
+ *  block_m: 16, 32, 64, 128, 256, or 0 for variable row blocks (see moe_pick_block_m).
  *  Outputs: sorted_pairs [moe_sorted_capacity] (pair ids; -1 in padding and in every
  *  entry past *num_padded), block_expert [capacity / block_m] (slot owning each
- *  block_m rows), pair_row [T*k] (row of each pair in sorted order, -1 if not local),
- *  num_padded [1] (device int32: total padded rows).
+ *  block_m rows; the block table for block_m = 0), pair_row [T*k] (row of each pair in sorted
+ *  order, -1 if not local), num_padded [1] (device int32: total padded rows).
  *  ws: device scratch, at least moe_workspace_size(p, T, block_m) bytes.
  */
 int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* topk_local,
@@ -215,7 +227,8 @@ int moe_align_permute(const moe_params* p, int64_t num_tokens, const int32_t* to
 
 /*
  * Grouped expert MLP over the sorted pairs: for each row r < *num_padded with pair
- * p = sorted_pairs[r] >= 0 and slot e = block_expert[r / block_m],
+ * p = sorted_pairs[r] >= 0 and slot e = block_expert[r / block_m] (block_m = 0: the slot of
+ * r's block in the block table),
  *   y[r] = W2_e act(W1_e x[p / k] + b1_e, W3_e x[p / k] + b3_e) + b2_e
  * (MixtralMLP of MixtralMoE; fused_experts with w13 / w2 in _ep_forward Step 3); the biases
  * b13 / b2 are optional (NULL = none), act follows p->activation.

@@ -352,6 +352,12 @@ def align_permute(topk_local, num_local_experts, block_m):
     offsets[e] = sum over e' < e of ceil(count[e'] / block_m) * block_m; unused slots of a
     segment hold -1. ``pair_row[p]`` is the position of pair p (-1 if its expert is not
     local); ``block_expert[b]`` is the slot that owns rows [b*block_m, (b+1)*block_m).
+
+    ``block_m == 0`` (variable row blocks): segments are padded to a multiple of 32 and each
+    is cut into blocks of 256 rows, except that a last piece of at most 64 rows stays in the
+    block before it (so a block has 32 to 320 rows). ``block_expert`` is then the block table:
+    the number of blocks nb, then (slot, first row) of each block in row order, then -1 and
+    num_padded, so that block b covers rows [table[2 + 2b], table[4 + 2b]).
     """
     tl = np.asarray(topk_local, np.int64).reshape(-1)
     E_l = int(num_local_experts)
@@ -359,7 +365,8 @@ def align_permute(topk_local, num_local_experts, block_m):
     order = np.argsort(tl[pairs], kind="stable")
     by_expert = pairs[order]
     counts = np.bincount(tl[pairs], minlength=E_l).astype(np.int64)
-    padded = -(-counts // block_m) * block_m
+    gran = block_m if block_m > 0 else 32
+    padded = -(-counts // gran) * gran
     offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
     starts = np.concatenate([[0], np.cumsum(counts)])
     num_padded = int(offsets[-1])
@@ -369,7 +376,15 @@ def align_permute(topk_local, num_local_experts, block_m):
         seg = by_expert[starts[e]:starts[e + 1]]
         sorted_pairs[offsets[e]:offsets[e] + counts[e]] = seg
         pair_row[seg] = offsets[e] + np.arange(counts[e])
-    block_expert = np.repeat(np.arange(E_l, dtype=np.int32), padded // block_m)
+    if block_m > 0:
+        block_expert = np.repeat(np.arange(E_l, dtype=np.int32), padded // block_m)
+    else:
+        table = []
+        for e in range(E_l):
+            q, r = divmod(int(padded[e]), 256)
+            n = q if (q >= 1 and r <= 64) else q + (1 if r > 0 else 0)
+            table += [v for j in range(n) for v in (e, int(offsets[e]) + 256 * j)]
+        block_expert = np.array([len(table) // 2] + table + [-1, num_padded], np.int32)
     return {"sorted_pairs": sorted_pairs, "block_expert": block_expert, "pair_row": pair_row,
             "num_padded": num_padded, "counts": counts.astype(np.int32),
             "offsets": offsets.astype(np.int32)}

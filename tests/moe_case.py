@@ -321,3 +321,13 @@ def sample_rows(ids, emap, T, n=512, seed=0):
             rows.add(int(hit[0]))
             rows.add(int(hit[-1]))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def slot_of_row(table, r, block_m):
+    """Slot that owns sorted row r (block_m rows per block, or the variable block table)."""
+    if block_m > 0:
+        return table[r // block_m]
+    nb = table[0]
+    starts = table[2:3 + 2 * nb:2]
+    b = int(np.searchsorted(starts, r, side="right")) - 1
+    return table[1 + 2 * b]

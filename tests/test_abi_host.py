@@ -61,8 +61,11 @@ def test_workload_params_valid(key):
     assert moe.moe_check_params(p) == moe.MOE_OK
     for T in w.tokens:
         bm = moe.moe_pick_block_m(p, T)
-        assert bm in (16, 32, 64, 128, 256)
-        assert moe.moe_sorted_capacity(p, T, bm) == T * w.top_k + w.num_local_experts * (bm - 1)
+        assert bm in (0, 16, 32, 64, 128, 256)
+        gran = bm if bm > 0 else 32
+        assert moe.moe_sorted_capacity(p, T, bm) == T * w.top_k + w.num_local_experts * (gran - 1)
+        if bm == 0:  # variable row blocks: bf16 with H and 2I multiples of 256
+            assert w.dtype == "bf16" and w.hidden_size % 256 == 0 and w.intermediate_size % 128 == 0
         assert moe.moe_workspace_size(p, T) > 0
 
 
@@ -167,7 +170,8 @@ def test_entry_point_argument_errors():
     L = moe.lib()
     pp = ctypes.byref(p)
     T = 64
-    ws = moe.moe_workspace_size(p, T)
+    # exactly what moe_forward needs (its own granule), so that one byte less is refused
+    ws = moe.moe_workspace_size(p, T, moe.moe_pick_block_m(p, T))
     F = FAKE
     # missing required pointers
     assert _forward_raw(pp, T, ws, x=None) == -1
@@ -190,7 +194,7 @@ def test_entry_point_argument_errors():
     assert _forward_raw(pp, -1, ws) == -1
     # bad block_m for the split entry points
     assert L.moe_align_permute(pp, T, F, 48, F, F, F, F, F, ws, None) == -1
-    assert L.moe_grouped_mlp(pp, T, F, F, F, None, None, F, F, F, 0, F, F, ws, None) == -1
+    assert L.moe_grouped_mlp(pp, T, F, F, F, None, None, F, F, F, 48, F, F, ws, None) == -1
     assert L.moe_align_permute(pp, T, F, 16, F, F, F, F, F, 8, None) == -3
     assert L.moe_route(pp, T, F, F, None, None, F, F, F, F, F, 8, None) == -3
     # shared MLP on a share without a shared expert
@@ -262,7 +266,7 @@ def test_eplb_tables_and_argument_errors():
     L = moe.lib()
     F = FAKE
     T = 32
-    ws = moe.moe_workspace_size(p, T)
+    ws = moe.moe_workspace_size(p, T, moe.moe_pick_block_m(p, T))  # moe_forward's exact need
     good = moe.moe_eplb(264, 2, F, F)
     for e in [moe.moe_eplb(255, 2, F, F), moe.moe_eplb(4097, 2, F, F), moe.moe_eplb(264, 0, F, F),
               moe.moe_eplb(264, 265, F, F), moe.moe_eplb(264, 2, None, F),
@@ -340,3 +344,20 @@ def test_forward_overlap_argument_errors():
     assert call(ctypes.byref(moe.moe_side_stream(F, F, None))) == -1
     assert call(ctypes.byref(moe.moe_side_stream(F, F, F)), stream=F) == -1
     assert call(ctypes.byref(moe.moe_side_stream(F, F, F)), stream=None) == 0
+
+
+def test_variable_blocks_granule_rules():
+    """Granule 0 (variable row blocks) is valid only for bf16 layers with H and 2I multiples of
+    256; the workspace of granule 0 covers both moe_forward and the variable split path."""
+    ok = _params(wl.WORKLOADS["mixtral"])
+    assert moe.moe_sorted_capacity(ok, 100, 0) == 100 * 2 + 8 * 31
+    assert moe.block_expert_len(ok, 100, 0) == 2 * ((200 + 248) // 256 + 1 + 8) + 4
+    assert moe.moe_workspace_size(ok, 100, 0) >= moe.moe_workspace_size(ok, 100, 16)
+    for key in ("tiny", "gptoss"):  # fp32; H = 2880
+        p = _params(wl.WORKLOADS[key])
+        with pytest.raises(moe.MoeError):
+            moe.moe_sorted_capacity(p, 100, 0)
+        assert moe.moe_pick_block_m(p, 4096) != 0
+        F = FAKE
+        assert moe.lib().moe_align_permute(ctypes.byref(p), 100, F, 0, F, F, F, F, F, 1 << 20,
+                                           None) == moe.MOE_EINVAL

@@ -185,7 +185,7 @@ def test_ep_exchange_around_shares(case, ep):
         ws = torch.empty(moe.moe_workspace_size(p, n, bm), dtype=torch.uint8, device=dev)
         cap = moe.moe_sorted_capacity(p, n, bm)
         sp = torch.empty(cap, dtype=torch.int32, device=dev)
-        be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+        be = torch.empty(moe.block_expert_len(p, n, bm), dtype=torch.int32, device=dev)
         pr = torch.empty(n * k, dtype=torch.int32, device=dev)
         npad = torch.empty(1, dtype=torch.int32, device=dev)
         xs = got["send_x"][lo:lo + n]

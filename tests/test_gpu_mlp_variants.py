@@ -10,7 +10,7 @@ import torch
 import expert_moe_amd as moe
 import oracle
 import workloads as wl
-from moe_case import OUT_TOL, Layer, params, reference_routing, rel_err, sample_rows
+from moe_case import OUT_TOL, Layer, params, reference_routing, rel_err, sample_rows, slot_of_row
 
 pytestmark = pytest.mark.gpu
 
@@ -63,11 +63,12 @@ def test_mlp_variant_decode_sizes(T):
     _check(Layer(w, T))
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("block_m", [0, 16, 32, 64, 128, 256])
 def test_mlp_variant_split_entry_points(block_m):
-    """align -> gate/up (bias, clamped SwiGLU) -> down (bias) -> combine at every granule: each
-    stage's rows against the oracle's expert MLP."""
+    """align -> gate/up (bias, clamped SwiGLU) -> down (bias) -> combine at every granule (0:
+    variable row blocks): each stage's rows against the oracle's expert MLP."""
     w, T = CASES["oai_bias"]
+    assert w.hidden_size % 256 == 0 and w.intermediate_size % 128 == 0
     layer = Layer(w, T)
     p = params(w)
     d = layer.d
@@ -78,7 +79,7 @@ def test_mlp_variant_split_entry_points(block_m):
     ws = torch.empty(moe.moe_workspace_size(p, T, block_m), dtype=torch.uint8, device=dev)
     cap = moe.moe_sorted_capacity(p, T, block_m)
     sp = torch.empty(cap, dtype=torch.int32, device=dev)
-    be = torch.empty(cap // block_m + 1, dtype=torch.int32, device=dev)
+    be = torch.empty(moe.block_expert_len(p, T, block_m), dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, local, block_m, sp, be, pr, npad, ws)
@@ -100,7 +101,7 @@ def test_mlp_variant_split_entry_points(block_m):
     y_h = y.float().cpu().numpy()
     for r in [r for r in range(n) if a["sorted_pairs"][r] >= 0][:: max(1, n // 24)]:
         pid = a["sorted_pairs"][r]
-        s = a["block_expert"][r // block_m]
+        s = slot_of_row(a["block_expert"], r, block_m)
         want = oracle.gated_mlp(wl.to_f32(layer.x[pid // k])[None], wl.to_f32(layer.w13[s]),
                                 wl.to_f32(layer.w2[s]), "swigluoai", layer.b13[s], layer.b2[s])[0]
         assert rel_err(y_h[r], want) <= 2 * OUT_TOL[w.dtype]

@@ -13,7 +13,7 @@ import expert_moe_amd as moe
 import oracle
 import workloads as wl
 from moe_case import (OUT_TOL, Layer, check_routing, dev_tensor, params, reference_routing,
-                      rel_err, sample_rows)
+                      rel_err, sample_rows, slot_of_row)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,41 @@ def _full_check(layer: Layer, rows=None, with_shared=True):
 def test_forward_small(case):
     w, T = SMALL[case]
     _full_check(Layer(w, T))
+
+
+# moe_forward on variable row blocks (experts of ~300 rows: one block of 288 or 320 rows each
+# where the 256 granule needs two) with a shared expert beside them, serial and overlapped
+VAR_SHARED = W("var_sh", 18, "variable row blocks with a shared expert", "bf16", (1200,), 256, 8,
+               4096, 2, True, shared_intermediate_size=512)
+
+
+@pytest.mark.parametrize("overlap", [False, True], ids=["serial", "overlap"])
+def test_forward_variable_blocks_with_shared(overlap):
+    w, T = VAR_SHARED, 1200
+    p = params(w)
+    assert moe.moe_pick_block_m(p, T) == 0, "this layer should take variable row blocks"
+    layer = Layer(w, T)
+    out, ids, tw = layer.forward()
+    if overlap:
+        d, dev = layer.d, layer.d["x"].device
+        st = torch.cuda.Stream(device=dev)
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(st)
+        join.record(st)
+        side = moe.make_side_stream(st, fork, join)
+        o2 = torch.empty(T, w.hidden_size, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device=dev)
+        moe.moe_forward_overlap(p, side, T, d["x"], d["gate"], d["bias"], d["emap"], d["w13"],
+                                d["w2"], d["sw13"], d["sw2"], o2, None, None, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(o2.float().cpu().numpy(), out)
+    ref = layer.oracle_route()
+    mism, near = layer.check_routing(ids, tw, ref)
+    rows = sample_rows(ids, layer.emap, T)
+    ids_ref, w_ref = reference_routing(w, ids, ref, mism)
+    err = rel_err(out[rows], layer.oracle_out(rows, ids_ref[rows], w_ref[rows]))
+    print(f"[var_sh T={T}] rel_err={err:.3e} rows={len(rows)}", flush=True)
+    assert err <= OUT_TOL[w.dtype], err
 
 
 @pytest.mark.parametrize("case", ["ds_s", "ep_s"])
@@ -215,11 +250,15 @@ def test_share_without_local_pairs():
     assert rel_err(out2, want) <= OUT_TOL["bf16"]
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("case", ["ds_s", "tiny_ragged"])
+@pytest.mark.parametrize("block_m", [0, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("case", ["ds_s", "tiny_ragged", "skew_s600"])
 def test_split_entry_points(case, block_m):
-    """route -> align_permute -> grouped_mlp (-> shared_mlp) -> combine, any granule."""
+    """route -> align_permute -> grouped_mlp (-> shared_mlp) -> combine, any granule (0: the
+    variable row blocks, where the shapes allow them)."""
     w, T = SMALL[case]
+    if block_m == 0 and not (w.dtype == "bf16" and w.hidden_size % 256 == 0
+                             and w.intermediate_size % 128 == 0):
+        pytest.skip("variable row blocks need bf16, H % 256 == 0 and 2I % 256 == 0")
     layer = Layer(w, T)
     p = params(w)
     d = layer.d
@@ -235,7 +274,7 @@ def test_split_entry_points(case, block_m):
     logits = ws[: T * w.num_experts * 4].view(torch.float32).view(T, w.num_experts).clone()
     cap = moe.moe_sorted_capacity(p, T, block_m)
     sp = torch.full((cap,), 7, dtype=torch.int32, device=dev)
-    be = torch.full((cap // block_m + 1,), -5, dtype=torch.int32, device=dev)
+    be = torch.full((moe.block_expert_len(p, T, block_m),), -5, dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, local, block_m, sp, be, pr, npad, ws)
@@ -245,7 +284,8 @@ def test_split_entry_points(case, block_m):
     n = int(npad.item())
     assert n == a["num_padded"]
     assert np.array_equal(sp.cpu().numpy()[:n], a["sorted_pairs"])
-    assert np.array_equal(be.cpu().numpy()[:n // block_m], a["block_expert"])
+    nbe = len(a["block_expert"])
+    assert np.array_equal(be.cpu().numpy()[:nbe], a["block_expert"])
     assert np.array_equal(pr.cpu().numpy(), a["pair_row"])
     y = torch.empty(cap, H, dtype=d["x"].dtype, device=dev)
     moe.moe_grouped_mlp(p, T, d["x"], d["w13"], d["w2"], sp, be, npad, block_m, y, ws)
@@ -268,7 +308,7 @@ def test_split_entry_points(case, block_m):
     rows = [r for r in range(n) if a["sorted_pairs"][r] >= 0][:: max(1, n // 16)]
     for r in rows:
         pid = a["sorted_pairs"][r]
-        s = a["block_expert"][r // block_m]
+        s = slot_of_row(a["block_expert"], r, block_m)
         want_y = oracle.gated_mlp(wl.to_f32(layer.x[pid // k])[None], wl.to_f32(layer.w13[s]),
                                   wl.to_f32(layer.w2[s]))[0]
         assert rel_err(y_h[r], want_y) <= OUT_TOL[w.dtype] * 2
@@ -289,7 +329,7 @@ def test_external_routing_through_align():
     ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
     cap = moe.moe_sorted_capacity(p, T, bm)
     sp = torch.empty(cap, dtype=torch.int32, device=dev)
-    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    be = torch.empty(moe.block_expert_len(p, T, bm), dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
@@ -346,7 +386,7 @@ def test_tail_tiles(case):
     ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
     cap = moe.moe_sorted_capacity(p, T, bm)
     sp = torch.empty(cap, dtype=torch.int32, device=dev)
-    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    be = torch.empty(moe.block_expert_len(p, T, bm), dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
@@ -364,7 +404,8 @@ def test_tail_tiles(case):
 
 
 @pytest.mark.parametrize("T,E_l,block_m", [(257, 64, 256), (16384, 64, 256), (16385, 64, 128),
-                                           (16385, 8, 16), (4000, 256, 16)])
+                                           (16385, 8, 16), (4000, 256, 16), (200, 64, 0),
+                                           (16384, 64, 0), (16385, 256, 0)])
 def test_align_chunk_counts(T, E_l, block_m):
     """moe_align_permute bit for bit against the oracle on both sides of the chunk count (64
     chunks of 256 tokens) up to which each scatter workgroup scans the counts itself; seeded
@@ -373,13 +414,13 @@ def test_align_chunk_counts(T, E_l, block_m):
     rng = np.random.default_rng(T + E_l)
     local = np.stack([rng.permutation(E_l + 16)[:k] for _ in range(T)]).astype(np.int32)
     local[local >= E_l] = -1
-    w = W("align_chunks", 70, "align sizes", "bf16", (T,), 128, E_l, 128, k, True)
+    w = W("align_chunks", 70, "align sizes", "bf16", (T,), 256, E_l, 128, k, True)
     p = params(w)
     dev = torch.device("cuda:0")
     ws = torch.empty(moe.moe_workspace_size(p, T, block_m), dtype=torch.uint8, device=dev)
     cap = moe.moe_sorted_capacity(p, T, block_m)
     sp = torch.full((cap,), 7, dtype=torch.int32, device=dev)
-    be = torch.full((cap // block_m + 1,), -5, dtype=torch.int32, device=dev)
+    be = torch.full((moe.block_expert_len(p, T, block_m),), -5, dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, dev_tensor(local), block_m, sp, be, pr, npad, ws)
@@ -389,7 +430,8 @@ def test_align_chunk_counts(T, E_l, block_m):
     assert n == a["num_padded"]
     assert np.array_equal(sp.cpu().numpy()[:n], a["sorted_pairs"])
     assert np.all(sp.cpu().numpy()[n:] == -1)
-    assert np.array_equal(be.cpu().numpy()[:n // block_m], a["block_expert"])
+    nbe = len(a["block_expert"])
+    assert np.array_equal(be.cpu().numpy()[:nbe], a["block_expert"])
     assert np.array_equal(pr.cpu().numpy(), a["pair_row"])
 
 
@@ -405,12 +447,17 @@ SPARSE = {
 }
 
 
+@pytest.mark.parametrize("bm", [256, 0])
 @pytest.mark.parametrize("case", sorted(SPARSE))
-def test_sparse_last_blocks(case):
-    """Nearly empty last row blocks of the sorted gate/up: every token's output vs the oracle."""
+def test_sparse_last_blocks(case, bm):
+    """Nearly empty last row blocks of the sorted gate/up (granule 256), and the same counts as
+    variable row blocks (granule 0: blocks of 288, 320, 256 and 64 rows where the shapes allow
+    them): every token's output vs the oracle."""
     H, I, act, bstd = SPARSE[case]
+    if bm == 0 and not (H % 256 == 0 and I % 128 == 0):
+        pytest.skip("variable row blocks need H % 256 == 0 and 2I % 256 == 0")
     counts = (257, 273, 287, 288, 289, 256, 300, 40)
-    k, bm = 2, 256
+    k = 2
     E = len(counts)
     T = sum(counts) // k
     w = W(f"sparse_{case}", 60 + sorted(SPARSE).index(case), "sparse last blocks", "bf16", (T,),
@@ -426,11 +473,10 @@ def test_sparse_last_blocks(case):
     tw_h = rng.uniform(0.25, 1.0, size=(T, k)).astype(np.float32)
     local = dev_tensor(ids)
     tw = dev_tensor(tw_h)
-    assert moe.moe_pick_block_m(p, T) == bm
     ws = torch.empty(moe.moe_workspace_size(p, T, bm), dtype=torch.uint8, device=dev)
     cap = moe.moe_sorted_capacity(p, T, bm)
     sp = torch.empty(cap, dtype=torch.int32, device=dev)
-    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    be = torch.empty(moe.block_expert_len(p, T, bm), dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)
@@ -548,7 +594,7 @@ def test_decode_forward_equals_split_path(case, T):
                   score_bias=d["sbias"])
     cap = moe.moe_sorted_capacity(p, T, bm)
     sp = torch.empty(cap, dtype=torch.int32, device=dev)
-    be = torch.empty(cap // bm + 1, dtype=torch.int32, device=dev)
+    be = torch.empty(moe.block_expert_len(p, T, bm), dtype=torch.int32, device=dev)
     pr = torch.empty(T * k, dtype=torch.int32, device=dev)
     npad = torch.empty(1, dtype=torch.int32, device=dev)
     moe.moe_align_permute(p, T, local, bm, sp, be, pr, npad, ws)

@@ -675,3 +675,56 @@ def test_mlp_variants_share_sum_and_per_token_form(R):
                                                   activation="swigluoai", b13_local=b13[sl],
                                                   b2_local=b2[sl])
     assert np.allclose(total, full, rtol=1e-12, atol=1e-12)
+
+
+def test_align_variable_blocks_hand_worked():
+    """Variable row blocks (block_m = 0) on hand-worked counts: padding to 32, blocks of 256,
+    a last piece of at most 64 rows kept in the block before it."""
+    counts = [1024, 1033, 1055, 974, 0, 1, 300, 330, 256, 288, 290]
+    tl = np.concatenate([np.full(c, e) for e, c in enumerate(counts)]).astype(np.int32)
+    a = oracle.align_permute(tl.reshape(-1, 1), len(counts), 0)
+    pad = [1024, 1056, 1056, 992, 0, 32, 320, 352, 256, 288, 320]
+    assert a["num_padded"] == sum(pad)
+    # expected blocks per slot (rows): 1024 -> 4 x 256; 1056 -> 3 x 256 + 288; 992 -> 3 x 256 +
+    # 224; 32 -> 32; 320 -> 320; 352 -> 256 + 96; 256; 288; 320
+    want_rows = [[256] * 4, [256] * 3 + [288], [256] * 3 + [288], [256] * 3 + [224], [], [32],
+                 [320], [256, 96], [256], [288], [320]]
+    t = a["block_expert"]
+    nb = t[0]
+    assert nb == sum(len(r) for r in want_rows)
+    assert t[1 + 2 * nb] == -1 and t[2 + 2 * nb] == a["num_padded"]
+    got = {}
+    for b in range(nb):
+        got.setdefault(int(t[1 + 2 * b]), []).append(int(t[4 + 2 * b] - t[2 + 2 * b]))
+    for e, rows in enumerate(want_rows):
+        assert got.get(e, []) == rows, (e, got.get(e))
+
+
+def test_align_variable_blocks_invariants():
+    """Random routings: the blocks tile [0, num_padded) in order, each inside one slot's padded
+    segment, 32 .. 320 rows and a multiple of 32; the pairs are those of the fixed granules."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        E_l = int(rng.integers(1, 40))
+        T, k = int(rng.integers(1, 3000)), int(rng.integers(1, 5))
+        tl = rng.integers(-1, E_l, size=(T, k)).astype(np.int32)
+        a = oracle.align_permute(tl, E_l, 0)
+        b = oracle.align_permute(tl, E_l, 32)
+        assert np.array_equal(a["sorted_pairs"], b["sorted_pairs"])
+        assert np.array_equal(a["pair_row"], b["pair_row"])
+        t = a["block_expert"]
+        nb = int(t[0])
+        starts = [int(t[2 + 2 * i]) for i in range(nb + 1)]
+        assert starts[0] == 0 or nb == 0
+        assert starts[-1] == a["num_padded"]
+        off = a["offsets"]
+        for i in range(nb):
+            e, r0, r1 = int(t[1 + 2 * i]), starts[i], starts[i + 1]
+            assert off[e] <= r0 < r1 <= off[e + 1]
+            assert 32 <= r1 - r0 <= 320 and (r1 - r0) % 32 == 0
+        # every non-empty slot is covered by its blocks, no more blocks than 256-row pieces
+        for e in range(E_l):
+            mine = [i for i in range(nb) if t[1 + 2 * i] == e]
+            seg = off[e + 1] - off[e]
+            assert sum(starts[i + 1] - starts[i] for i in mine) == seg
+            assert len(mine) <= -(-seg // 256)
