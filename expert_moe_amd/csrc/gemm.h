@@ -75,13 +75,19 @@ constexpr int kGroupN = 4;
 // its L2. Inside a run, tiles go row-block-major within groups of kGroupN N tiles: the row
 // blocks of one expert that read the same weight tile are consecutive and run together.
 //
-// Linear tile L -> (row block, N tile).
-__device__ __forceinline__ void tile_coords(int L, int active_m, int n_tiles, int& mb, int& nt) {
-  const int ng = L / (active_m * kGroupN);
-  const int rem = L - ng * active_m * kGroupN;
-  const int width = min(kGroupN, n_tiles - ng * kGroupN);
+// N tiles per group in the variable-block kernels' tile order: eight 256-wide weight tiles
+// times an expert's row blocks stay on one XCD, so its L2 serves the weight tile to every row
+// block of the expert (measured 0.5% faster than four on the Mixtral-shaped layer, 16 is 8% slower).
+constexpr int kVarGroupN = 8;
+
+// Linear tile L -> (row block, N tile), in groups of gn N tiles.
+__device__ __forceinline__ void tile_coords(int L, int active_m, int n_tiles, int& mb, int& nt,
+                                            int gn = kGroupN) {
+  const int ng = L / (active_m * gn);
+  const int rem = L - ng * active_m * gn;
+  const int width = min(gn, n_tiles - ng * gn);
   mb = rem / width;
-  nt = ng * kGroupN + rem % width;
+  nt = ng * gn + rem % width;
 }
 
 // Workgroup bid -> linear tile of the first `count`, striped over the XCDs; false for
@@ -554,6 +560,75 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   }
 }
 
+// Epilogue of the variable-block kernels: the wave's TMB x TNB accumulator blocks (transposed
+// MFMA blocks, as gemm_bf16_dma) to bf16 rows of C, with the activation (gate/up) or the bias;
+// rows past the block (m0 + vrows) or the output are not stored.
+template <int MODE, int TMB, int TNB, int TM, int TNR, int BNR>
+__device__ __forceinline__ void var_epilogue(const GemmArgs& a, f32x16 (&acc)[TMB][TNB], int m0, int vrows,
+                                             int slot, int nt, int wm, int wn, int lane) {
+  const int fr = lane & 31;
+  const int orow = m0 + wm * TM + fr;
+  constexpr int OUTB = MODE == kSiluMul ? TNB / 2 : TNB;
+  const int col0 = (MODE == kSiluMul ? nt * (BNR / 2) + wn * (TNR / 2) : nt * BNR + wn * TNR) + 8 * (lane >> 5);
+  const int colb = col0 - 8 * (lane >> 5) + 4 * (lane >> 5);
+  const float* const bias = a.bias ? a.bias + slot * a.bias_stride : nullptr;
+  const int act = a.act;
+  const int rend = min(m0 + vrows, a.M_rows);
+#pragma unroll
+  for (int i = 0; i < TMB; ++i) {
+    const int row = orow + i * 32;
+    const bool keep = row < rend && (!a.store_map || a.store_map[row] >= 0);
+    uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc + col0;
+#pragma unroll
+    for (int j = 0; j < OUTB; ++j) {
+      uint32_t p[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float v0, v1;
+          if constexpr (MODE == kSiluMul) {
+            float g0 = acc[i][j][4 * q + 2 * h], g1 = acc[i][j][4 * q + 2 * h + 1];
+            float u0 = acc[i][j + TNB / 2][4 * q + 2 * h], u1 = acc[i][j + TNB / 2][4 * q + 2 * h + 1];
+            if (bias) {
+              const int c = colb + 32 * j + 8 * q + 2 * h;
+              const float2 bg = *reinterpret_cast<const float2*>(bias + c);
+              const float2 bu = *reinterpret_cast<const float2*>(bias + a.N + c);
+              g0 += bg.x;
+              g1 += bg.y;
+              u0 += bu.x;
+              u1 += bu.y;
+            }
+            v0 = act_mul(g0, u0, act);
+            v1 = act_mul(g1, u1, act);
+          } else {
+            v0 = acc[i][j][4 * q + 2 * h];
+            v1 = acc[i][j][4 * q + 2 * h + 1];
+            if (bias) {
+              const float2 b = *reinterpret_cast<const float2*>(bias + colb + 32 * j + 8 * q + 2 * h);
+              v0 += b.x;
+              v1 += b.y;
+            }
+          }
+          p[q][h] = pack_bf16x2(v0, v1);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto s01 = __builtin_amdgcn_permlane32_swap(p[0][h], p[1][h], false, false);
+        const auto s23 = __builtin_amdgcn_permlane32_swap(p[2][h], p[3][h], false, false);
+        p[0][h] = s01[0];
+        p[1][h] = s01[1];
+        p[2][h] = s23[0];
+        p[3][h] = s23[1];
+      }
+      if (keep) {
+        *reinterpret_cast<uint4*>(C + j * 32) = uint4{p[0][0], p[0][1], p[1][0], p[1][1]};
+        *reinterpret_cast<uint4*>(C + j * 32 + 16) = uint4{p[2][0], p[2][1], p[3][0], p[3][1]};
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------------------
 // Variable row blocks: one block of the block table per tile row range (32 .. 320 rows, a
 // multiple of 32, inside one expert's segment: 256-row blocks, where an expert's last piece of
@@ -585,7 +660,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
   const int nblk = bt[0];
   int L, mb, nt;
   if (!xcd_tile(static_cast<int>(blockIdx.x), nblk * a.n_tiles, L)) return;
-  tile_coords(L, nblk, a.n_tiles, mb, nt);
+  tile_coords(L, nblk, a.n_tiles, mb, nt, kVarGroupN);
   const int slot = bt[1 + 2 * mb];
   const int m0 = bt[2 + 2 * mb];
   const int vrows = min(BM, bt[4 + 2 * mb] - m0);
@@ -782,66 +857,217 @@ __global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
   }
 
   // epilogue, as gemm_bf16_dma; rows past the block are not stored
-  const int orow = m0 + wm * TM + fr;
-  constexpr int OUTB = MODE == kSiluMul ? TNB / 2 : TNB;
-  const int col0 = (MODE == kSiluMul ? nt * (BNR / 2) + wn * (TNR / 2) : nt * BNR + wn * TNR) + 8 * (lane >> 5);
-  const int colb = col0 - 8 * (lane >> 5) + 4 * (lane >> 5);
-  const float* const bias = a.bias ? a.bias + slot * a.bias_stride : nullptr;
-  const int act = a.act;
-  const int rend = min(m0 + vrows, a.M_rows);
+  var_epilogue<MODE, TMB, TNB, TM, TNR, BNR>(a, acc, m0, vrows, slot, nt, wm, wn, lane);
+}
+
+// ----------------------------------------------------------------------------------------
+// Variable row blocks, deep pipeline: the tile of gemm_bf16_var (320 x 256, 8 waves of
+// 160 x 64) with K step 32 and four LDS stages in a ring, so the loads run three and a half K
+// steps ahead of the MFMAs instead of one and a half: about 108 KiB in flight per CU instead
+// of 72. For launches that stream their weights from HBM (one or two row blocks per expert),
+// where a load takes longer to come back than one K step of MFMAs.
+// LDS rows are the 32 bf16 (64 bytes) of one tile row; the four 16-byte chunks of row r sit at
+// chunk ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows cover all banks. One
+// load instruction fills 16 rows (lane l: row 16 j + l / 4, position l % 4). Per wave and K
+// step: A instructions j = 0..2 for 16-row groups wave + 8 j < 20 that start inside the block,
+// B instructions j = 0, 1. A wave waits at each step boundary for its loads of the next step
+// only (vmcnt = its loads issued since), then the workgroup meets at a barrier without the
+// fence of __syncthreads (which would wait for every load in flight).
+// ----------------------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
+  constexpr int BM = 320, BNR = 256, WM = 2, WN = 4, NW = 8;
+  constexpr int BK = 32, ROWB = 64, NS = 4;
+  constexpr int TM = BM / WM, TMB = TM / 32;        // 160 rows, 5 MFMA row blocks per wave
+  constexpr int TNR = BNR / WN, TNB = TNR / 32;     // 64 weight rows, 2 MFMA column blocks
+  constexpr int AG = BM / 16, BG = BNR / 16;        // 16-row load groups: 20 and 16
+  constexpr int NA = (AG + NW - 1) / NW, NB = BG / NW, ND = NA + NB;
+  constexpr int SA = BM * ROWB, SB = BNR * ROWB;    // stage bytes
+  static_assert(MODE != kStoreF32, "bf16 outputs");
+  static_assert(BG % NW == 0, "whole B load groups per wave");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[NS * SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[NS * SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* bt = a.block_expert;
+  const int nblk = bt[0];
+  int L, mb, nt;
+  if (!xcd_tile(static_cast<int>(blockIdx.x), nblk * a.n_tiles, L)) return;
+  tile_coords(L, nblk, a.n_tiles, mb, nt, kVarGroupN);
+  const int slot = bt[1 + 2 * mb];
+  const int m0 = bt[2 + 2 * mb];
+  const int vrows = min(BM, bt[4 + 2 * mb] - m0);
+  const char* const Abase = static_cast<const char*>(a.A);
+  const char* const Bbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.B) + slot * a.b_stride);
+  const int K = a.K;
+
+  // load sources (rows past the block read its last row)
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t goff[ND];
+  {
+    int rows[NA], src[NA];
 #pragma unroll
-  for (int i = 0; i < TMB; ++i) {
-    const int row = orow + i * 32;
-    const bool keep = row < rend && (!a.store_map || a.store_map[row] >= 0);
-    uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(row) * a.ldc + col0;
+    for (int j = 0; j < NA; ++j) rows[j] = m0 + min(16 * (wave + NW * j) + lrow, vrows - 1);
+    gemm_src_rows(a, rows, src);
 #pragma unroll
-    for (int j = 0; j < OUTB; ++j) {
-      uint32_t p[4][2];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float v0, v1;
-          if constexpr (MODE == kSiluMul) {
-            float g0 = acc[i][j][4 * q + 2 * h], g1 = acc[i][j][4 * q + 2 * h + 1];
-            float u0 = acc[i][j + TNB / 2][4 * q + 2 * h], u1 = acc[i][j + TNB / 2][4 * q + 2 * h + 1];
-            if (bias) {
-              const int c = colb + 32 * j + 8 * q + 2 * h;
-              const float2 bg = *reinterpret_cast<const float2*>(bias + c);
-              const float2 bu = *reinterpret_cast<const float2*>(bias + a.N + c);
-              g0 += bg.x;
-              g1 += bg.y;
-              u0 += bu.x;
-              u1 += bu.y;
-            }
-            v0 = act_mul(g0, u0, act);
-            v1 = act_mul(g1, u1, act);
-          } else {
-            v0 = acc[i][j][4 * q + 2 * h];
-            v1 = acc[i][j][4 * q + 2 * h + 1];
-            if (bias) {
-              const float2 b = *reinterpret_cast<const float2*>(bias + colb + 32 * j + 8 * q + 2 * h);
-              v0 += b.x;
-              v1 += b.y;
-            }
-          }
-          p[q][h] = pack_bf16x2(v0, v1);
-        }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const auto s01 = __builtin_amdgcn_permlane32_swap(p[0][h], p[1][h], false, false);
-        const auto s23 = __builtin_amdgcn_permlane32_swap(p[2][h], p[3][h], false, false);
-        p[0][h] = s01[0];
-        p[1][h] = s01[1];
-        p[2][h] = s23[0];
-        p[3][h] = s23[1];
-      }
-      if (keep) {
-        *reinterpret_cast<uint4*>(C + j * 32) = uint4{p[0][0], p[0][1], p[1][0], p[1][1]};
-        *reinterpret_cast<uint4*>(C + j * 32 + 16) = uint4{p[2][0], p[2][1], p[3][0], p[3][1]};
-      }
-    }
+    for (int j = 0; j < NA; ++j) goff[j] = static_cast<uint32_t>(src[j]) * static_cast<uint32_t>(K * 2) + lchunk * 16;
   }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r = 16 * (wave + NW * j) + lrow;
+    const int brow = MODE == kSiluMul ? (r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2))
+                                      : nt * BNR + r;
+    goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + lchunk * 16;
+  }
+  const uint32_t lA0 = lds_addr(sA), lB0 = lds_addr(sB);
+  // A load instructions of this wave (bit j): the 16-row groups wave + 8 j of the 20
+  constexpr uint32_t kAmaskLo = (1u << NA) - 1, kAmaskHi = (1u << (NA - 1)) - 1;
+  const uint32_t amask = wave + NW * (NA - 1) < AG ? kAmaskLo : kAmaskHi;
+  constexpr int kMinLoads = AG / NW + NB;  // load instructions per K step of every wave, at least
+  // load instruction d of K step kt into stage st
+  auto dma = [&](int d, int kt, int st) {
+    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
+    if (d < NA) {
+      if (amask & (1u << d))
+        dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA0 + st * SA + (wave + NW * d) * 1024));
+    } else {
+      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024));
+    }
+  };
+
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int fr = lane & 31;
+  const int sw = (fr >> 2) & 3;
+  int coff[BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) coff[ks] = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+  const int arow = (wm * TM + fr) * ROWB;  // + i * 32 * ROWB for row block i
+  int brow0[TNB];
+#pragma unroll
+  for (int j = 0; j < TNB; ++j) {
+    const int r0 = MODE == kSiluMul
+                       ? (j < TNB / 2 ? wn * (TNR / 2) + j * 32 : BNR / 2 + wn * (TNR / 2) + (j - TNB / 2) * 32)
+                       : wn * TNR + j * 32;
+    brow0[j] = (r0 + fr) * ROWB;
+  }
+
+  f32x16 acc[TMB][TNB];
+#pragma unroll
+  for (int i = 0; i < TMB; ++i)
+#pragma unroll
+    for (int j = 0; j < TNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / BK;  // at least NS: K is a multiple of 128
+
+  auto kloop = [&](auto nact_c) {
+    constexpr int NACT = decltype(nact_c)::value;
+    constexpr int NM = NACT * TNB;
+    bf16x8 fa[TMB], fb[2][TNB];
+    auto readA = [&](const uint8_t* pA, int ks, int i) {
+      fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(pA + arow + i * 32 * ROWB + coff[ks]));
+    };
+    auto readB = [&](const uint8_t* pB, int ks, int set) {
+#pragma unroll
+      for (int j = 0; j < TNB; ++j)
+        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(pB + brow0[j] + coff[ks]));
+    };
+    // MFMAs of one K slice on B set `set`; NEXT: after row block i's MFMAs, A fragment i of
+    // slice ks of pA is read; DMA: the loads of K step kt_dma into stage dst go between them
+    auto slice = [&](int set, auto next_c, const uint8_t* pA, int ks, auto dma_c, int kt_dma, int dst) {
+      constexpr bool NEXT = decltype(next_c)::value != 0;
+      constexpr bool DMA = decltype(dma_c)::value != 0;
+      if constexpr (DMA && NM == 0) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dma(d, kt_dma, dst);
+      }
+#pragma unroll
+      for (int i = 0; i < NACT; ++i) {
+#pragma unroll
+        for (int j = 0; j < TNB; ++j) {
+          const int m = i * TNB + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[i], acc[i][j], 0, 0, 0);
+          if constexpr (DMA) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = m * ND / (NM > 0 ? NM : 1); d < (m + 1) * ND / (NM > 0 ? NM : 1); ++d) dma(d, kt_dma, dst);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if constexpr (NEXT) readA(pA, ks, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using On = std::integral_constant<int, 1>;
+    using Off = std::integral_constant<int, 0>;
+
+    // K step kt on stage kt % NS. KIND 0: the loads of step kt+NS go out during slice 1;
+    // 1, 2, 3: no more loads, the boundary waits for all but 2, 1, 0 steps' loads; 4: the last
+    // step (no boundary). Waits count kMinLoads loads per step: a wave with one A instruction
+    // more waits for one or two loads of a later step as well.
+    auto step = [&](auto kind_c, int kt) {
+      constexpr int KIND = decltype(kind_c)::value;
+      const int st = kt & (NS - 1);
+      const uint8_t* pA = sA + st * SA;
+      const uint8_t* pB = sB + st * SB;
+      if (NACT > 0) readB(pB, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      slice(0, On{}, pA, 1, Off{}, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (KIND < 4) {
+        // the loads of step kt+1 landed and every wave's reads of stage st are done
+        constexpr int kAhead = KIND <= 1 ? 2 : 3 - KIND;
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kAhead * kMinLoads));
+        wg_barrier();
+        const int nx = (kt + 1) & (NS - 1);
+        if (NACT > 0) readB(sB + nx * SB, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KIND == 0)
+          slice(1, On{}, sA + nx * SA, 0, On{}, kt + NS, st);
+        else
+          slice(1, On{}, sA + nx * SA, 0, Off{}, 0, 0);
+      } else {
+        slice(1, Off{}, pA, 0, Off{}, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: steps 0 .. NS-1 in flight (nk >= NS), wait for step 0, slice 0 read
+#pragma unroll
+    for (int kt = 0; kt < NS; ++kt) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) dma(d, kt, kt);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NS - 1) * kMinLoads));
+    wg_barrier();
+    if (NACT > 0) readB(sB, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NACT; ++i) readA(sA, 0, i);
+    int kt = 0;
+    for (; kt + NS < nk; ++kt) step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt);
+    step(std::integral_constant<int, 2>{}, kt + 1);
+    step(std::integral_constant<int, 3>{}, kt + 2);
+    step(std::integral_constant<int, 4>{}, kt + 3);
+  };
+  // this wave's MFMA row blocks that hold rows of the block
+  const int na = __builtin_amdgcn_readfirstlane(min(TMB, max(0, (vrows - wm * TM + 31) / 32)));
+  switch (na) {
+    case 0: kloop(std::integral_constant<int, 0>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    default: kloop(std::integral_constant<int, 5>{}); break;
+  }
+
+  var_epilogue<MODE, TMB, TNB, TM, TNR, BNR>(a, acc, m0, vrows, slot, nt, wm, wn, lane);
 }
 
 // ----------------------------------------------------------------------------------------

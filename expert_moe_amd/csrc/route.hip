@@ -117,20 +117,44 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   const bool valid = t < a.T;
   const int E = a.E;
 
-  float pv[NQ];
+  // Every load of the token goes out before the first use (addresses clamped into the
+  // arrays, values masked afterwards): the logits, the K-split partial sums four splits at a
+  // time, and the biases. Loads behind per-value guards each waited for the one before.
+  const int tc = valid ? t : a.T - 1;
+  float* row = a.logits + static_cast<int64_t>(tc) * E;
+  const int64_t stride = static_cast<int64_t>(a.T) * E;
+  int ec[NQ];
+  float pv[NQ], lb[NQ], sb[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int e = lane + 64 * q;
-    float l = -INFINITY;
-    if (valid && e < E) {
-      float* lp = a.logits + static_cast<int64_t>(t) * E + e;
-      l = lp[0];
-      const int64_t stride = static_cast<int64_t>(a.T) * E;
-      for (int sk = 1; sk < a.splits; ++sk) l += lp[sk * stride];
-      if (a.splits > 1) lp[0] = l;
-      if (a.bias) l += a.bias[e];
+    ec[q] = min(lane + 64 * q, E - 1);
+    pv[q] = row[ec[q]];
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    lb[q] = a.bias ? a.bias[ec[q]] : 0.f;
+    sb[q] = a.sbias ? a.sbias[ec[q]] : 0.f;
+  }
+  for (int s0 = 1; s0 < a.splits; s0 += 4) {
+    float v[4][NQ];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t off = static_cast<int64_t>(min(s0 + j, a.splits - 1)) * stride;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) v[j][q] = row[off + ec[q]];
     }
-    pv[q] = l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < a.splits) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) pv[q] += v[j][q];
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const bool ok = valid && lane + 64 * q < E;
+    if (ok && a.splits > 1) row[ec[q]] = pv[q];
+    pv[q] = ok ? pv[q] + lb[q] : -INFINITY;
   }
   if (a.sigmoid) {
 #pragma unroll
@@ -154,11 +178,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   // selection scores: p, plus the selection bias when there is one
   float sv[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int e = lane + 64 * q;
-    sv[q] = pv[q];
-    if (a.sbias && valid && e < E) sv[q] += a.sbias[e];
-  }
+  for (int q = 0; q < NQ; ++q) sv[q] = pv[q] + sb[q];
   uint32_t key[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) key[q] = (lane + 64 * q < E) ? order_key(sv[q]) : 0u;

@@ -72,13 +72,15 @@ def test_forward_small(case):
 
 # moe_forward on variable row blocks (experts of ~300 rows: one block of 288 or 320 rows each
 # where the 256 granule needs two) with a shared expert beside them, serial and overlapped
-VAR_SHARED = W("var_sh", 18, "variable row blocks with a shared expert", "bf16", (1200,), 256, 8,
-               4096, 2, True, shared_intermediate_size=512)
+VAR_SHARED = W("var_sh", 18, "variable row blocks with a shared expert", "bf16", (1200, 3000), 256,
+               8, 4096, 2, True, shared_intermediate_size=512)
 
 
+# 1200 tokens: 300 rows per expert, the deep-pipeline kernel; 3000: 750, the two-stage one
+@pytest.mark.parametrize("T", VAR_SHARED.tokens)
 @pytest.mark.parametrize("overlap", [False, True], ids=["serial", "overlap"])
-def test_forward_variable_blocks_with_shared(overlap):
-    w, T = VAR_SHARED, 1200
+def test_forward_variable_blocks_with_shared(overlap, T):
+    w = VAR_SHARED
     p = params(w)
     assert moe.moe_pick_block_m(p, T) == 0, "this layer should take variable row blocks"
     layer = Layer(w, T)
