@@ -102,6 +102,9 @@ def _parse():
                     help="flushed hipEvent steps per configuration point (median, p10, p90)")
     ap.add_argument("--no-slices", action="store_true",
                     help="skip the per-share times of the expert-parallel layers")
+    ap.add_argument("--weight-layout", choices=("packed", "row_major"), default="packed",
+                    help="expert weights on the device: packed once at set-up (moe_pack_weights, "
+                         "bf16 layers) or as row-major tensors")
     return ap.parse_args()
 
 
@@ -118,7 +121,7 @@ class Bench:
                                  w.renormalize, w.use_grouped_topk, w.num_expert_group,
                                  w.topk_group, w.routed_scaling_factor, w.num_local_experts,
                                  w.shared_intermediate_size, w.dtype, w.scoring_func,
-                                 w.activation)
+                                 w.activation, layout_for(w))
         self.d = host.device_tensors(T)
         dt = self.d["x"].dtype
         k, H = w.top_k, w.hidden_size
@@ -189,6 +192,15 @@ class Bench:
         rec(6)
 
 
+# Layout of the expert weights on the device: "packed" (moe_pack_weights, once at set-up like a
+# weight load; bf16 layers) or "row_major" (--weight-layout).
+WEIGHT_LAYOUT = "packed"
+
+
+def layout_for(w):
+    return "packed" if WEIGHT_LAYOUT == "packed" and w.dtype == "bf16" else "row_major"
+
+
 class HostLayer:
     """Seeded host inputs of the largest token count; device copies per token count."""
 
@@ -210,6 +222,11 @@ class HostLayer:
             self._dev = {k: _dev(getattr(self, k)) for k in
                          ("gate", "bias", "sbias", "emap", "w13", "w2", "sw13", "sw2", "b13",
                           "b2")}
+            if layout_for(self.w) == "packed":
+                import expert_moe_amd as moe
+                for k in ("w13", "w2", "sw13", "sw2"):
+                    if self._dev[k] is not None:
+                        self._dev[k] = moe.moe_pack_weights(self._dev[k])
         return self._dev
 
     def device_tensors(self, T):
@@ -592,7 +609,7 @@ def share_slices(host, w, T, base, steps, flush):
         p = moe.make_params(E, w.top_k, H, I, w.renormalize, w.use_grouped_topk,
                             w.num_expert_group, w.topk_group, w.routed_scaling_factor, El,
                             w.shared_intermediate_size if sh else 0, w.dtype, w.scoring_func,
-                            w.activation)
+                            w.activation, layout_for(w))
         ws = torch.empty(moe.moe_workspace_size(p, T), dtype=torch.uint8, device="cuda")
         side = base.side if sh else None
 
@@ -739,6 +756,8 @@ def main():
               "multi-GPU path: each expert-parallel share is benchmarked on its own GPU.",
               file=sys.stderr)
         sys.exit(2)
+    global WEIGHT_LAYOUT
+    WEIGHT_LAYOUT = args.weight_layout
     import torch
 
     import workloads as wl
@@ -783,7 +802,8 @@ def main():
         "config": {"workload": f"{w.desc}, T={T}", "tokens": T, "hidden": w.hidden_size,
                    "experts": w.num_experts, "local_experts": w.num_local_experts,
                    "intermediate": w.intermediate_size, "top_k": w.top_k,
-                   "shared_intermediate": w.shared_intermediate_size, "block_m": b.bm},
+                   "shared_intermediate": w.shared_intermediate_size, "block_m": b.bm,
+                   "weight_layout": layout_for(w)},
         "achieved_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
         "achieved_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "roofline": dict(roofline(alg, stage, bound), traffic=measured_traffic(w.key, T)),

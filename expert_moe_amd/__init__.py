@@ -24,6 +24,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_ACT_SILU, MOE_ACT_SWIGLUOAI = 0, 1
+MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -33,7 +34,7 @@ EXPORTS = (
     "moe_shared_mlp", "moe_combine", "moe_forward",
     "moe_ep_send_capacity", "moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_combine",
     "moe_eplb_tables", "moe_route_eplb", "moe_forward_eplb", "moe_forward_overlap",
-    "moe_forward_noalloc",
+    "moe_forward_noalloc", "moe_pack_weights",
 )
 
 # bytes of the library's own workspace array behind moe_forward_noalloc
@@ -63,6 +64,7 @@ class moe_params(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scoring_func", ctypes.c_int32),
         ("activation", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -115,7 +117,8 @@ def make_eplb(num_physical_experts, max_replicas, logical_to_physical, replica_c
 def make_params(num_experts, top_k, hidden_size, intermediate_size, renormalize=True,
                 use_grouped_topk=False, num_expert_group=1, topk_group=1,
                 routed_scaling_factor=1.0, num_local_experts=None, shared_intermediate_size=0,
-                dtype="bf16", scoring_func="softmax", activation="silu") -> moe_params:
+                dtype="bf16", scoring_func="softmax", activation="silu",
+                weight_layout="row_major") -> moe_params:
     if scoring_func in ("softmax", MOE_SCORE_SOFTMAX):
         sf = MOE_SCORE_SOFTMAX
     elif scoring_func in ("sigmoid", MOE_SCORE_SIGMOID):
@@ -128,12 +131,18 @@ def make_params(num_experts, top_k, hidden_size, intermediate_size, renormalize=
         act = MOE_ACT_SWIGLUOAI
     else:
         raise ValueError(f"activation {activation!r}")
+    if weight_layout in ("row_major", MOE_WEIGHTS_ROW_MAJOR):
+        wlay = MOE_WEIGHTS_ROW_MAJOR
+    elif weight_layout in ("packed", MOE_WEIGHTS_PACKED):
+        wlay = MOE_WEIGHTS_PACKED
+    else:
+        raise ValueError(f"weight_layout {weight_layout!r}")
     return moe_params(
         int(num_experts), int(top_k), int(hidden_size), int(intermediate_size),
         int(bool(renormalize)), int(bool(use_grouped_topk)), int(num_expert_group),
         int(topk_group), float(routed_scaling_factor),
         int(num_experts if num_local_experts is None else num_local_experts),
-        int(shared_intermediate_size), _dtype_code(dtype), sf, act)
+        int(shared_intermediate_size), _dtype_code(dtype), sf, act, wlay)
 
 
 def _dtype_code(dtype) -> int:
@@ -163,6 +172,7 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 _SIGS = {
     "moe_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "moe_check_params": ([_P], ctypes.c_int),
+    "moe_pack_weights": ([_i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "moe_pick_block_m": ([_P, _i64, ctypes.POINTER(_i32)], ctypes.c_int),
     "moe_sorted_capacity": ([_P, _i64, _i32], _i64),
     "moe_workspace_size": ([_P, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
@@ -264,6 +274,23 @@ def strerror(code: int) -> str:
 
 def moe_check_params(p: moe_params) -> int:
     return lib().moe_check_params(ctypes.byref(p))
+
+
+def moe_pack_weights(w, out=None, stream=None):
+    """The packed weight layout (MOE_WEIGHTS_PACKED) of a bf16 weight tensor [..., rows, cols]
+    (w13 [E_l, 2I, H], w2 [E_l, H, I], shared_w13 [2 I_s, H], shared_w2 [H, I_s]): a new tensor
+    of the same shape and dtype (or `out`) holding the rearranged elements."""
+    import torch
+    if w.dtype != torch.bfloat16 or w.dim() < 2:
+        raise ValueError("moe_pack_weights: a bf16 tensor [..., rows, cols] is expected")
+    rows, cols = w.shape[-2], w.shape[-1]
+    n = w.numel() // (rows * cols) if rows * cols else 0
+    if out is None:
+        out = torch.empty_like(w)
+    elif out.dtype != torch.bfloat16 or out.numel() != w.numel():
+        raise ValueError("moe_pack_weights: out must be a bf16 tensor of the same size")
+    _check(lib().moe_pack_weights(n, rows, cols, _ptr(w), _ptr(out), _stream(stream)), "moe_pack_weights")
+    return out
 
 
 def moe_pick_block_m(p: moe_params, num_tokens: int) -> int:

@@ -26,6 +26,8 @@ int check_params(const moe_params* p) {
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (p->scoring_func != MOE_SCORE_SOFTMAX && p->scoring_func != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   if (p->activation != MOE_ACT_SILU && p->activation != MOE_ACT_SWIGLUOAI) return MOE_EINVAL;
+  if (p->weight_layout != MOE_WEIGHTS_ROW_MAJOR && p->weight_layout != MOE_WEIGHTS_PACKED) return MOE_EINVAL;
+  if (p->weight_layout == MOE_WEIGHTS_PACKED && p->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   const int E = p->num_experts;
   if (E < 1 || p->top_k < 1 || p->top_k > E) return MOE_EINVAL;
   if (!mult64(p->hidden_size) || !mult64(p->intermediate_size)) return MOE_EINVAL;
@@ -182,6 +184,20 @@ const char* moe_strerror(int code) {
 }
 
 int moe_check_params(const moe_params* p) { return check_params(p); }
+
+int moe_pack_weights(int64_t num_matrices, int64_t rows, int64_t cols, const void* src, void* dst,
+                     void* stream) {
+  if (num_matrices < 0 || rows < 16 || cols < 32 || rows % 16 != 0 || cols % 32 != 0) return MOE_EINVAL;
+  if (num_matrices == 0) return MOE_OK;
+  if (!src || !dst || !aligned16({src, dst})) return MOE_EINVAL;
+  const int64_t chunks = num_matrices * rows * (cols / 8);
+  if (chunks / num_matrices / rows != cols / 8 || chunks >= (int64_t{1} << 31)) return MOE_EINVAL;
+  const int64_t bytes = chunks * 16;
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_EINVAL;  // overlapping buffers
+  return moe::launch_pack_weights(num_matrices, rows, cols, src, dst, as_stream(stream));
+}
 
 int moe_pick_block_m(const moe_params* p, int64_t num_tokens, int32_t* block_m) {
   int rc = check_params(p);

@@ -56,7 +56,24 @@ struct GemmArgs {
                                // slot s at bias + s * bias_stride; NULL = none
   int64_t bias_stride;
   int32_t act;                 // kSiluMul: 0 = silu, 1 = swigluoai
+  int32_t b_packed;            // 1: B in the packed weight layout (b_offset), bf16 kernels only
 };
+
+// Packed weight layout: each [rows, K] bf16 matrix is stored as 1 KiB blocks of 16 rows x 32
+// K elements (row-major inside the block); the K blocks of one 16-row panel follow each other,
+// then the next panel. A load instruction that fetches 16 rows x 64 bytes, or 8 rows x 128
+// bytes, then reads one or two contiguous pieces of 1 KiB or 512 bytes instead of 16 or 8
+// separate row segments. Byte offset of element (row, k), k a multiple of 8:
+__device__ __forceinline__ uint32_t b_offset(const GemmArgs& a, int row, int k) {
+  if (!a.b_packed) return static_cast<uint32_t>(row) * static_cast<uint32_t>(a.K * 2) + k * 2;
+  return (static_cast<uint32_t>(row >> 4) * static_cast<uint32_t>(a.K >> 5) + (k >> 5)) * 1024u +
+         (row & 15) * 64 + (k & 31) * 2;
+}
+
+// Bytes between the B data of consecutive K steps of bk elements (bk a multiple of 32).
+__device__ __forceinline__ uint32_t b_step(const GemmArgs& a, int bk) {
+  return a.b_packed ? bk * 32 : bk * 2;
+}
 
 // K range [k0, k0 + klen) of this workgroup (blockIdx.y selects the split).
 __device__ __forceinline__ void k_range(const GemmArgs& a, int& k0, int& klen) {
@@ -262,8 +279,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
       brow = nt * BNR + r;
       if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
     }
-    goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16 + k0 * 2;
+    goff[NA + j] = b_offset(a, brow, k0 + c * 8);
   }
+  const uint32_t bstep = b_step(a, BK);
   // SKIP: real rows of the tile (a prefix, since padding ends each expert's segment). Every
   // tile row is one of this lane group's DMA rows; lanes with (lane & 7) == 0 count each once.
   __shared__ int real_rows[SKIP ? NW : 1];
@@ -286,7 +304,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   }
   // load instruction d of K step kt into stage st
   auto dma = [&](int d, int kt, int st) {
-    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
+    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (d < NA ? BK * 2 : bstep);
     if (d < NA)
       dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
     else
@@ -690,8 +708,9 @@ __global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
     const int c = (lane & 7) ^ lrow ^ (blk & 1);
     const int brow = MODE == kSiluMul ? (r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2))
                                       : nt * BNR + r;
-    goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + c * 16;
+    goff[NA + j] = b_offset(a, brow, c * 8);
   }
+  const uint32_t bstep = b_step(a, BK);
   uint32_t lA[2], lB[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
@@ -706,7 +725,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
   amask = __builtin_amdgcn_readfirstlane(amask);
   // load instruction d of K step kt into stage st; A rows past the block are not loaded
   auto dma = [&](int d, int kt, int st) {
-    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
+    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (d < NA ? BK * 2 : bstep);
     if (d < NA) {
       if (amask & (1u << d))
         dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
@@ -921,8 +940,9 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
     const int r = 16 * (wave + NW * j) + lrow;
     const int brow = MODE == kSiluMul ? (r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2))
                                       : nt * BNR + r;
-    goff[NA + j] = static_cast<uint32_t>(brow) * static_cast<uint32_t>(K * 2) + lchunk * 16;
+    goff[NA + j] = b_offset(a, brow, lchunk * 8);
   }
+  const uint32_t bstep = b_step(a, BK);
   const uint32_t lA0 = lds_addr(sA), lB0 = lds_addr(sB);
   // A load instructions of this wave (bit j): the 16-row groups wave + 8 j of the 20
   constexpr uint32_t kAmaskLo = (1u << NA) - 1, kAmaskHi = (1u << (NA - 1)) - 1;
@@ -930,7 +950,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
   constexpr int kMinLoads = AG / NW + NB;  // load instructions per K step of every wave, at least
   // load instruction d of K step kt into stage st
   auto dma = [&](int d, int kt, int st) {
-    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (BK * 2);
+    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (d < NA ? BK * 2 : bstep);
     if (d < NA) {
       if (amask & (1u << d))
         dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA0 + st * SA + (wave + NW * d) * 1024));
@@ -1118,8 +1138,9 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
       brow = nt * BNR + nb * 16 + q;
       if (MODE == kStoreF32 && brow >= a.N_valid) brow = a.N_valid - 1;
     }
-    pb[nb] = B + static_cast<int64_t>(brow) * K + k0 + kq;
+    pb[nb] = B + b_offset(a, brow, k0 + kq) / 2;
   }
+  const int bstep = static_cast<int>(b_step(a, 32) / 2);  // elements per K step of 32
 
   f32x4 acc[MB][NB];
 #pragma unroll
@@ -1136,7 +1157,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16(pb[nb] + (s + u) * 32);
+      for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16(pb[nb] + (s + u) * bstep);
 #pragma unroll
       for (int i = 0; i < MB; ++i) va[u][i] = load16(pa[i] + (s + u) * 32);
     }
@@ -1155,7 +1176,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
     for (int i = 0; i < MB; ++i) fa[i] = as_bf16x8(load16(pa[i] + s * 32));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 fb = as_bf16x8(load16(pb[nb] + s * 32));
+      const bf16x8 fb = as_bf16x8(load16(pb[nb] + s * bstep));
 #pragma unroll
       for (int i = 0; i < MB; ++i)
         acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb, acc[i][nb], 0, 0, 0);

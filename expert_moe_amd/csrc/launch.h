@@ -66,6 +66,10 @@ int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const
                const int32_t* block_expert, int block_m, int rows, void* act, void* y,
                hipStream_t s, const float* b13 = nullptr, const float* b2 = nullptr);
 
+// Packed weight layout (b_offset in gemm.h) of n row-major bf16 [rows, cols] matrices; the
+// total number of 16-byte chunks is below 2^31.
+int launch_pack_weights(int64_t n, int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s);
+
 // Compute units of the current device (cached per device); 0 if the query fails.
 int device_cu_count();
 

@@ -261,6 +261,7 @@ int launch_stream(GemmArgs g, int n_rows_b, int rows_per_block, int est_blocks, 
 GemmArgs base_args(const moe_params& p, int T, const int32_t* num_padded,
                    const int32_t* block_expert, int block_m, int rows) {
   GemmArgs a{};
+  a.b_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   a.row_div = p.top_k;
   a.M_pairs = T * p.top_k;
   a.M_rows = rows;
@@ -270,7 +271,30 @@ GemmArgs base_args(const moe_params& p, int T, const int32_t* num_padded,
   return a;
 }
 
+// One thread per 16-byte chunk of the packed output, in output order: chunk q is row
+// (q / 4) % 16 and column chunk q % 4 of block q / 64; consecutive threads write consecutive
+// 16 bytes.
+__global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           int rows, int cols, int total) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= total) return;
+  const int kblocks = cols / 32, panels = rows / 16;
+  const int blk = q >> 6, w = q & 63;
+  const int kb = blk % kblocks;
+  const int rest = blk / kblocks;            // matrix * panels + panel
+  const int row = (rest % panels) * 16 + (w >> 2);
+  const int64_t m = rest / panels;
+  const int64_t src_chunk = (m * rows + row) * (cols / 8) + kb * 4 + (w & 3);
+  dst[q] = src[src_chunk];
+}
+
 }  // namespace
+
+int launch_pack_weights(int64_t n, int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s) {
+  const int total = static_cast<int>(n * rows * (cols / 8));
+  return launch(pack_weights_kernel, ceil_div(total, 256), 256, 0, s, static_cast<const uint4*>(src),
+                static_cast<uint4*>(dst), static_cast<int>(rows), static_cast<int>(cols), total);
+}
 
 int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, int inter,
                    const int32_t* row_map, const int32_t* num_padded,

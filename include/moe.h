@@ -73,6 +73,9 @@ extern "C" {
 #define MOE_ACT_SILU 0
 #define MOE_ACT_SWIGLUOAI 1
 
+#define MOE_WEIGHTS_ROW_MAJOR 0
+#define MOE_WEIGHTS_PACKED 1
+
 /*
  * Layer parameters, named after the EP-aware FusedMoE constructor (_ep_init on the
  * ep_fused_moe_patch.py page) and the config fields of MoEMixin.recursive_replace.
@@ -100,6 +103,13 @@ extern "C" {
  *                            act = g' * sigmoid(1.702 g') * (u' + 1). recursive_replace names
  *                            "swigluoai" for gpt-oss; the formula is gpt-oss's. Applies to the
  *                            routed and the shared experts.
+ *  weight_layout             MOE_WEIGHTS_ROW_MAJOR (0, the default): w13, w2, shared_w13 and
+ *                            shared_w2 as listed under "Row-major layouts"; or
+ *                            MOE_WEIGHTS_PACKED (1, bf16 only, else MOE_EUNSUPPORTED): the
+ *                            same matrices rearranged by moe_pack_weights. The router gate
+ *                            Wg is always row-major. The arithmetic (and so every result bit)
+ *                            is the same for both layouts; packed weights stream from HBM in
+ *                            whole 1 KiB blocks instead of row segments of 64 or 128 bytes.
  *
  * Expert biases (has_bias of recursive_replace): optional fp32 b13 [E_l, 2I] (per slot: the I
  * gate biases, then the I up biases, the order of w13's rows) added to the gate/up
@@ -127,6 +137,7 @@ typedef struct moe_params {
   int32_t dtype;
   int32_t scoring_func;
   int32_t activation;
+  int32_t weight_layout;
 } moe_params;
 
 /* ------------------------------------------------------------------ host helpers */
@@ -138,6 +149,21 @@ const char* moe_strerror(int code);
  * Checks `p` (the rules listed with moe_params). MOE_OK, MOE_EINVAL or MOE_EUNSUPPORTED.
  */
 int moe_check_params(const moe_params* p);
+
+/*
+ * Rearranges num_matrices row-major bf16 matrices [rows, cols], stored back to back (w13
+ * [E_l, 2I, H] is E_l matrices [2I, H], w2 [E_l, H, I] is E_l matrices [H, I]; the shared
+ * expert's are one matrix each), into the packed weight layout of MOE_WEIGHTS_PACKED: per
+ * matrix, the 16-row panels one after the other; per panel, its cols / 32 blocks in column
+ * order; per block, its 16 rows x 32 elements row-major (1 KiB). Element (m, r, c) goes to
+ * element ((m * rows/16 + r/16) * cols/32 + c/32) * 512 + (r % 16) * 32 + c % 32 of dst.
+ * A weight preparation step, run once per weight set: dst has the size of src and must not
+ * overlap it; both 16-byte aligned device pointers. rows % 16 == 0 and cols % 32 == 0 (every
+ * weight matrix of a layer with H, I, I_s multiples of 64), num_matrices >= 0, the total
+ * below 2^31 16-byte chunks per call; else MOE_EINVAL. Enqueued on `stream`.
+ */
+int moe_pack_weights(int64_t num_matrices, int64_t rows, int64_t cols, const void* src, void* dst,
+                     void* stream);
 
 /*
  * The per-expert padding granule moe_forward uses for T tokens: the M-tile of the grouped

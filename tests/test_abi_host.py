@@ -361,3 +361,39 @@ def test_variable_blocks_granule_rules():
         F = FAKE
         assert moe.lib().moe_align_permute(ctypes.byref(p), 100, F, 0, F, F, F, F, F, 1 << 20,
                                            None) == moe.MOE_EINVAL
+
+
+def test_weight_layout_rules():
+    """Packed weights are a bf16 layout (fp32 layers: MOE_EUNSUPPORTED); other values are
+    invalid; a zeroed field is the row-major layout."""
+    assert moe.make_params(8, 2, 128, 256).weight_layout == moe.MOE_WEIGHTS_ROW_MAJOR
+    assert moe.moe_check_params(moe.make_params(8, 2, 128, 256, weight_layout="packed")) == moe.MOE_OK
+    p = moe.make_params(8, 2, 128, 256, dtype="f32", weight_layout="packed")
+    assert moe.moe_check_params(p) == moe.MOE_EUNSUPPORTED
+    p = moe.make_params(8, 2, 128, 256)
+    p.weight_layout = 2
+    assert moe.moe_check_params(p) == moe.MOE_EINVAL
+    with pytest.raises(ValueError, match="weight_layout"):
+        moe.make_params(8, 2, 128, 256, weight_layout="tiled")
+
+
+def test_pack_weights_argument_errors():
+    """moe_pack_weights refuses shapes off its 16 x 32 blocks, NULL, misaligned or overlapping
+    buffers before it launches anything (fake device addresses are never dereferenced)."""
+    lib = moe.lib()
+    a, b = 1 << 32, 1 << 33
+    assert lib.moe_pack_weights(0, 16, 32, None, None, None) == moe.MOE_OK
+    assert lib.moe_pack_weights(-1, 16, 32, a, b, None) == moe.MOE_EINVAL
+    assert lib.moe_pack_weights(1, 8, 32, a, b, None) == moe.MOE_EINVAL
+    assert lib.moe_pack_weights(1, 24, 32, a, b, None) == moe.MOE_EINVAL
+    assert lib.moe_pack_weights(1, 16, 48, a, b, None) == moe.MOE_EINVAL
+    assert lib.moe_pack_weights(1, 16, 32, None, b, None) == moe.MOE_EINVAL
+    assert lib.moe_pack_weights(1, 16, 32, a + 8, b, None) == moe.MOE_EINVAL
+    # 1 KiB matrices: dst inside src's range, and src inside dst's
+    assert lib.moe_pack_weights(2, 16, 32, a, a + 1024, None) == moe.MOE_EINVAL
+    assert lib.moe_pack_weights(2, 16, 32, a + 1024, a, None) == moe.MOE_EINVAL
+    # 2^31 chunks of 16 bytes or more
+    assert lib.moe_pack_weights(1 << 20, 1024, 1024 * 2, a, b, None) == moe.MOE_EINVAL
+    with pytest.raises(ValueError):
+        import torch
+        moe.moe_pack_weights(torch.zeros(16, 32, dtype=torch.float32))
