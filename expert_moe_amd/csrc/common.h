@@ -74,6 +74,24 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 #endif
 }
 
+// dma16 with the non-temporal hint (nt): data read once, streamed past the caches' reuse.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(base), "{m0}"(lds_addr)
+               : "memory");
+#endif
+}
+
+// dma16 or dma16_nt by a wave-uniform flag.
+__device__ __forceinline__ void dma16_hint(const void* base, uint32_t voff, uint32_t lds_addr, int nt) {
+  if (nt)
+    dma16_nt(base, voff, lds_addr);
+  else
+    dma16(base, voff, lds_addr);
+}
+
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   using lds_ptr = const __attribute__((address_space(3))) uint8_t*;
@@ -97,6 +115,13 @@ __device__ __forceinline__ void wg_barrier() {
 
 // Plain 16-byte global load.
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// 16-byte global load with the non-temporal hint.
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+}
 
 inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 

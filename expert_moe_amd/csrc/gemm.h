@@ -57,6 +57,7 @@ struct GemmArgs {
   int64_t bias_stride;
   int32_t act;                 // kSiluMul: 0 = silu, 1 = swigluoai
   int32_t b_packed;            // 1: B in the packed weight layout (b_offset), bf16 kernels only
+  int32_t b_nt;                // LDS tile kernels: 1 = weight loads with the non-temporal hint
 };
 
 // Packed weight layout: each [rows, K] bf16 matrix is stored as 1 KiB blocks of 16 rows x 32
@@ -308,7 +309,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
     if (d < NA)
       dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
     else
-      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024));
+      dma16_hint(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024), a.b_nt);
   };
 
   // wave -> (row group, weight-row group)
@@ -730,7 +731,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
       if (amask & (1u << d))
         dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
     } else {
-      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024));
+      dma16_hint(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024), a.b_nt);
     }
   };
 
@@ -884,7 +885,9 @@ __global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
 // 160 x 64) with K step 32 and four LDS stages in a ring, so the loads run three and a half K
 // steps ahead of the MFMAs instead of one and a half: about 108 KiB in flight per CU instead
 // of 72. For launches that stream their weights from HBM (one or two row blocks per expert),
-// where a load takes longer to come back than one K step of MFMAs.
+// where a load takes longer to come back than one K step of MFMAs; the weight loads carry the
+// non-temporal hint (measured, EP share T=8192: layer 0.240 -> 0.218 ms; on the two-stage
+// kernel, whose weight tiles serve several row blocks from L2, the hint costs 5%).
 // LDS rows are the 32 bf16 (64 bytes) of one tile row; the four 16-byte chunks of row r sit at
 // chunk ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows cover all banks. One
 // load instruction fills 16 rows (lane l: row 16 j + l / 4, position l % 4). Per wave and K
@@ -955,7 +958,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
       if (amask & (1u << d))
         dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA0 + st * SA + (wave + NW * d) * 1024));
     } else {
-      dma16(Bbase, voff, __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024));
+      dma16_nt(Bbase, voff, __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024));
     }
   };
 
@@ -1094,7 +1097,9 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
 // Weight-streaming tile for small row counts: 16*MB rows x 16*NB B rows per workgroup; the 4
 // waves split K, each streams its K range of every B row and A row straight from global
 // memory into v_mfma_f32_16x16x32_bf16 operands (U K steps in flight); partial sums meet in
-// LDS. Tiles follow the XCD-aware order of the LDS-fed kernel.
+// LDS. Tiles follow the XCD-aware order of the LDS-fed kernel. A weight tile is read by the
+// one or few row blocks of its expert: the weight loads carry the non-temporal hint (measured: skewed share T=1 layer
+// 0.182 -> 0.125 ms, Mixtral-shaped T=32 0.544 -> 0.460 ms).
 // ----------------------------------------------------------------------------------------
 template <int NB, int MODE, int MB = 1>
 __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
@@ -1157,7 +1162,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16(pb[nb] + (s + u) * bstep);
+      for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16_nt(pb[nb] + (s + u) * bstep);
 #pragma unroll
       for (int i = 0; i < MB; ++i) va[u][i] = load16(pa[i] + (s + u) * 32);
     }
@@ -1176,7 +1181,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
     for (int i = 0; i < MB; ++i) fa[i] = as_bf16x8(load16(pa[i] + s * 32));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 fb = as_bf16x8(load16(pb[nb] + s * bstep));
+      const bf16x8 fb = as_bf16x8(load16_nt(pb[nb] + s * bstep));
 #pragma unroll
       for (int i = 0; i < MB; ++i)
         acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb, acc[i][nb], 0, 0, 0);
