@@ -1156,16 +1156,18 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
   const int steps = klen / 32;
   const int s0 = steps * wave / 4;
   const int s1 = steps * (wave + 1) / 4;
-  int s = s0;
-  for (; s + U <= s1; s += U) {
-    uint4 va[U][MB], vb[U][NB];
+  // batches of U K steps, double-buffered: the loads of batch b+1 go out before the MFMAs of
+  // batch b wait for theirs, so a wave always has a batch in flight
+  auto load_batch = [&](uint4 (&va)[U][MB], uint4 (&vb)[U][NB], int sb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16_nt(pb[nb] + (s + u) * bstep);
+      for (int nb = 0; nb < NB; ++nb) vb[u][nb] = load16_nt(pb[nb] + (sb + u) * bstep);
 #pragma unroll
-      for (int i = 0; i < MB; ++i) va[u][i] = load16(pa[i] + (s + u) * 32);
+      for (int i = 0; i < MB; ++i) va[u][i] = load16(pa[i] + (sb + u) * 32);
     }
+  };
+  auto mfma_batch = [&](const uint4 (&va)[U][MB], const uint4 (&vb)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -1174,6 +1176,33 @@ __global__ void __launch_bounds__(256) gemm_bf16_stream(GemmArgs a) {
         for (int nb = 0; nb < NB; ++nb)
           acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[u][i]), as_bf16x8(vb[u][nb]),
                                                                acc[i][nb], 0, 0, 0);
+  };
+  int s = s0;
+  if (s + U <= s1) {
+    uint4 va0[U][MB], vb0[U][NB], va1[U][MB], vb1[U][NB];
+    load_batch(va0, vb0, s);
+    // each path has its own MFMA copy: where a path without the next batch's loads joins one
+    // with them, the compiler's wait counts take the smaller and drain the next batch too
+    while (true) {
+      if (s + 2 * U <= s1) {
+        load_batch(va1, vb1, s + U);
+        mfma_batch(va0, vb0);
+        s += U;
+      } else {
+        mfma_batch(va0, vb0);
+        s += U;
+        break;
+      }
+      if (s + 2 * U <= s1) {
+        load_batch(va0, vb0, s + U);
+        mfma_batch(va1, vb1);
+        s += U;
+      } else {
+        mfma_batch(va1, vb1);
+        s += U;
+        break;
+      }
+    }
   }
   for (; s < s1; ++s) {
     bf16x8 fa[MB];
