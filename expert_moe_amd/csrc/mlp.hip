@@ -428,7 +428,11 @@ bool prefer_var_blocks(const moe_params& p, int64_t T) {
   const double touched = 1.0 - std::exp(-per);
   const double tiles = p.num_local_experts * touched * bvar / 8.0 * (2.0 * p.intermediate_size / 256.0);
   const int n_cu = cu_count() > 0 ? cu_count() : 256;
-  return bvar <= 0.95 * b256 && tiles >= n_cu;
+  if (bvar <= 0.95 * b256 && tiles >= n_cu) return true;
+  // As many blocks, 128 to 512 rows per expert: the variable blocks run the deep-pipeline
+  // kernel, the 256 granule a two-stage one (DeepSeek-V2-shaped, 153 rows per expert: 0.636 ->
+  // 0.619 ms; skewed T=256 and T=16384, 32 and 2048 rows per expert, lose 8% and 7%).
+  return per >= 128.0 && stream_var_blocks(p, static_cast<int>(T)) && bvar <= b256;
 }
 
 int launch_mlp(const moe_params& p, int T, const void* x, const void* w13, const void* w2,
