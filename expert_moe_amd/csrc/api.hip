@@ -260,9 +260,8 @@ static int route_impl(const moe_params* p, const moe::EplbMap* eplb, int64_t num
   if (ws_bytes < L.route_need) return MOE_ENOSPC;
   const int T = static_cast<int>(num_tokens);
   float* logits = static_cast<float*>(ws);
-  if ((rc = moe::launch_router_logits(*p, T, x, w_gate, logits, as_stream(stream)))) return rc;
-  return moe::launch_topk(*p, T, logits, logit_bias, score_bias, expert_map, topk_ids, topk_w,
-                          topk_local, as_stream(stream), eplb);
+  return moe::launch_route(*p, T, x, w_gate, logits, logit_bias, score_bias, expert_map, topk_ids,
+                           topk_w, topk_local, as_stream(stream), eplb);
 }
 
 int moe_route(const moe_params* p, int64_t num_tokens, const void* x, const void* w_gate,
@@ -439,10 +438,8 @@ static int forward_impl(const moe_params* p, const moe::EplbMap* eplb, const moe
     if (hipEventRecord(join, ss) != hipSuccess) return rc ? rc : MOE_EHIP;
   }
   if (rc == MOE_OK)
-    rc = moe::launch_router_logits(*p, T, x, w_gate, static_cast<float*>(scratch), s);
-  if (rc == MOE_OK)
-    rc = moe::launch_topk(*p, T, static_cast<float*>(scratch), logit_bias, score_bias, expert_map,
-                          ids, tw, local, s, eplb);
+    rc = moe::launch_route(*p, T, x, w_gate, static_cast<float*>(scratch), logit_bias, score_bias,
+                           expert_map, ids, tw, local, s, eplb);
   if (rc == MOE_OK)
     rc = moe::launch_align(*p, T, local, bm, sorted_pairs, block_expert, pair_row, num_padded,
                            at<int32_t>(ws, L.meta), at<int32_t>(ws, L.chunk), s);

@@ -40,6 +40,11 @@ int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
                 const float* score_bias, const int32_t* expert_map, int32_t* ids, float* w,
                 int32_t* local, hipStream_t s, const EplbMap* eplb = nullptr);
 
+// The whole router: the logits GEMM into `logits`, then launch_topk.
+int launch_route(const moe_params& p, int T, const void* x, const void* w_gate, float* logits,
+                 const float* bias, const float* score_bias, const int32_t* expert_map,
+                 int32_t* ids, float* w, int32_t* local, hipStream_t s, const EplbMap* eplb = nullptr);
+
 // Count / scan / scatter of the (token, slot) pairs by local expert (block_expert may be NULL).
 // meta: [num_padded(1) | offsets(E_l+1) | counts(E_l)], chunk: [align_chunks(T) * E_l].
 int launch_align(const moe_params& p, int T, const int32_t* topk_local, int block_m,

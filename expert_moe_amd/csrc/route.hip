@@ -107,55 +107,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// 4 tokens per workgroup (one per wave); lane l holds experts l + 64 q for q < NQ, E <= 64 NQ.
+// Scores, selection and outputs of token t, whose logits plus logit bias lane l holds in
+// pv[q] (expert l + 64 q; -inf past E or for an invalid token) and its selection biases in
+// sb[q]; sp: this wave's LDS row of 64 NQ floats (grouped routing only). Every lane of the
+// wave calls it; lanes < k write the token's outputs.
 template <int NQ>
-__global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
-  __shared__ float sp[4][64 * NQ];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  const bool valid = t < a.T;
+__device__ __forceinline__ void select_token(const TopkArgs& a, int t, bool valid, float (&pv)[NQ],
+                                             const float (&sb)[NQ], float* sp, int lane) {
   const int E = a.E;
-
-  // Every load of the token goes out before the first use (addresses clamped into the
-  // arrays, values masked afterwards): the logits, the K-split partial sums four splits at a
-  // time, and the biases. Loads behind per-value guards each waited for the one before.
-  const int tc = valid ? t : a.T - 1;
-  float* row = a.logits + static_cast<int64_t>(tc) * E;
-  const int64_t stride = static_cast<int64_t>(a.T) * E;
-  int ec[NQ];
-  float pv[NQ], lb[NQ], sb[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    ec[q] = min(lane + 64 * q, E - 1);
-    pv[q] = row[ec[q]];
-  }
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    lb[q] = a.bias ? a.bias[ec[q]] : 0.f;
-    sb[q] = a.sbias ? a.sbias[ec[q]] : 0.f;
-  }
-  for (int s0 = 1; s0 < a.splits; s0 += 4) {
-    float v[4][NQ];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t off = static_cast<int64_t>(min(s0 + j, a.splits - 1)) * stride;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) v[j][q] = row[off + ec[q]];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (s0 + j < a.splits) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) pv[q] += v[j][q];
-      }
-  }
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const bool ok = valid && lane + 64 * q < E;
-    if (ok && a.splits > 1) row[ec[q]] = pv[q];
-    pv[q] = ok ? pv[q] + lb[q] : -INFINITY;
-  }
   if (a.sigmoid) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) pv[q] = (lane + 64 * q < E) ? 1.f / (1.f + expf(-pv[q])) : 0.f;
@@ -189,17 +148,18 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     // topk_group best groups (ties to the lower group) stay candidates
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      if (lane + 64 * q < E) sp[wave][lane + 64 * q] = sv[q];
-    __syncthreads();
+      if (lane + 64 * q < E) sp[lane + 64 * q] = sv[q];
+    // the wave reads back only its own row: its LDS accesses are processed in order
+    __builtin_amdgcn_wave_barrier();
     const int gsz = E / a.G;
     float gs = -INFINITY;
     if (lane < a.G) {
       if (a.sbias == nullptr) {
-        for (int i = 0; i < gsz; ++i) gs = fmaxf(gs, sp[wave][lane * gsz + i]);
+        for (int i = 0; i < gsz; ++i) gs = fmaxf(gs, sp[lane * gsz + i]);
       } else {
         float t1 = -INFINITY, t2 = -INFINITY;
         for (int i = 0; i < gsz; ++i) {
-          const float v = sp[wave][lane * gsz + i];
+          const float v = sp[lane * gsz + i];
           if (v > t1) {
             t2 = t1;
             t1 = v;
@@ -277,6 +237,58 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   }
 }
 
+// 4 tokens per workgroup (one per wave); lane l holds experts l + 64 q for q < NQ, E <= 64 NQ.
+template <int NQ>
+__global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
+  __shared__ float sp[4][64 * NQ];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  const bool valid = t < a.T;
+  const int E = a.E;
+
+  // Every load of the token goes out before the first use (addresses clamped into the
+  // arrays, values masked afterwards): the logits, the K-split partial sums four splits at a
+  // time, and the biases. Loads behind per-value guards each waited for the one before.
+  const int tc = valid ? t : a.T - 1;
+  float* row = a.logits + static_cast<int64_t>(tc) * E;
+  const int64_t stride = static_cast<int64_t>(a.T) * E;
+  int ec[NQ];
+  float pv[NQ], lb[NQ], sb[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    ec[q] = min(lane + 64 * q, E - 1);
+    pv[q] = row[ec[q]];
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    lb[q] = a.bias ? a.bias[ec[q]] : 0.f;
+    sb[q] = a.sbias ? a.sbias[ec[q]] : 0.f;
+  }
+  for (int s0 = 1; s0 < a.splits; s0 += 4) {
+    float v[4][NQ];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t off = static_cast<int64_t>(min(s0 + j, a.splits - 1)) * stride;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) v[j][q] = row[off + ec[q]];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < a.splits) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) pv[q] += v[j][q];
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const bool ok = valid && lane + 64 * q < E;
+    if (ok && a.splits > 1) row[ec[q]] = pv[q];
+    pv[q] = ok ? pv[q] + lb[q] : -INFINITY;
+  }
+  select_token<NQ>(a, t, valid, pv, sb, sp[wave], lane);
+}
+
 }  // namespace
 
 int router_splits(const moe_params& p, int T) {
@@ -342,12 +354,14 @@ int launch_router_logits(const moe_params& p, int T, const void* x, const void* 
   }
 }
 
-int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
-                const float* score_bias, const int32_t* expert_map, int32_t* ids, float* w,
-                int32_t* local, hipStream_t s, const EplbMap* eplb) {
+namespace {
+
+TopkArgs topk_args(const moe_params& p, int T, float* logits, int splits, const float* bias,
+                   const float* score_bias, const int32_t* expert_map, int32_t* ids, float* w,
+                   int32_t* local, const EplbMap* eplb) {
   TopkArgs a;
   a.logits = logits;
-  a.splits = router_splits(p, T);
+  a.splits = splits;
   a.bias = bias;
   a.sbias = score_bias;
   a.sigmoid = p.scoring_func == MOE_SCORE_SIGMOID;
@@ -368,10 +382,27 @@ int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
   a.keep = p.use_grouped_topk ? p.topk_group : 1;
   a.E_l = p.num_local_experts;
   a.rsf = p.routed_scaling_factor;
+  return a;
+}
+
+}  // namespace
+
+int launch_topk(const moe_params& p, int T, float* logits, const float* bias,
+                const float* score_bias, const int32_t* expert_map, int32_t* ids, float* w,
+                int32_t* local, hipStream_t s, const EplbMap* eplb) {
+  const TopkArgs a = topk_args(p, T, logits, router_splits(p, T), bias, score_bias, expert_map, ids,
+                               w, local, eplb);
   const int blocks = ceil_div(T, 4);
   if (a.E <= 64) return launch(topk_kernel<1>, blocks, 256, 0, s, a);
   if (a.E <= 128) return launch(topk_kernel<2>, blocks, 256, 0, s, a);
   return launch(topk_kernel<4>, blocks, 256, 0, s, a);
+}
+
+int launch_route(const moe_params& p, int T, const void* x, const void* w_gate, float* logits,
+                 const float* bias, const float* score_bias, const int32_t* expert_map,
+                 int32_t* ids, float* w, int32_t* local, hipStream_t s, const EplbMap* eplb) {
+  if (int rc = launch_router_logits(p, T, x, w_gate, logits, s)) return rc;
+  return launch_topk(p, T, logits, bias, score_bias, expert_map, ids, w, local, s, eplb);
 }
 
 }  // namespace moe
