@@ -24,9 +24,16 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ int local_slot(const int32_t* tl, int64_t i, int E_l) {
-  const int s = tl[i];
-  return (s >= 0 && s < E_l) ? s : -1;
+// Slots of a token's pairs in batches of kSlotBatch (pairs i0 .. i0 + n - 1, n >= 1): the
+// batch's loads are all issued before the first is used (addresses clamped to the last pair,
+// values past n masked), one memory round trip per batch; -1 for a slot that is not local.
+constexpr int kSlotBatch = 8;
+__device__ __forceinline__ void load_slots(const int32_t* tl, int64_t i0, int n, int E_l,
+                                           int (&s)[kSlotBatch]) {
+#pragma unroll
+  for (int u = 0; u < kSlotBatch; ++u) s[u] = tl[i0 + min(u, n - 1)];
+#pragma unroll
+  for (int u = 0; u < kSlotBatch; ++u) s[u] = (u < n && s[u] >= 0 && s[u] < E_l) ? s[u] : -1;
 }
 
 // Exclusive prefix sum of v over the 256 threads of the workgroup (thread order), and the
@@ -107,25 +114,35 @@ __device__ __forceinline__ void chunk_scatter(const int32_t* __restrict__ tl, in
   const int t = blockIdx.x * kAlignChunk + tid;
   const bool valid = t < T;
   if (valid)
-    for (int j = 0; j < k; ++j) {
-      const int s = local_slot(tl, static_cast<int64_t>(t) * k + j, E_l);
-      if (s >= 0) atomicOr(&mask[wave][s], 1ull << lane);
+    for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+      int sl[kSlotBatch];
+      load_slots(tl, static_cast<int64_t>(t) * k + j0, min(kSlotBatch, k - j0), E_l, sl);
+#pragma unroll
+      for (int u = 0; u < kSlotBatch; ++u)
+        if (sl[u] >= 0) atomicOr(&mask[wave][sl[u]], 1ull << lane);
     }
   __syncthreads();
   if (!valid) return;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const int64_t pid = static_cast<int64_t>(t) * k + j;
-    const int s = local_slot(tl, pid, E_l);
-    if (s < 0) {
-      pair_row[pid] = -1;
-      continue;
+  for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+    int sl[kSlotBatch];
+    const int n = min(kSlotBatch, k - j0);
+    load_slots(tl, static_cast<int64_t>(t) * k + j0, n, E_l, sl);
+#pragma unroll
+    for (int u = 0; u < kSlotBatch; ++u) {
+      if (u >= n) break;
+      const int64_t pid = static_cast<int64_t>(t) * k + j0 + u;
+      const int s = sl[u];
+      if (s < 0) {
+        pair_row[pid] = -1;
+        continue;
+      }
+      int before = __popcll(mask[wave][s] & below);
+      for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
+      const int pos = base[s] + before;
+      sorted_pairs[pos] = static_cast<int32_t>(pid);
+      pair_row[pid] = pos;
     }
-    int before = __popcll(mask[wave][s] & below);
-    for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
-    const int pos = base[s] + before;
-    sorted_pairs[pos] = static_cast<int32_t>(pid);
-    pair_row[pid] = pos;
   }
 }
 
@@ -139,9 +156,12 @@ __global__ void __launch_bounds__(256) align_count(const int32_t* __restrict__ t
   __syncthreads();
   const int t = blockIdx.x * kAlignChunk + threadIdx.x;
   if (t < T)
-    for (int j = 0; j < k; ++j) {
-      const int s = local_slot(tl, static_cast<int64_t>(t) * k + j, E_l);
-      if (s >= 0) atomicAdd(&hist[s], 1);
+    for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+      int sl[kSlotBatch];
+      load_slots(tl, static_cast<int64_t>(t) * k + j0, min(kSlotBatch, k - j0), E_l, sl);
+#pragma unroll
+      for (int u = 0; u < kSlotBatch; ++u)
+        if (sl[u] >= 0) atomicAdd(&hist[sl[u]], 1);
     }
   __syncthreads();
   for (int e = threadIdx.x; e < E_l; e += 256) chunk[static_cast<int64_t>(blockIdx.x) * E_l + e] = hist[e];
@@ -290,12 +310,15 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
   __syncthreads();
   const bool valid = tid < T;
   if (valid)
-    for (int j = 0; j < k; ++j) {
-      const int s = local_slot(tl, static_cast<int64_t>(tid) * k + j, E_l);
-      if (s >= 0) {
-        atomicAdd(&hist[s], 1);
-        atomicOr(&mask[wave][s], 1ull << lane);
-      }
+    for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+      int sl[kSlotBatch];
+      load_slots(tl, static_cast<int64_t>(tid) * k + j0, min(kSlotBatch, k - j0), E_l, sl);
+#pragma unroll
+      for (int u = 0; u < kSlotBatch; ++u)
+        if (sl[u] >= 0) {
+          atomicAdd(&hist[sl[u]], 1);
+          atomicOr(&mask[wave][sl[u]], 1ull << lane);
+        }
     }
   __syncthreads();
   int32_t* offsets = meta + 1;
@@ -321,18 +344,25 @@ __global__ void __launch_bounds__(256) align_single(const int32_t* __restrict__ 
   __syncthreads();
   if (!valid) return;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const int64_t pid = static_cast<int64_t>(tid) * k + j;
-    const int s = local_slot(tl, pid, E_l);
-    if (s < 0) {
-      pair_row[pid] = -1;
-      continue;
+  for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+    int sl[kSlotBatch];
+    const int n = min(kSlotBatch, k - j0);
+    load_slots(tl, static_cast<int64_t>(tid) * k + j0, n, E_l, sl);
+#pragma unroll
+    for (int u = 0; u < kSlotBatch; ++u) {
+      if (u >= n) break;
+      const int64_t pid = static_cast<int64_t>(tid) * k + j0 + u;
+      const int s = sl[u];
+      if (s < 0) {
+        pair_row[pid] = -1;
+        continue;
+      }
+      int before = __popcll(mask[wave][s] & below);
+      for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
+      const int pos = seg[s] + before;
+      sorted_pairs[pos] = static_cast<int32_t>(pid);
+      pair_row[pid] = pos;
     }
-    int before = __popcll(mask[wave][s] & below);
-    for (int w = 0; w < wave; ++w) before += __popcll(mask[w][s]);
-    const int pos = seg[s] + before;
-    sorted_pairs[pos] = static_cast<int32_t>(pid);
-    pair_row[pid] = pos;
   }
 }
 
