@@ -13,8 +13,13 @@ gate/up and down GEMMs, combine); inputs are resident in HBM before timing start
 expert-parallel exchange around the path (dispatch and unpack, at the workload's EP degree)
 is timed on the step's routing and reported in the ``ep_exchange`` field.
 
-Warm-up: the requested W steps, extended until at least 0.3 s of steps have run (the GPU clock
-ramps over the first tens of milliseconds of load; ``warmup_run`` reports the count).
+Expert weights are rearranged once at set-up into the packed layout (``moe_pack_weights``,
+like a weight load; ``--weight-layout row_major`` keeps the plain one); ``config.weight_layout``
+says which. Warm-up: the requested W steps, extended until at least 0.3 s of steps have run
+(the GPU clock ramps over the first tens of milliseconds of load; ``warmup_run`` reports the
+count). ``timing`` holds hipEvent times of 50 single steps, each after a 512 MB write that
+evicts the MALL (median, p10, p90); ``configs`` holds the same for every configuration point of
+the layer families, with each point's target and whether it is met.
 
 The dominant kernel's duration comes from HIP events recorded on the launch stream
 around ``moe_expert_gate_up`` in a second timed loop that runs the same kernels through
@@ -77,8 +82,10 @@ def measured_traffic(workload: str, T: int):
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 2000 steps: several seconds of timed GPU work on the default layer (2.4 ms a step), long
+    # enough for a once-a-second utilisation sampler to see the GPU busy
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--tokens", type=int, default=None, help="token count (default: the largest)")
     ap.add_argument("--decode-tokens", type=int, default=None,
