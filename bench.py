@@ -292,15 +292,63 @@ def warm_up(fn, steps):
     return n
 
 
+class SclkSampler:
+    """Samples the GPU's current shader clock (the starred line of the DRM pp_dpm_sclk file)
+    every 20 ms on a host thread while a timed loop runs; median in MHz, or None where the file
+    cannot be read."""
+
+    def __init__(self):
+        import glob
+        import threading
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if files else None
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().split("M")[0])
+        return None
+
+    def _run(self):
+        while not self.stop.is_set():
+            try:
+                v = self._read()
+                if v is not None and v > 200:  # deep-sleep readings between launches
+                    self.samples.append(v)
+            except (OSError, ValueError, IndexError):
+                return
+            self.stop.wait(0.02)
+
+    def __enter__(self):
+        if self.path:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.path:
+            self.thread.join()
+
+    def median_mhz(self):
+        import statistics
+        return statistics.median(self.samples) if self.samples else None
+
+
 def run_point(host, w, T, steps, warmup):
     import torch
     b = Bench(w, T, host)
     b.warmup_run = warm_up(b.forward, warmup)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        b.forward()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    with SclkSampler() as clk:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            b.forward()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+    b.sclk_mhz = clk.median_mhz()
     ids = b.ids.cpu().numpy()
     alg = algorithmic(w, T, ids)
 
@@ -333,6 +381,11 @@ def roofline(alg, stage_ms, bound):
             "kernel": "moe_expert_gate_up (weight-streaming bf16 MFMA)",
             "per_launch": f"touched w13 + x + act = {alg['gate_up_bytes']} B",
             "avg_ms": round(stage_ms["gate_up"], 4)}
+
+
+def res_frac_at_clock(roof, sclk_mhz):
+    """The roofline fraction against the MFMA peak at the measured clock instead of 2.4 GHz."""
+    return roof["frac"] * 2400.0 / sclk_mhz
 
 
 def exchange_ep_size(w):
@@ -814,6 +867,11 @@ def main():
         "achieved_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
         "achieved_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "roofline": dict(roofline(alg, stage, bound), traffic=measured_traffic(w.key, T)),
+        # the shader clock during the timed loop (median of 20 ms samples) and the dominant
+        # kernel's fraction of the MFMA peak at that clock (the peak scales with it; 2.4 GHz)
+        "sclk_mhz": b.sclk_mhz,
+        "frac_at_clock": (round(res_frac_at_clock(roofline(alg, stage, bound), b.sclk_mhz), 4)
+                          if b.sclk_mhz and bound == "mfma" else None),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "split_path_ms_per_step": round(split_ms, 4),
         "timing": dict(timing, note="single steps timed with hipEvents after a 512 MB cache "
