@@ -652,242 +652,16 @@ __device__ __forceinline__ void var_epilogue(const GemmArgs& a, f32x16 (&acc)[TM
 // Variable row blocks: one block of the block table per tile row range (32 .. 320 rows, a
 // multiple of 32, inside one expert's segment: 256-row blocks, where an expert's last piece of
 // at most 64 rows joins the block before it instead of taking a nearly empty tile of its own).
-// 320 x 256 tile, 8 waves (2 x 4, 160 x 64 each, two per SIMD), K step 64, two LDS stages fed
-// by global->LDS loads, as gemm_bf16_dma. Each wave runs the K loop compiled for the number of
-// its five 32-row MFMA blocks that hold rows of the block (no MFMA or fragment read for the
-// others); the A loads of rows past the block are not issued (the waits are all vmcnt(0)).
-// Register budget (two waves per SIMD): the A fragments are single-buffered, each read for the
-// next K slice right after its row block's last MFMA of this slice; the B fragments alternate
-// between two sets.
-// ----------------------------------------------------------------------------------------
-template <int MODE>
-__global__ void __launch_bounds__(512) gemm_bf16_var(GemmArgs a) {
-  constexpr int BM = 320, BNR = 256, WM = 2, WN = 4, NW = 8;
-  constexpr int BK = 64, ROWB = 128;
-  constexpr int TM = BM / WM, TMB = TM / 32;        // 160 rows, 5 MFMA row blocks per wave
-  constexpr int TNR = BNR / WN, TNB = TNR / 32;     // 64 weight rows, 2 MFMA column blocks
-  constexpr int NA = BM / (8 * NW), NB = BNR / (8 * NW), ND = NA + NB;
-  static_assert(MODE != kStoreF32, "bf16 outputs");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][BM * ROWB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB[2][BNR * ROWB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t* bt = a.block_expert;
-  const int nblk = bt[0];
-  int L, mb, nt;
-  if (!xcd_tile(static_cast<int>(blockIdx.x), nblk * a.n_tiles, L)) return;
-  tile_coords(L, nblk, a.n_tiles, mb, nt, kVarGroupN);
-  const int slot = bt[1 + 2 * mb];
-  const int m0 = bt[2 + 2 * mb];
-  const int vrows = min(BM, bt[4 + 2 * mb] - m0);
-  const char* const Abase = static_cast<const char*>(a.A);
-  const char* const Bbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.B) + slot * a.b_stride);
-  const int K = a.K;
-
-  // load sources, as gemm_bf16_dma (rows past the block read its last row)
-  const int lrow = lane >> 3;
-  uint32_t goff[ND];
-  {
-    int rows[NA], src[NA];
-#pragma unroll
-    for (int j = 0; j < NA; ++j) rows[j] = m0 + min(8 * (wave + NW * j) + lrow, vrows - 1);
-    gemm_src_rows(a, rows, src);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int blk = wave + NW * j;
-      const int c = (lane & 7) ^ lrow ^ (blk & 1);
-      goff[j] = static_cast<uint32_t>(src[j]) * static_cast<uint32_t>(K * 2) + c * 16;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int blk = wave + NW * j;
-    const int r = 8 * blk + lrow;
-    const int c = (lane & 7) ^ lrow ^ (blk & 1);
-    const int brow = MODE == kSiluMul ? (r < BNR / 2 ? nt * (BNR / 2) + r : a.N + nt * (BNR / 2) + (r - BNR / 2))
-                                      : nt * BNR + r;
-    goff[NA + j] = b_offset(a, brow, c * 8);
-  }
-  const uint32_t bstep = b_step(a, BK);
-  uint32_t lA[2], lB[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    lA[st] = lds_addr(sA[st]);
-    lB[st] = lds_addr(sB[st]);
-  }
-  // A load instructions of this wave that fill rows of the block (bit d), wave-uniform
-  uint32_t amask = 0;
-#pragma unroll
-  for (int d = 0; d < NA; ++d)
-    if (8 * (wave + NW * d) < vrows) amask |= 1u << d;
-  amask = __builtin_amdgcn_readfirstlane(amask);
-  // load instruction d of K step kt into stage st; A rows past the block are not loaded
-  auto dma = [&](int d, int kt, int st) {
-    const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (d < NA ? BK * 2 : bstep);
-    if (d < NA) {
-      if (amask & (1u << d))
-        dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
-    } else {
-      dma16_hint(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024), a.b_nt);
-    }
-  };
-
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const int fr = lane & 31;
-  const int sw = (fr & 7) ^ ((fr >> 3) & 1);
-  int coff[BK / 16];
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) coff[ks] = ((2 * ks + (lane >> 5)) ^ sw) * 16;
-  const int arow = (wm * TM + fr) * ROWB;  // + i * 32 * ROWB for row block i
-  int brow0[TNB];
-#pragma unroll
-  for (int j = 0; j < TNB; ++j) {
-    const int r0 = MODE == kSiluMul
-                       ? (j < TNB / 2 ? wn * (TNR / 2) + j * 32 : BNR / 2 + wn * (TNR / 2) + (j - TNB / 2) * 32)
-                       : wn * TNR + j * 32;
-    brow0[j] = (r0 + fr) * ROWB;
-  }
-
-  f32x16 acc[TMB][TNB];
-#pragma unroll
-  for (int i = 0; i < TMB; ++i)
-#pragma unroll
-    for (int j = 0; j < TNB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = K / BK;
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-
-  auto kloop = [&](auto nact_c) {
-    constexpr int NACT = decltype(nact_c)::value;
-    constexpr int NM = NACT * TNB;
-    bf16x8 fa[TMB], fb[2][TNB];
-    auto readA = [&](const uint8_t* pA, int ks, int i) {
-      fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(pA + arow + i * 32 * ROWB + coff[ks]));
-    };
-    auto readB = [&](const uint8_t* pB, int ks, int set) {
-#pragma unroll
-      for (int j = 0; j < TNB; ++j)
-        fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(pB + brow0[j] + coff[ks]));
-    };
-    // MFMAs of one K slice on B set `set`. NEXT: after row block i's MFMAs, A fragment i of the
-    // next slice (pA, ks) is read. DMA: the loads of K step kt_dma into stage dst, spread over
-    // the MFMAs.
-    auto slice = [&](int set, auto next_c, const uint8_t* pA, int ks, auto dma_c, int kt_dma, int dst) {
-      constexpr bool NEXT = decltype(next_c)::value != 0;
-      constexpr bool DMA = decltype(dma_c)::value != 0;
-      if constexpr (DMA && NM == 0) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) dma(d, kt_dma, dst);
-      }
-#pragma unroll
-      for (int i = 0; i < NACT; ++i) {
-#pragma unroll
-        for (int j = 0; j < TNB; ++j) {
-          const int m = i * TNB + j;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[i], acc[i][j], 0, 0, 0);
-          if constexpr (DMA) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = m * ND / (NM > 0 ? NM : 1); d < (m + 1) * ND / (NM > 0 ? NM : 1); ++d) dma(d, kt_dma, dst);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        if constexpr (NEXT) readA(pA, ks, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    // K step kt on stage ST. KIND 0: step kt+2 is loaded during slice 3; 1: step kt+1 is the
-    // last; 2: kt is the last step.
-    auto step = [&](auto st_c, auto kind_c, int kt) {
-      constexpr int ST = decltype(st_c)::value;
-      constexpr int KIND = decltype(kind_c)::value;
-      constexpr int NX = ST ^ 1;
-      using On = std::integral_constant<int, 1>;
-      using Off = std::integral_constant<int, 0>;
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        if (NACT > 0) readB(sB[ST], s + 1, (s + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        slice(s & 1, On{}, sA[ST], s + 1, Off{}, 0, 0);
-      }
-      if constexpr (KIND < 2) {
-        // every load of step kt+1 has landed and no wave still reads stage ST
-        __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
-        __syncthreads();
-        if (NACT > 0) readB(sB[NX], 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (KIND == 0)
-          slice(1, On{}, sA[NX], 0, On{}, kt + 2, ST);
-        else
-          slice(1, On{}, sA[NX], 0, Off{}, 0, 0);
-      } else {
-        slice(1, Off{}, sA[ST], 0, Off{}, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // prologue: steps 0 and 1 in flight, all landed (some A loads may be skipped), slice 0 read
-#pragma unroll
-    for (int d = 0; d < ND; ++d) dma(d, 0, 0);
-    if (nk > 1) {
-#pragma unroll
-      for (int d = 0; d < ND; ++d) dma(d, 1, 1);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (NACT > 0) readB(sB[0], 0, 0);
-#pragma unroll
-    for (int i = 0; i < NACT; ++i) readA(sA[0], 0, i);
-    if (nk == 1) {
-      step(C0{}, C2{}, 0);
-    } else if ((nk & 1) == 0) {
-      for (int kt = 0; kt < nk - 2; kt += 2) {
-        step(C0{}, C0{}, kt);
-        step(C1{}, C0{}, kt + 1);
-      }
-      step(C0{}, C1{}, nk - 2);
-      step(C1{}, C2{}, nk - 1);
-    } else {
-      for (int kt = 0; kt < nk - 3; kt += 2) {
-        step(C0{}, C0{}, kt);
-        step(C1{}, C0{}, kt + 1);
-      }
-      step(C0{}, C0{}, nk - 3);
-      step(C1{}, C1{}, nk - 2);
-      step(C0{}, C2{}, nk - 1);
-    }
-  };
-  // this wave's MFMA row blocks that hold rows of the block
-  const int na = __builtin_amdgcn_readfirstlane(min(TMB, max(0, (vrows - wm * TM + 31) / 32)));
-  switch (na) {
-    case 0: kloop(std::integral_constant<int, 0>{}); break;
-    case 1: kloop(std::integral_constant<int, 1>{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}); break;
-    case 4: kloop(std::integral_constant<int, 4>{}); break;
-    default: kloop(std::integral_constant<int, 5>{}); break;
-  }
-
-  // epilogue, as gemm_bf16_dma; rows past the block are not stored
-  var_epilogue<MODE, TMB, TNB, TM, TNR, BNR>(a, acc, m0, vrows, slot, nt, wm, wn, lane);
-}
-
-// ----------------------------------------------------------------------------------------
-// Variable row blocks, deep pipeline: the tile of gemm_bf16_var (320 x 256, 8 waves of
-// 160 x 64) with K step 32 and four LDS stages in a ring, so the loads run three and a half K
-// steps ahead of the MFMAs instead of one and a half: about 108 KiB in flight per CU instead
-// of 72. For launches that stream their weights from HBM (one or two row blocks per expert),
-// where a load takes longer to come back than one K step of MFMAs; the weight loads carry the
-// non-temporal hint (measured, EP share T=8192: layer 0.240 -> 0.218 ms; on the two-stage
-// kernel, whose weight tiles serve several row blocks from L2, the hint costs 5%).
+// 320 x 256 tile, 8 waves (2 x 4, 160 x 64 each, two per SIMD), v_mfma_f32_32x32x16_bf16. Each
+// wave runs the K loop compiled for the number of its five 32-row MFMA blocks that hold rows of
+// the block (no MFMA or fragment read for the others). Register budget (two waves per SIMD):
+// the A fragments are single-buffered, each read for the next K slice right after its row
+// block's last MFMA of this slice; the B fragments alternate between two sets.
+// K step 32 and four LDS stages in a ring (144 KiB), so the loads run three and a half K steps
+// ahead of the MFMAs: about 108 KiB in flight per CU. Measured against a two-stage version
+// with K step 64 (loads one and a half steps ahead): EP share T=8192 gate/up 87 -> 80 us, down
+// 57 -> 52 us, Mixtral-shaped T=4096 layer 2.48 -> 2.44 ms (same box, two rounds). Weight
+// loads carry the non-temporal hint where the weights stream (GemmArgs::b_nt).
 // LDS rows are the 32 bf16 (64 bytes) of one tile row; the four 16-byte chunks of row r sit at
 // chunk ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows cover all banks. One
 // load instruction fills 16 rows (lane l: row 16 j + l / 4, position l % 4). Per wave and K
@@ -958,7 +732,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
       if (amask & (1u << d))
         dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA0 + st * SA + (wave + NW * d) * 1024));
     } else {
-      dma16_nt(Bbase, voff, __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024));
+      dma16_hint(Bbase, voff, __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024), a.b_nt);
     }
   };
 

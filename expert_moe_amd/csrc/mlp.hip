@@ -213,11 +213,8 @@ double est_padding(const moe_params& p, int T, int tr) {
   return all > 0.0 ? pad / all : 0.0;
 }
 
-// Variable row blocks whose weights stream from HBM: under 512 rows per expert expected (one
-// or two row blocks read each weight tile, so little of it comes from L2) take the deep-pipeline
-// kernel, whose loads run further ahead (measured with 256 rows per expert, EP share: gate/up
-// 87 -> 80 us, down 57 -> 52 us); with more rows per expert the weight tiles are shared in L2
-// and the two-stage kernel is faster (Mixtral-shaped T=4096, 1024 rows per expert: by 2%).
+// Under 512 rows per expert expected, one or two row blocks read each weight tile, so the
+// weights stream from HBM rather than from L2.
 bool stream_var_blocks(const moe_params& p, int T) {
   return static_cast<double>(T) * p.top_k < 512.0 * p.num_experts;
 }
@@ -339,9 +336,7 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
     g.valid_map = nullptr;
     g.n_tiles = 2 * I / 256;
     const int nbmax = rows / 256 + 1 + p.num_local_experts;
-    if (stream_var_blocks(p, T))
-      return launch(gemm_bf16_var4<kSiluMul>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
-    return launch(gemm_bf16_var<kSiluMul>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
+    return launch(gemm_bf16_var4<kSiluMul>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
   }
   const bool sorted = row_map != nullptr;
   const Plan pl = plan_rows(p, sorted, block_m, rows, 2 * I);
@@ -388,9 +383,7 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
     g.store_map = nullptr;
     g.n_tiles = H / 256;
     const int nbmax = rows / 256 + 1 + p.num_local_experts;
-    if (stream_var_blocks(p, T))
-      return launch(gemm_bf16_var4<kStore>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
-    return launch(gemm_bf16_var<kStore>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
+    return launch(gemm_bf16_var4<kStore>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
   }
   const bool sorted = num_padded != nullptr;
   const Plan pl = plan_rows(p, sorted, block_m, rows, H);
@@ -429,9 +422,10 @@ bool prefer_var_blocks(const moe_params& p, int64_t T) {
   const double tiles = p.num_local_experts * touched * bvar / 8.0 * (2.0 * p.intermediate_size / 256.0);
   const int n_cu = cu_count() > 0 ? cu_count() : 256;
   if (bvar <= 0.95 * b256 && tiles >= n_cu) return true;
-  // As many blocks, 128 to 512 rows per expert: the variable blocks run the deep-pipeline
-  // kernel, the 256 granule a two-stage one (DeepSeek-V2-shaped, 153 rows per expert: 0.636 ->
-  // 0.619 ms; skewed T=256 and T=16384, 32 and 2048 rows per expert, lose 8% and 7%).
+  // As many blocks, 128 to 512 rows per expert: the variable blocks run a four-stage pipeline,
+  // the 256 granule a two-stage one (DeepSeek-V2-shaped, 153 rows per expert: 0.636 -> 0.619
+  // ms; skewed T=256 and T=16384, 32 and 2048 rows per expert, lose 8% and 7%, and again 7% and
+  // 1-2% with the weight hint only where weights stream).
   return per >= 128.0 && stream_var_blocks(p, static_cast<int>(T)) && bvar <= b256;
 }
 

@@ -76,7 +76,8 @@ VAR_SHARED = W("var_sh", 18, "variable row blocks with a shared expert", "bf16",
                8, 4096, 2, True, shared_intermediate_size=512)
 
 
-# 1200 tokens: 300 rows per expert, the deep-pipeline kernel; 3000: 750, the two-stage one
+# 1200 tokens: 300 rows per expert, weights streamed (non-temporal hint); 3000: 750, weight tiles
+# shared by three row blocks (plain loads)
 @pytest.mark.parametrize("T", VAR_SHARED.tokens)
 @pytest.mark.parametrize("overlap", [False, True], ids=["serial", "overlap"])
 def test_forward_variable_blocks_with_shared(overlap, T):
