@@ -84,14 +84,6 @@ __device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32
 #endif
 }
 
-// dma16 or dma16_nt by a wave-uniform flag.
-__device__ __forceinline__ void dma16_hint(const void* base, uint32_t voff, uint32_t lds_addr, int nt) {
-  if (nt)
-    dma16_nt(base, voff, lds_addr);
-  else
-    dma16(base, voff, lds_addr);
-}
-
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   using lds_ptr = const __attribute__((address_space(3))) uint8_t*;

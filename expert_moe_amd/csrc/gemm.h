@@ -58,6 +58,7 @@ struct GemmArgs {
   int32_t act;                 // kSiluMul: 0 = silu, 1 = swigluoai
   int32_t b_packed;            // 1: B in the packed weight layout (b_offset), bf16 kernels only
   int32_t b_nt;                // LDS tile kernels: 1 = weight loads with the non-temporal hint
+                               // (the launch picks the kernel instantiation that has it)
 };
 
 // Packed weight layout: each [rows, K] bf16 matrix is stored as 1 KiB blocks of 16 rows x 32
@@ -216,9 +217,12 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int& mb, int& nt) {
 // LDS rows are the 64 bf16 (128 bytes) of one tile row; the eight 16-byte chunks of row r are
 // stored at chunk ^ sw(r), sw(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of
 // 16 consecutive rows hit distinct banks. One load instruction fills 8 rows (1 KiB, lane l at
-// byte 16 l): lane l loads row 8 j + l / 8, logical chunk (l % 8) ^ sw(row).
+// byte 16 l): lane l loads row 8 j + l / 8, logical chunk (l % 8) ^ sw(row). NT: the weight
+// loads carry the non-temporal hint (a compile-time choice, as in gemm_bf16_var4: measured,
+// skewed T=16384 layer 6.50 -> 6.40 ms and DeepSeek-V2-shaped 0.616 -> 0.607 ms against a
+// branch on GemmArgs::b_nt per weight load).
 // ----------------------------------------------------------------------------------------
-template <int BM, int BNR, int WM, int WN, int MODE, int NS = 2, bool SKIP = false>
+template <int BM, int BNR, int WM, int WN, int MODE, int NS = 2, bool SKIP = false, bool NT = false>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   constexpr int NW = WM * WN;              // waves (4, or 8 = two per SIMD)
   constexpr int BK = 64;
@@ -306,10 +310,15 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_dma(GemmArgs a) {
   // load instruction d of K step kt into stage st
   auto dma = [&](int d, int kt, int st) {
     const uint32_t voff = goff[d] + static_cast<uint32_t>(kt) * (d < NA ? BK * 2 : bstep);
-    if (d < NA)
+    if (d < NA) {
       dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA[st] + (wave + NW * d) * 1024));
-    else
-      dma16_hint(Bbase, voff, __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024), a.b_nt);
+    } else {
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lB[st] + (wave + NW * (d - NA)) * 1024);
+      if constexpr (NT)
+        dma16_nt(Bbase, voff, lds);
+      else
+        dma16(Bbase, voff, lds);
+    }
   };
 
   // wave -> (row group, weight-row group)
@@ -661,7 +670,9 @@ __device__ __forceinline__ void var_epilogue(const GemmArgs& a, f32x16 (&acc)[TM
 // ahead of the MFMAs: about 108 KiB in flight per CU. Measured against a two-stage version
 // with K step 64 (loads one and a half steps ahead): EP share T=8192 gate/up 87 -> 80 us, down
 // 57 -> 52 us, Mixtral-shaped T=4096 layer 2.48 -> 2.44 ms (same box, two rounds). Weight
-// loads carry the non-temporal hint where the weights stream (GemmArgs::b_nt).
+// loads carry the non-temporal hint where the weights stream (NT, taken from GemmArgs::b_nt
+// at launch). The hint is a compile-time choice: one branch per weight load on the flag cost
+// 1-1.7% on the Mixtral-shaped layer (two branches per K step in the loop).
 // LDS rows are the 32 bf16 (64 bytes) of one tile row; the four 16-byte chunks of row r sit at
 // chunk ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows cover all banks. One
 // load instruction fills 16 rows (lane l: row 16 j + l / 4, position l % 4). Per wave and K
@@ -670,7 +681,7 @@ __device__ __forceinline__ void var_epilogue(const GemmArgs& a, f32x16 (&acc)[TM
 // only (vmcnt = its loads issued since), then the workgroup meets at a barrier without the
 // fence of __syncthreads (which would wait for every load in flight).
 // ----------------------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, bool NT>
 __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
   constexpr int BM = 320, BNR = 256, WM = 2, WN = 4, NW = 8;
   constexpr int BK = 32, ROWB = 64, NS = 4;
@@ -732,7 +743,11 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
       if (amask & (1u << d))
         dma16(Abase, voff, __builtin_amdgcn_readfirstlane(lA0 + st * SA + (wave + NW * d) * 1024));
     } else {
-      dma16_hint(Bbase, voff, __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024), a.b_nt);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lB0 + st * SB + (wave + NW * (d - NA)) * 1024);
+      if constexpr (NT)
+        dma16_nt(Bbase, voff, lds);
+      else
+        dma16(Bbase, voff, lds);
     }
   };
 

@@ -29,6 +29,13 @@ int cu_count() {
   return n;
 }
 
+// The LDS tile with the weight hint of the launch (GemmArgs::b_nt) as a compile-time choice.
+template <int BM, int BNR, int WM, int WN, int MODE, int NS, bool SKIP>
+int launch_dma(const GemmArgs& a, int grid, int threads, size_t dyn, hipStream_t s) {
+  if (a.b_nt) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, SKIP, true>, grid, threads, dyn, s, a);
+  return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, SKIP, false>, grid, threads, dyn, s, a);
+}
+
 template <int BM, int BNR, int WM, int WN, int MODE>
 int launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, hipStream_t s) {
   a.n_tiles = n_rows_b / BNR;
@@ -45,8 +52,8 @@ int launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, hi
     constexpr size_t kStatic = NS * kStage;
     const size_t dyn = kStatic <= kLdsCu / 2 ? kLdsCu / 2 + 1024 - kStatic : 0;
     const int grid = (a.n_cu + kXcds - 1) / kXcds * kXcds;
-    if (a.valid_map) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, true>, grid, kThreads, dyn, s, a);
-    return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS, false>, grid, kThreads, dyn, s, a);
+    if (a.valid_map) return launch_dma<BM, BNR, WM, WN, MODE, NS, true>(a, grid, kThreads, dyn, s);
+    return launch_dma<BM, BNR, WM, WN, MODE, NS, false>(a, grid, kThreads, dyn, s);
   } else {
     // Three stages (one workgroup per CU) where two already take more than half of the CU's
     // LDS, or where the expected tiles fill at most two rounds of the CUs, so that latency and
@@ -59,11 +66,11 @@ int launch_tile_only(GemmArgs a, int n_rows_b, int est_blocks, int tail_mode, hi
     const bool deep = kFits3 && (kBig || few);
     // sorted rows skip padding row groups; dense launches keep the branch-free loop
     if (a.valid_map) {
-      if (deep) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, true>, grid, kThreads, 0, s, a);
-      return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, true>, grid, kThreads, 0, s, a);
+      if (deep) return launch_dma<BM, BNR, WM, WN, MODE, NS3, true>(a, grid, kThreads, 0, s);
+      return launch_dma<BM, BNR, WM, WN, MODE, 2, true>(a, grid, kThreads, 0, s);
     }
-    if (deep) return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, NS3, false>, grid, kThreads, 0, s, a);
-    return launch(gemm_bf16_dma<BM, BNR, WM, WN, MODE, 2, false>, grid, kThreads, 0, s, a);
+    if (deep) return launch_dma<BM, BNR, WM, WN, MODE, NS3, false>(a, grid, kThreads, 0, s);
+    return launch_dma<BM, BNR, WM, WN, MODE, 2, false>(a, grid, kThreads, 0, s);
   }
 }
 
@@ -336,7 +343,8 @@ int launch_gate_up(const moe_params& p, int T, const void* x, const void* w13, i
     g.valid_map = nullptr;
     g.n_tiles = 2 * I / 256;
     const int nbmax = rows / 256 + 1 + p.num_local_experts;
-    return launch(gemm_bf16_var4<kSiluMul>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
+    if (g.b_nt) return launch(gemm_bf16_var4<kSiluMul, true>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
+    return launch(gemm_bf16_var4<kSiluMul, false>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
   }
   const bool sorted = row_map != nullptr;
   const Plan pl = plan_rows(p, sorted, block_m, rows, 2 * I);
@@ -383,7 +391,8 @@ int launch_down(const moe_params& p, int T, const void* act, const void* w2, int
     g.store_map = nullptr;
     g.n_tiles = H / 256;
     const int nbmax = rows / 256 + 1 + p.num_local_experts;
-    return launch(gemm_bf16_var4<kStore>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
+    if (g.b_nt) return launch(gemm_bf16_var4<kStore, true>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
+    return launch(gemm_bf16_var4<kStore, false>, tile_grid(nbmax, g.n_tiles), 512, 0, s, g);
   }
   const bool sorted = num_padded != nullptr;
   const Plan pl = plan_rows(p, sorted, block_m, rows, H);
