@@ -732,9 +732,13 @@ __global__ void __launch_bounds__(512) gemm_bf16_var4(GemmArgs a) {
   }
   const uint32_t bstep = b_step(a, BK);
   const uint32_t lA0 = lds_addr(sA), lB0 = lds_addr(sB);
-  // A load instructions of this wave (bit j): the 16-row groups wave + 8 j of the 20
-  constexpr uint32_t kAmaskLo = (1u << NA) - 1, kAmaskHi = (1u << (NA - 1)) - 1;
-  const uint32_t amask = wave + NW * (NA - 1) < AG ? kAmaskLo : kAmaskHi;
+  // A load instructions of this wave (bit j): the 16-row groups wave + 8 j of the 20; the last
+  // one only where its group starts inside the block (rows 256 .. 319 of a block of at most 256
+  // rows would move copies of its last row into LDS). Every wave keeps at least AG / NW A loads
+  // per K step, the count the waits assume.
+  static_assert(NA == 3 && AG / NW == NA - 1, "the last A load is the only one skipped");
+  const int glast = wave + NW * (NA - 1);
+  const uint32_t amask = glast < AG && 16 * glast < vrows ? (1u << NA) - 1 : (1u << (NA - 1)) - 1;
   constexpr int kMinLoads = AG / NW + NB;  // load instructions per K step of every wave, at least
   // load instruction d of K step kt into stage st
   auto dma = [&](int d, int kt, int st) {
