@@ -108,11 +108,12 @@ def test_forward_variable_blocks_with_shared(overlap, T):
     assert err <= OUT_TOL[w.dtype], err
 
 
-@pytest.mark.parametrize("case", ["ds_s", "ep_s"])
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("case", ["ds_s", "ep_s", "skew_s1"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 9, 16])
 def test_forward_decode_sizes(case, T):
-    """Decode-sized calls (one to five tokens, granule 16, weight-streaming kernels): routing and
-    output vs the oracle on every token."""
+    """Decode-sized calls (1 to 16 tokens, granule 16, weight-streaming kernels; at 16 tokens on
+    the skewed share one expert takes most of them): routing and output vs the oracle on every
+    token."""
     w, _ = SMALL[case]
     _full_check(Layer(w, T))
 
